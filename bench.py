@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Throughput of the KV-cache eviction step on one MI355X.
+
+A step is one decode token through every layer: L launches (one per layer),
+each stepping all B*H caches of that layer through keyformer_step or
+pyramid_step.  Inputs are resident in HBM before the timed region.  Timing is
+bracketed by HIP events on the stream the kernels run on.
+
+Prints ONE JSON line: cache-row updates/s (B*L*H*tokens per second) as
+`value`, the achieved algorithmic HBM bandwidth of the step kernel against
+MI355X's 8 TB/s in `roofline`, and the CPU oracle timed on the host cores in
+`cpu_baseline`.
+
+Algorithmic bytes per cache-step (n = rows stored before the step, D = head
+dim, m = rows whose slot changes: n - e for an evicted stored row e, 0 when
+nothing or the incoming row is evicted):
+  Keyformer: 2nD + 12n + 8D + 12 + m(8D + 24)
+  PyramidKV: 2nD +  8n + 8D +  8 + m(8D + 16)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--config", type=int, default=4, help="workload index 0..4")
+    ap.add_argument("--fill", choices=["synthetic", "real"], default="synthetic",
+                    help="reach the steady state by synthesising it (default) or by "
+                         "stepping the prompt through the real step")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall-clock budget of the CPU oracle baseline (0 = skip)")
+    return ap.parse_args()
+
+
+def step_bytes(kind: str, n: int, d: int, m):
+    """Algorithmic bytes of one cache-step (m may be an array)."""
+    if kind == "keyformer":
+        return 2 * n * d + 12 * n + 8 * d + 12 + m * (8 * d + 24)
+    return 2 * n * d + 8 * n + 8 * d + 8 + m * (8 * d + 16)
+
+
+def cpu_baseline(w, budgets, seconds: float):
+    """The CPU oracle stepping caches of the same workload at their steady state."""
+    from concurrent.futures import ProcessPoolExecutor
+    procs = max(1, min(16, os.cpu_count() or 1))
+    layers = [l % w.layers for l in range(procs)]
+    with ProcessPoolExecutor(procs) as ex:
+        res = list(ex.map(_cpu_worker, [(w, l, budgets[l], seconds / 2) for l in layers]))
+    one = _cpu_worker((w, layers[0], budgets[layers[0]], seconds / 2))
+    steps_all = sum(r[0] for r in res)
+    wall_all = max(r[1] for r in res)
+    return {
+        "value": steps_all / wall_all, "unit": "cache-row updates/s", "cores": procs,
+        "kind": "oracle", "single_core": one[0] / one[1],
+        "sample": (f"{procs} caches (one per process, layers {layers[0]}..{layers[-1]}), each "
+                   f"from a synthetic steady state at its layer budget, stepped token by token "
+                   f"for ~{seconds / 2:.0f} s; single_core = one such cache alone"),
+        "cpu": platform.processor() or platform.machine(),
+    }
+
+
+def _cpu_worker(args):
+    w, layer, budget, seconds = args
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import numpy as np
+    import synth
+    from gpu_harness import random_state
+    from oracle.guard import params_for
+    c = random_state(w, layer, 0, budget, budget + 1, w.prompt)
+    prm = params_for(w, budget, 0)
+    ks, vs = synth.token_kv(w, layer, 0, np.arange(w.prompt, w.prompt + 4096))
+    t0 = time.perf_counter()
+    steps = 0
+    while time.perf_counter() - t0 < seconds and steps < len(ks):
+        c.step(ks[steps], vs[steps], prm)
+        steps += 1
+    return steps, time.perf_counter() - t0
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the eviction step shards with no exchange; run one process per GPU).",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import synth
+    import kv_cache_eviction_step_amd as kve
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.config]
+    kf = w.kind == "keyformer"
+    budgets = w.budgets(kve.pyramid_budgets)
+    L, bh, d = w.layers, w.bh, w.d
+    layers = [kve.Layer.empty(bh, b + 1, d, dev, gumbel=kf) for b in budgets]
+    cls = [x.c_struct() for x in layers]
+    ctrs = [kve.Counters(0, 0, 0) for _ in range(L)]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2024)
+
+    def step_layer(l, k, v, ev=None):
+        if kf:
+            kve.keyformer_step(layers[l], k, v, ctrs[l], budgets[l], w.n_sink, w.tau_init,
+                               w.tau_end, w.anneal_steps, w.rope_base, w.gumbel_seed, ev,
+                               c_layer=cls[l])
+        else:
+            kve.pyramid_step(layers[l], k, v, ctrs[l], budgets[l], w.n_sink, w.rope_base, ev,
+                             c_layer=cls[l])
+
+    # ---- reach the steady state (untimed) ------------------------------------
+    t_fill = time.time()
+    pos0 = w.prompt
+    if args.fill == "synthetic":
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from gpu_harness import bulk_state
+        for l in range(L):
+            bulk_state(layers[l], budgets[l], w, gen)
+            ctrs[l] = kve.Counters(budgets[l], pos0, pos0)
+    else:
+        chunk = 64
+        for t0 in range(0, w.prompt, chunk):
+            cnt = min(chunk, w.prompt - t0)
+            ins = [synth.bulk_kv_torch(w, t0, cnt, bh, gen, dev) for _ in range(L)]
+            for t in range(cnt):
+                for l in range(L):
+                    step_layer(l, ins[l][0][t], ins[l][1][t])
+    torch.cuda.synchronize()
+    t_fill = time.time() - t_fill
+
+    # ---- inputs for warmup + timed steps, resident in HBM ----------------------
+    S = args.warmup + args.steps
+    nk = torch.empty((S, L, bh, d), dtype=torch.float16, device=dev)
+    nv = torch.empty_like(nk)
+    for l in range(L):
+        k, v = synth.bulk_kv_torch(w, pos0, S, bh, gen, dev)
+        nk[:, l], nv[:, l] = k, v
+    ev = torch.full((args.steps, L, bh), -9, dtype=torch.int32, device=dev)
+    n_prev = [[0] * L for _ in range(args.steps)]
+    torch.cuda.synchronize()
+
+    for s in range(args.warmup):
+        for l in range(L):
+            step_layer(l, nk[s, l], nv[s, l])
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for s in range(args.steps):
+        for l in range(L):
+            n_prev[s][l] = ctrs[l].n_kept
+            step_layer(l, nk[args.warmup + s, l], nv[args.warmup + s, l], ev[s, l])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+
+    # ---- algorithmic bytes from the eviction log --------------------------------
+    evn = ev.cpu().numpy()
+    total_bytes = 0
+    for s in range(args.steps):
+        for l in range(L):
+            n = n_prev[s][l]
+            e = evn[s, l]
+            m = np.where((e >= 0) & (e < n), n - e, 0).astype(np.int64)
+            total_bytes += int(step_bytes(w.kind, n, d, m).sum())
+    launches = args.steps * L
+    sec = ms / 1e3
+    updates = bh * L * args.steps
+    avg_launch_s = sec / launches
+    bytes_per_launch = total_bytes / launches
+    achieved = bytes_per_launch / avg_launch_s / 1e9
+    mean_m = float(np.where((evn >= 0), np.maximum(0, np.array(n_prev)[:, :, None] - evn),
+                            0).mean())
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(w, budgets, args.cpu_seconds)
+
+    out = {
+        "metric": "cache-row updates/sec (B·L·H·tokens) and achieved HBM GB/s vs peak, 1 GPU",
+        "value": updates / sec,
+        "unit": "cache-row updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"configs[{args.config}] {w.name}: B={w.batch} layers={L} "
+                        f"kv_heads={w.kv_heads} D={d} {w.kind} budget="
+                        f"{'pyramid avg ' if w.kind == 'pyramid' else ''}{w.budget} "
+                        f"n_sink={w.n_sink}",
+            "kv_storage": "f16", "bh_per_launch": bh, "layers": L,
+            "budgets": [budgets[0], budgets[-1]], "steady_state_fill": args.fill,
+            "fill_seconds": round(t_fill, 1), "mean_rows_moved_per_cache_step": mean_m,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+            "kernel": "kve::step_kernel", "avg_launch_us": avg_launch_s * 1e6,
+            "algorithmic_bytes_per_launch": bytes_per_launch,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

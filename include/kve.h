@@ -1,0 +1,153 @@
+/*
+ * kve.h -- C ABI of the MI355X (gfx950) KV-cache eviction step.
+ *
+ * One call steps one token into every cache of one layer: for each of the
+ * layer's B*H caches (one per batch element and kv-head) it
+ *   1. scores the stored keys with the incoming key as the query,
+ *      softmax(K_stored . k_new / sqrt(d)), and adds that mass to each stored
+ *      row's fp32 cumulative score;
+ *   2. appends the new fp16 key/value row with score 0, position next_pos and
+ *      (Keyformer) its frozen Gumbel value;
+ *   3. if the cache now holds budget + 1 rows, evicts the non-sink row with
+ *      the smallest  score + tau * gumbel  (ties: lowest index), moves the
+ *      later rows down one slot, and re-rotates the moved keys' RoPE in fp32
+ *      so that positions are again the contiguous range 0 .. n_kept-1.
+ *
+ * Sources (VeloxQuant-MLX documentation pages):
+ *   "veloxquant_mlx.quantizers.keyformer module": keyformer_update (steps
+ *     1-3), keyformer_update_batched (one call over the B*H rows, per-row
+ *     noise streams), KeyformerState (field meanings), init_keyformer_state
+ *     (argument checks), FIXED GAP #1 (annealed temperature), FIXED GAP #2
+ *     (position tracking and RoPE remap), FUSED METAL KERNEL (fp32 rotation).
+ *   "PyramidKV -- Layer-Adaptive Budget Attention-Mass Eviction": How it
+ *     works (the H2O step per layer), The budget schedule, Parameters,
+ *     Relationship to H2O.
+ *
+ * Conventions
+ *   - Every tensor pointer is DEVICE memory owned by the caller (for example
+ *     torch.Tensor.data_ptr() of a contiguous tensor on the current device).
+ *     The library keeps no pointer after a call returns.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and the call returns without synchronising.  Results are visible to
+ *     later work on the same stream; synchronise before reading elsewhere.
+ *   - Per call the library allocates nothing and keeps no state besides
+ *     small per-thread caches of rotation frequencies; calls are reentrant.
+ *   - Arguments are checked on the host before anything is enqueued.  A
+ *     failing check returns KVE_EINVAL and leaves the counters and every
+ *     tensor untouched.  A device fault is asynchronous and surfaces at the
+ *     caller's next synchronisation.
+ */
+#ifndef KVE_H
+#define KVE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVE_OK        0
+#define KVE_EINVAL   -1   /* an argument failed a host-side check            */
+#define KVE_ELAUNCH  -2   /* the HIP runtime rejected the kernel launch       */
+#define KVE_ENODEV   -3   /* no HIP device, or the current device is not gfx950 */
+
+/* One layer's B*H caches.  Rows of a cache are contiguous, caches follow
+ * each other:  element (hh, row, j) of k lives at k[(hh*cap + row)*d + j].
+ * Rows [0, n_kept) are live and in temporal order; rows >= n_kept hold
+ * unspecified data after a call. */
+typedef struct kve_layer {
+    void    *k;          /* fp16 [bh][cap][d]  keys, RoPE'd at `positions`          */
+    void    *v;          /* fp16 [bh][cap][d]  values                               */
+    float   *scores;     /* f32  [bh][cap]     cumulative proxy-attention mass       */
+    float   *gumbel;     /* f32  [bh][cap]     frozen Gumbel value of each row;
+                            required by keyformer_step, unused (may be NULL) by
+                            pyramid_step                                             */
+    int32_t *positions;  /* i32  [bh][cap]     position each key is rotated at; the
+                            library writes it.  Precondition (true of any state
+                            built by these calls from an empty cache):
+                            positions[hh][i] == i for every live row i            */
+    int32_t  bh;         /* number of caches (batch * kv-heads), >= 1              */
+    int32_t  cap;        /* rows allocated per cache, >= budget + 1                */
+    int32_t  d;          /* head dimension: 64 or 128                             */
+    int32_t  hh_base;    /* index of row 0 of this call in the Gumbel stream
+                            numbering (0 unless the B*H set is split across calls
+                            or devices); cache hh draws from stream hh_base + hh  */
+} kve_layer;
+
+/* HOST memory, read and updated by each successful call; shared by every
+ * cache of the layer (keyformer_update_batched shares them across rows). */
+typedef struct kve_counters {
+    int32_t n_kept;      /* live rows before the call (uniform across the bh caches) */
+    int32_t next_pos;    /* absolute position of the incoming token                  */
+    int32_t pos;         /* running insertion count: the Gumbel counter and the
+                            annealing clock                                          */
+} kve_counters;
+
+/*
+ * keyformer_step -- Keyformer-adapted step (keyformer_update_batched with one
+ * token, return_indices replaced by `evicted`).
+ *
+ *   L          layer tensors (see kve_layer); L->gumbel must not be NULL
+ *   new_k      fp16 [bh][d] device: incoming keys, already RoPE'd at next_pos
+ *   new_v      fp16 [bh][d] device: incoming values
+ *   ctr        host counters; on success n_kept = min(n_kept + 1, budget),
+ *              next_pos += 1, pos += 1
+ *   budget     rows kept at most, sinks included; budget > n_sink
+ *   n_sink     leading rows never evicted; >= 0
+ *   tau_init, tau_end, anneal_steps
+ *              temperature tau = tau_init + min(pos, anneal_steps) *
+ *              (tau_end - tau_init) / anneal_steps, evaluated in double on the
+ *              device and rounded to float; constant tau_init when
+ *              anneal_steps == 0 or tau_init == tau_end.  Both >= 0,
+ *              anneal_steps >= 0.  tau == 0 gives H2O exactly.
+ *   rope_base  RoPE frequency base (> 0) used to re-rotate moved keys
+ *   seed       base seed of the Gumbel streams: the value of the row inserted
+ *              at running position pos in cache hh is
+ *              g = -log(-log u), u = ((h >> 11) + 1/2) / 2^53,
+ *              h = mix(mix(mix(seed) ^ (hh_base + hh)) ^ pos), mix = the
+ *              SplitMix64 output function
+ *   evicted    optional device i32 [bh]: the evicted row index (counted before
+ *              compaction, the new row being index n_kept) or -1; may be NULL
+ *   stream     hipStream_t or NULL
+ * Returns KVE_OK, KVE_EINVAL (bad argument; also when no eviction happens but
+ * next_pos != n_kept, which would break the contiguous-position invariant,
+ * e.g. a budget raised after evictions), KVE_ENODEV or KVE_ELAUNCH.
+ */
+int keyformer_step(const kve_layer *L, const void *new_k, const void *new_v,
+                   kve_counters *ctr, int32_t budget, int32_t n_sink,
+                   double tau_init, double tau_end, int32_t anneal_steps,
+                   double rope_base, uint64_t seed, int32_t *evicted, void *stream);
+
+/*
+ * pyramid_step -- H2O-adapted step at one layer's budget (PyramidKV-adapted
+ * when `budget` comes from pyramid_budgets).  Same as keyformer_step with
+ * tau == 0 and no noise: the eviction key is the raw score and L->gumbel is
+ * neither read nor written.
+ */
+int pyramid_step(const kve_layer *L, const void *new_k, const void *new_v,
+                 kve_counters *ctr, int32_t budget, int32_t n_sink, double rope_base,
+                 int32_t *evicted, void *stream);
+
+/*
+ * pyramid_budgets -- per-layer budgets ("The budget schedule"): a linear taper
+ * from the largest budget at layer 0 to the smallest at the last layer, mean
+ * avg_budget, every entry at least n_sink + 1.  The smallest is
+ * max((2 - beta) * avg_budget, n_sink + 1), the largest 2 * avg_budget minus
+ * the smallest; entry l is their linear interpolation rounded to nearest
+ * (halves to even).  beta == 1 gives every layer avg_budget; n_layers == 1
+ * gives {avg_budget}; n_layers == 0 writes nothing.
+ *   out   HOST i32 [n_layers]
+ * Returns KVE_OK, or KVE_EINVAL if beta < 1 (or NaN), n_layers < 0,
+ * n_sink < 0, avg_budget < n_sink + 1, or out == NULL with n_layers > 0.
+ * Pure host arithmetic; needs no device.
+ */
+int pyramid_budgets(int32_t n_layers, int32_t avg_budget, int32_t n_sink, double beta,
+                    int32_t *out);
+
+/* Text for a KVE_* code (static storage). */
+const char *kve_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVE_H */

@@ -1,0 +1,191 @@
+"""Python binding of libkve.so, the gfx950 KV-cache eviction step.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of ``include/kve.h``.  PyTorch supplies device
+memory and streams.  There is no fallback: if the library is missing this
+module fails to import.
+
+Calls (same names as the C ABI):
+    keyformer_step(layer, new_k, new_v, ctr, budget, n_sink, tau_init, tau_end,
+                   anneal_steps, rope_base, seed, evicted=None, stream=None)
+    pyramid_step(layer, new_k, new_v, ctr, budget, n_sink, rope_base,
+                 evicted=None, stream=None)
+    pyramid_budgets(n_layers, avg_budget, n_sink, beta) -> list[int]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (loads torch's HIP runtime first; libkve binds to it)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkve.so")
+
+KVE_OK, KVE_EINVAL, KVE_ELAUNCH, KVE_ENODEV = 0, -1, -2, -3
+
+
+class KveLayer(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("scores", ctypes.c_void_p), ("gumbel", ctypes.c_void_p),
+        ("positions", ctypes.c_void_p),
+        ("bh", ctypes.c_int32), ("cap", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("hh_base", ctypes.c_int32),
+    ]
+
+
+class Counters(ctypes.Structure):
+    """Host counters shared by a layer's caches (n_kept, next_pos, pos)."""
+    _fields_ = [("n_kept", ctypes.c_int32), ("next_pos", ctypes.c_int32),
+                ("pos", ctypes.c_int32)]
+
+    def copy(self) -> "Counters":
+        return Counters(self.n_kept, self.next_pos, self.pos)
+
+    def __repr__(self) -> str:
+        return f"Counters(n_kept={self.n_kept}, next_pos={self.next_pos}, pos={self.pos})"
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it first "
+                      "(python -c 'import __graft_entry__ as g; g.build()')")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_lib.keyformer_step.restype = ctypes.c_int
+_lib.keyformer_step.argtypes = [
+    ctypes.POINTER(KveLayer), ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(Counters),
+    ctypes.c_int32, ctypes.c_int32, ctypes.c_double, ctypes.c_double, ctypes.c_int32,
+    ctypes.c_double, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+_lib.pyramid_step.restype = ctypes.c_int
+_lib.pyramid_step.argtypes = [
+    ctypes.POINTER(KveLayer), ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(Counters),
+    ctypes.c_int32, ctypes.c_int32, ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p]
+_lib.pyramid_budgets.restype = ctypes.c_int
+_lib.pyramid_budgets.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                 ctypes.c_double, ctypes.c_void_p]
+_lib.kve_strerror.restype = ctypes.c_char_p
+_lib.kve_strerror.argtypes = [ctypes.c_int]
+
+EXPORTED = ("keyformer_step", "pyramid_step", "pyramid_budgets", "kve_strerror")
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return _lib.kve_strerror(code).decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc == KVE_OK:
+        return
+    msg = f"{what}: {strerror(rc)} (code {rc})"
+    if rc == KVE_EINVAL:
+        raise ValueError(msg)
+    raise RuntimeError(msg)
+
+
+def hip_runtimes_mapped() -> list[str]:
+    """Paths of every libamdhip64 mapped into this process (should be one)."""
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                paths.add(os.path.realpath(line.split()[-1]))
+    return sorted(paths)
+
+
+class Layer:
+    """One layer's B*H caches as caller-owned device tensors (the ABI's kve_layer).
+
+    k, v:       fp16 [bh, cap, d]
+    scores:     fp32 [bh, cap]
+    gumbel:     fp32 [bh, cap] or None (pyramid_step)
+    positions:  int32 [bh, cap]
+    """
+
+    def __init__(self, k, v, scores, gumbel, positions, hh_base: int = 0):
+        bh, cap, d = k.shape
+        for t, dt, shp in ((k, torch.float16, (bh, cap, d)), (v, torch.float16, (bh, cap, d)),
+                           (scores, torch.float32, (bh, cap)),
+                           (positions, torch.int32, (bh, cap))):
+            if t.dtype != dt or tuple(t.shape) != shp or not t.is_contiguous():
+                raise ValueError(f"layer tensor must be contiguous {dt} {shp}, got "
+                                 f"{t.dtype} {tuple(t.shape)}")
+            if t.device != k.device:
+                raise ValueError("layer tensors must share one device")
+        if gumbel is not None and (gumbel.dtype != torch.float32 or
+                                   tuple(gumbel.shape) != (bh, cap) or
+                                   not gumbel.is_contiguous() or gumbel.device != k.device):
+            raise ValueError("gumbel must be contiguous float32 [bh, cap] on the same device")
+        self.k, self.v, self.scores, self.gumbel, self.positions = k, v, scores, gumbel, positions
+        self.bh, self.cap, self.d, self.hh_base = bh, cap, d, hh_base
+
+    @classmethod
+    def empty(cls, bh: int, cap: int, d: int, device, gumbel: bool = True, hh_base: int = 0):
+        z = dict(device=device)
+        return cls(torch.zeros((bh, cap, d), dtype=torch.float16, **z),
+                   torch.zeros((bh, cap, d), dtype=torch.float16, **z),
+                   torch.zeros((bh, cap), dtype=torch.float32, **z),
+                   torch.zeros((bh, cap), dtype=torch.float32, **z) if gumbel else None,
+                   torch.zeros((bh, cap), dtype=torch.int32, **z), hh_base)
+
+    def c_struct(self) -> KveLayer:
+        return KveLayer(self.k.data_ptr(), self.v.data_ptr(), self.scores.data_ptr(),
+                        self.gumbel.data_ptr() if self.gumbel is not None else None,
+                        self.positions.data_ptr(), self.bh, self.cap, self.d, self.hh_base)
+
+
+def _rows(t, layer: Layer, name: str):
+    if (t.dtype != torch.float16 or tuple(t.shape) != (layer.bh, layer.d) or
+            not t.is_contiguous() or t.device != layer.k.device):
+        raise ValueError(f"{name} must be contiguous float16 [{layer.bh}, {layer.d}] on "
+                         f"{layer.k.device}")
+    return t.data_ptr()
+
+
+def _evicted_ptr(evicted, layer: Layer):
+    if evicted is None:
+        return None
+    if (evicted.dtype != torch.int32 or tuple(evicted.shape) != (layer.bh,) or
+            not evicted.is_contiguous() or evicted.device != layer.k.device):
+        raise ValueError(f"evicted must be contiguous int32 [{layer.bh}] on {layer.k.device}")
+    return evicted.data_ptr()
+
+
+def _stream_ptr(stream, layer: Layer):
+    if stream is None:
+        return torch.cuda.current_stream(layer.k.device).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def keyformer_step(layer: Layer, new_k, new_v, ctr: Counters, budget: int, n_sink: int,
+                   tau_init: float, tau_end: float, anneal_steps: int, rope_base: float,
+                   seed: int, evicted=None, stream=None, c_layer: KveLayer | None = None) -> None:
+    """One token into every cache of `layer` (Keyformer-adapted).  Updates `ctr`."""
+    cl = c_layer if c_layer is not None else layer.c_struct()
+    rc = _lib.keyformer_step(ctypes.byref(cl), _rows(new_k, layer, "new_k"),
+                             _rows(new_v, layer, "new_v"), ctypes.byref(ctr), budget, n_sink,
+                             tau_init, tau_end, anneal_steps, rope_base,
+                             seed & 0xFFFFFFFFFFFFFFFF, _evicted_ptr(evicted, layer),
+                             _stream_ptr(stream, layer))
+    _check(rc, "keyformer_step")
+
+
+def pyramid_step(layer: Layer, new_k, new_v, ctr: Counters, budget: int, n_sink: int,
+                 rope_base: float, evicted=None, stream=None,
+                 c_layer: KveLayer | None = None) -> None:
+    """One token into every cache of `layer` (H2O / PyramidKV-adapted).  Updates `ctr`."""
+    cl = c_layer if c_layer is not None else layer.c_struct()
+    rc = _lib.pyramid_step(ctypes.byref(cl), _rows(new_k, layer, "new_k"),
+                           _rows(new_v, layer, "new_v"), ctypes.byref(ctr), budget, n_sink,
+                           rope_base, _evicted_ptr(evicted, layer), _stream_ptr(stream, layer))
+    _check(rc, "pyramid_step")
+
+
+def pyramid_budgets(n_layers: int, avg_budget: int, n_sink: int, beta: float) -> list[int]:
+    buf = (ctypes.c_int32 * max(n_layers, 1))()
+    _check(_lib.pyramid_budgets(n_layers, avg_budget, n_sink, beta, buf), "pyramid_budgets")
+    return [int(buf[i]) for i in range(n_layers)]

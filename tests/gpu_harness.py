@@ -1,0 +1,210 @@
+"""Helpers shared by the GPU parity tests and the smoke entry point.
+
+A parity case steps a whole layer launch (every cache of the B*H set) on the
+GPU through the C ABI, while a few sampled caches also run through the CPU
+oracle on identical inputs.  The sampled caches get margin-guarded input
+streams (no eviction decided by a near-tie); the other caches get bulk random
+inputs of the same distribution.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ProcessPoolExecutor
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+from oracle import OracleCache
+from oracle.guard import guarded_trajectory, params_for
+
+# acceptance (per cache): kept rows and evicted indices bit-exact, values
+# bit-exact, keys within 1 fp16 ULP, scores within 1e-5 relative, Gumbel
+# values within 1 fp32 ULP
+SCORE_RTOL = 1e-5
+KEY_ULP = 1
+GUMBEL_ULP = 1
+
+
+@dataclass
+class Sample:
+    hh: int
+    budget: int
+    init: dict | None            # oracle snapshot of the initial state (None = empty)
+    ks: np.ndarray               # [T, D] guarded inputs
+    vs: np.ndarray
+    evicted: np.ndarray          # [T] oracle eviction log
+    final: dict                  # oracle snapshot after T tokens
+    attempts: int
+
+
+def random_state(w: synth.Workload, layer: int, hh: int, n: int, cap: int, next_pos: int,
+                 seed: int = 1) -> OracleCache:
+    """A plausible mid-run cache: n rows with keys at positions 0..n-1, positive
+    scores, frozen Gumbel values, positions == index."""
+    c = OracleCache(w.d, cap)
+    if n > 0:
+        ks, vs = synth.token_kv(w, layer, hh, np.arange(n), attempt=10_000 + seed)
+        rng = np.random.default_rng([seed, layer, hh])
+        c.k[:n], c.v[:n] = ks, vs
+        c.s[:n] = rng.gamma(0.7, 1.5, n).astype(np.float32)
+        c.g[:n] = np.array([oracle.gumbel(w.gumbel_seed, hh, 7_000_000 + i) for i in range(n)],
+                           dtype=np.float32) if w.kind == "keyformer" else 0.0
+        c.p[:n] = np.arange(n)
+        c.tid[:n] = np.arange(n)
+    c.set_counters(n, next_pos, next_pos)
+    return c
+
+
+def _sample_job(args) -> Sample:
+    w, layer, hh, budget, T, cap, init_n, next_pos = args
+    if init_n is None:
+        tr = guarded_trajectory(w, layer, hh, budget, T, cap=cap)
+        init = None
+    else:
+        c = random_state(w, layer, hh, init_n, cap, next_pos)
+        init = c.snapshot()
+        tr = guarded_trajectory(w, layer, hh, budget, T, cap=cap, t0=next_pos, cache=c)
+    return Sample(hh, budget, init, tr.ks, tr.vs, tr.evicted, tr.cache.snapshot(),
+                  int(tr.attempts.sum()))
+
+
+def oracle_samples(w: synth.Workload, layer: int, hhs, budget: int, T: int, cap: int,
+                   init_n: int | None = None, next_pos: int = 0,
+                   workers: int | None = None) -> list[Sample]:
+    jobs = [(w, layer, hh, budget, T, cap, init_n, next_pos) for hh in hhs]
+    workers = workers or min(len(jobs), max(1, min(16, (os.cpu_count() or 2) - 1)))
+    if workers <= 1 or len(jobs) == 1:
+        return [_sample_job(j) for j in jobs]
+    with ProcessPoolExecutor(workers) as ex:
+        return list(ex.map(_sample_job, jobs))
+
+
+def load_state_into(layer, hh: int, st: dict) -> None:
+    """Copy an oracle snapshot into row hh of a GPU layer."""
+    n = st["n"]
+    dev = layer.k.device
+    if n == 0:
+        return
+    layer.k[hh, :n] = torch.from_numpy(st["k"].view(np.float16)).to(dev)
+    layer.v[hh, :n] = torch.from_numpy(st["v"].view(np.float16)).to(dev)
+    layer.scores[hh, :n] = torch.from_numpy(st["s"]).to(dev)
+    if layer.gumbel is not None:
+        layer.gumbel[hh, :n] = torch.from_numpy(st["g"]).to(dev)
+    layer.positions[hh, :n] = torch.from_numpy(st["p"]).to(dev)
+
+
+def bulk_state(layer, n: int, w: synth.Workload, gen) -> None:
+    """Fill rows [0, n) of every cache with a random plausible state."""
+    if n == 0:
+        return
+    dev = layer.k.device
+    bh = layer.bh
+    k, v = synth.bulk_kv_torch(w, 0, n, bh, gen, dev)          # [n, bh, d]
+    layer.k[:, :n] = k.transpose(0, 1)
+    layer.v[:, :n] = v.transpose(0, 1)
+    layer.scores[:, :n] = torch.rand((bh, n), generator=gen, device=dev) * 3.0 + 1e-3
+    if layer.gumbel is not None:
+        u = torch.rand((bh, n), generator=gen, device=dev, dtype=torch.float64)
+        layer.gumbel[:, :n] = (-torch.log(-torch.log(u.clamp(1e-12, 1 - 1e-12)))).float()
+    layer.positions[:, :n] = torch.arange(n, device=dev, dtype=torch.int32)[None, :]
+
+
+def ulp16(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    def ordered(x):
+        x = x.astype(np.int32)
+        return np.where(x & 0x8000, -(x & 0x7FFF), x)
+    return np.abs(ordered(a) - ordered(b))
+
+
+def ulp32(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    def ordered(x):
+        x = x.view(np.int32).astype(np.int64)
+        return np.where(x < 0, -(x & 0x7FFFFFFF), x)
+    return np.abs(ordered(a.astype(np.float32)) - ordered(b.astype(np.float32)))
+
+
+def kept_tids(init_n: int, first_tid: int, ev_log: np.ndarray) -> list[int]:
+    """Replay an eviction log: the original token position of every kept row."""
+    tids = list(range(init_n))
+    for t, e in enumerate(ev_log):
+        tids.append(first_tid + t)
+        if e >= 0:
+            tids.pop(int(e))
+    return tids
+
+
+def compare_cache(layer, hh: int, s: Sample, gpu_ev: np.ndarray, first_tid: int) -> list[str]:
+    """Differences between GPU cache hh and oracle sample s (empty list = parity)."""
+    errs = []
+    o = s.final
+    n = o["n"]
+    if not np.array_equal(gpu_ev, s.evicted):
+        bad = np.nonzero(gpu_ev != s.evicted)[0]
+        errs.append(f"hh {hh}: evicted differs at {len(bad)} steps, first t={bad[0]}: "
+                    f"gpu {gpu_ev[bad[0]]} oracle {s.evicted[bad[0]]}")
+        return errs
+    init_n = s.init["n"] if s.init else 0
+    if kept_tids(init_n, first_tid, gpu_ev) != list(o["tid"]):
+        errs.append(f"hh {hh}: kept token positions differ")
+    gk = layer.k[hh, :n].contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+    gv = layer.v[hh, :n].contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+    gs = layer.scores[hh, :n].cpu().numpy()
+    gp = layer.positions[hh, :n].cpu().numpy()
+    if not np.array_equal(gv, o["v"]):
+        errs.append(f"hh {hh}: values differ ({int((gv != o['v']).sum())} elements)")
+    ku = ulp16(gk, o["k"])
+    if ku.max(initial=0) > KEY_ULP:
+        errs.append(f"hh {hh}: keys differ by up to {ku.max()} ulp")
+    if not np.array_equal(gp, o["p"]):
+        errs.append(f"hh {hh}: positions differ")
+    rel = np.abs(gs.astype(np.float64) - o["s"]) / np.maximum(np.abs(o["s"].astype(np.float64)), 1e-30)
+    rel[(gs == 0) & (o["s"] == 0)] = 0
+    if rel.max(initial=0) > SCORE_RTOL:
+        i = int(np.argmax(rel))
+        errs.append(f"hh {hh}: score rel err {rel.max():.3g} at row {i} "
+                    f"(gpu {gs[i]!r} oracle {o['s'][i]!r})")
+    if layer.gumbel is not None:
+        gg = layer.gumbel[hh, :n].cpu().numpy()
+        gu = ulp32(gg, o["g"])
+        if gu.max(initial=0) > GUMBEL_ULP:
+            errs.append(f"hh {hh}: gumbel differs by up to {gu.max()} ulp")
+    return errs
+
+
+def run_layer(w: synth.Workload, layer_idx: int, budget: int, T: int, samples: list[Sample],
+              init_n: int | None, next_pos: int, device, cap: int | None = None,
+              bh: int | None = None, gen_seed: int = 1234, hh_base: int = 0):
+    """Step one layer launch T tokens on the GPU; sampled caches get the oracle's
+    inputs and initial states.  Returns (layer, evicted log [T, bh] numpy, counters)."""
+    import kv_cache_eviction_step_amd as kve
+    bh = bh or w.bh
+    cap = cap or budget + 1
+    kf = w.kind == "keyformer"
+    L = kve.Layer.empty(bh, cap, w.d, device, gumbel=kf, hh_base=hh_base)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(gen_seed)
+    n0 = init_n or 0
+    bulk_state(L, n0, w, gen)
+    for s in samples:
+        if s.init is not None:
+            load_state_into(L, s.hh, s.init)
+    nk, nv = synth.bulk_kv_torch(w, next_pos, T, bh, gen, device)      # [T, bh, d]
+    for s in samples:
+        nk[:, s.hh] = torch.from_numpy(s.ks.view(np.float16)).to(device)
+        nv[:, s.hh] = torch.from_numpy(s.vs.view(np.float16)).to(device)
+    ev = torch.full((T, bh), -7, dtype=torch.int32, device=device)
+    ctr = kve.Counters(n0, next_pos, next_pos)
+    prm = params_for(w, budget, 0)
+    cl = L.c_struct()
+    for t in range(T):
+        if kf:
+            kve.keyformer_step(L, nk[t], nv[t], ctr, budget, w.n_sink, prm.tau_init, prm.tau_end,
+                               prm.anneal_steps, w.rope_base, w.gumbel_seed, ev[t], c_layer=cl)
+        else:
+            kve.pyramid_step(L, nk[t], nv[t], ctr, budget, w.n_sink, w.rope_base, ev[t],
+                             c_layer=cl)
+    torch.cuda.synchronize(device)
+    return L, ev.cpu().numpy(), ctr

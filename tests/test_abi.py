@@ -1,0 +1,164 @@
+"""The C-ABI library on the host: it loads, exports what include/kve.h
+declares, rejects bad arguments before touching any device, and computes the
+pyramid schedule of the PyramidKV page ("The budget schedule")."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import kv_cache_eviction_step_amd as kve
+from kv_cache_eviction_step_amd import Counters, KveLayer
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kve.h")
+
+
+def _declared() -> list[str]:
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:int|const char \*)\s*(\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_abi():
+    assert set(_declared()) == {"keyformer_step", "pyramid_step", "pyramid_budgets",
+                                "kve_strerror"}
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", kve.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in _declared():
+        assert name in syms, f"{name} not exported"
+        assert hasattr(kve.lib(), name)
+
+
+def test_single_hip_runtime_mapped():
+    rts = kve.hip_runtimes_mapped()
+    assert len(rts) <= 1, rts
+
+
+def test_strerror():
+    assert kve.strerror(0) == "ok"
+    assert "invalid" in kve.strerror(-1)
+    assert kve.strerror(12345) == "unknown error"
+
+
+# ---------------------------------------------------------------------------
+# pyramid_budgets: "The budget schedule" (PyramidKV page)
+# ---------------------------------------------------------------------------
+
+def test_pyramid_budgets_page_example():
+    assert kve.pyramid_budgets(12, 512, 4, 2.0) == \
+        [1019, 927, 835, 742, 650, 558, 466, 374, 282, 189, 97, 5]
+
+
+@pytest.mark.parametrize("args", [(28, 512, 4, 2.0), (28, 512, 4, 1.0), (32, 4096, 4, 1.5),
+                                  (12, 512, 4, 1.5), (0, 512, 4, 2.0), (1, 77, 4, 3.0),
+                                  (64, 1000, 7, 1.77), (9, 6, 5, 2.5), (3, 8, 2, 1.0)])
+def test_pyramid_budgets_matches_oracle(args):
+    assert kve.pyramid_budgets(*args) == oracle.pyramid_budgets(*args)
+
+
+@pytest.mark.parametrize("args", [(12, 512, 4, 0.5), (12, 512, 4, float("nan")),
+                                  (-1, 512, 4, 2.0), (12, 4, 4, 2.0), (12, 512, -1, 2.0)])
+def test_pyramid_budgets_rejects(args):
+    with pytest.raises(ValueError):
+        kve.pyramid_budgets(*args)
+
+
+def test_pyramid_budgets_null_out():
+    assert kve.lib().pyramid_budgets(3, 512, 4, 2.0, None) == kve.KVE_EINVAL
+    assert kve.lib().pyramid_budgets(0, 512, 4, 2.0, None) == kve.KVE_OK
+
+
+# ---------------------------------------------------------------------------
+# host-side argument checks: no device is touched, counters stay unchanged
+# ---------------------------------------------------------------------------
+
+FAKE = 0x10000          # aligned, never dereferenced: every case fails a host check first
+
+
+def _layer(**kw) -> KveLayer:
+    base = dict(k=FAKE, v=FAKE, scores=FAKE, gumbel=FAKE, positions=FAKE, bh=8, cap=33, d=64,
+                hh_base=0)
+    base.update(kw)
+    return KveLayer(**base)
+
+
+def _kf(layer, ctr, budget=32, n_sink=4, tau_init=1.0, tau_end=2.0, anneal=64, base=1e4,
+        new_k=FAKE, new_v=FAKE):
+    return kve.lib().keyformer_step(ctypes.byref(layer) if layer is not None else None,
+                                    new_k, new_v, ctypes.byref(ctr) if ctr is not None else None,
+                                    budget, n_sink, tau_init, tau_end, anneal, base, 0, None,
+                                    None)
+
+
+BAD_CASES = {
+    "null_layer": dict(layer=None),
+    "null_k": dict(layer_kw=dict(k=None)),
+    "null_scores": dict(layer_kw=dict(scores=None)),
+    "null_positions": dict(layer_kw=dict(positions=None)),
+    "null_gumbel_keyformer": dict(layer_kw=dict(gumbel=None)),
+    "null_new_k": dict(call_kw=dict(new_k=None)),
+    "misaligned_k": dict(layer_kw=dict(k=FAKE + 2)),
+    "misaligned_new_v": dict(call_kw=dict(new_v=FAKE + 8)),
+    "d_96": dict(layer_kw=dict(d=96)),
+    "bh_0": dict(layer_kw=dict(bh=0)),
+    "cap_too_small": dict(layer_kw=dict(cap=32)),
+    "budget_le_sink": dict(call_kw=dict(budget=4, n_sink=4)),
+    "negative_sink": dict(call_kw=dict(n_sink=-1)),
+    "budget_over_max": dict(call_kw=dict(budget=20000), layer_kw=dict(cap=20001)),
+    "negative_tau": dict(call_kw=dict(tau_init=-0.1)),
+    "nan_tau": dict(call_kw=dict(tau_end=float("nan"))),
+    "negative_anneal": dict(call_kw=dict(anneal=-1)),
+    "bad_rope_base": dict(call_kw=dict(base=0.0)),
+    "n_kept_over_budget": dict(ctr=(33, 40, 40)),
+    "n_kept_negative": dict(ctr=(-1, 0, 0)),
+    "gap_without_eviction": dict(ctr=(10, 50, 50)),   # next_pos != n_kept, no eviction
+    "next_pos_below_n_kept": dict(ctr=(32, 10, 10)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BAD_CASES))
+def test_keyformer_step_rejects_before_any_launch(name):
+    case = BAD_CASES[name]
+    layer = None if case.get("layer", 1) is None else _layer(**case.get("layer_kw", {}))
+    ctr = Counters(*case.get("ctr", (32, 100, 100)))
+    rc = _kf(layer, ctr, **case.get("call_kw", {}))
+    assert rc == kve.KVE_EINVAL
+    assert (ctr.n_kept, ctr.next_pos, ctr.pos) == case.get("ctr", (32, 100, 100))
+
+
+def test_null_counters_rejected():
+    assert _kf(_layer(), None) == kve.KVE_EINVAL
+
+
+def test_pyramid_step_accepts_null_gumbel_then_needs_a_device():
+    layer = _layer(gumbel=None)
+    ctr = Counters(32, 100, 100)
+    rc = kve.lib().pyramid_step(ctypes.byref(layer), FAKE, FAKE, ctypes.byref(ctr), 32, 4, 1e4,
+                                None, None)
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; the no-device path is not reachable")
+    assert rc == kve.KVE_ENODEV                    # passed every host check
+    assert (ctr.n_kept, ctr.next_pos, ctr.pos) == (32, 100, 100)
+
+
+def test_python_binding_validates_tensors():
+    L = kve.Layer.empty(2, 9, 64, "cpu", gumbel=True)
+    with pytest.raises(ValueError):
+        kve.keyformer_step(L, torch.zeros(2, 32, dtype=torch.float16),
+                           torch.zeros(2, 64, dtype=torch.float16), Counters(0, 0, 0), 8, 2,
+                           1.0, 2.0, 8, 1e4, 0)
+    with pytest.raises(ValueError):
+        kve.Layer(torch.zeros(2, 9, 64, dtype=torch.float32), L.v, L.scores, L.gumbel,
+                  L.positions)
+    _ = np

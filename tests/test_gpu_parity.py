@@ -1,0 +1,272 @@
+"""GPU parity: the C-ABI library on gfx950 against the CPU oracle.
+
+Every case steps a full launch (all B*H caches of a layer) through
+keyformer_step / pyramid_step and compares sampled caches with the oracle on
+identical, margin-guarded inputs: evicted indices, kept token positions,
+values and positions bit-exact; keys within 1 fp16 ULP; scores within 1e-5
+relative; Gumbel values within 1 fp32 ULP.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_harness import (Sample, compare_cache, load_state_into, oracle_samples, random_state,
+                         run_layer)
+from oracle.guard import guarded_trajectory, params_for
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kv_cache_eviction_step_amd as kve
+    assert len(kve.hip_runtimes_mapped()) == 1, kve.hip_runtimes_mapped()
+    return torch.device("cuda:0")
+
+
+def _say(msg: str) -> None:
+    print(msg, flush=True)
+
+
+def _assert_parity(L, ev, samples, first_tid):
+    errs = []
+    for s in samples:
+        errs += compare_cache(L, s.hh, s, ev[:, s.hh], first_tid)
+    assert not errs, "\n".join(errs[:20])
+
+
+# ---------------------------------------------------------------------------
+# the tiny workload, both temperature runs, every cache, full trajectory
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("w", [synth.WORKLOADS[0], synth.TINY_ANNEALED], ids=lambda w: w.name)
+def test_tiny_full_trajectory(dev, w):
+    _say(f"[tiny] {w.name} bh={w.bh} d={w.d} budget={w.budget} T={w.tokens}")
+    samples = oracle_samples(w, 0, range(w.bh), w.budget, w.tokens, w.budget + 1, workers=1)
+    L, ev, ctr = run_layer(w, 0, w.budget, w.tokens, samples, None, 0, dev)
+    _assert_parity(L, ev, samples, 0)
+    assert (ctr.n_kept, ctr.next_pos, ctr.pos) == (w.budget, w.tokens, w.tokens)
+
+
+# ---------------------------------------------------------------------------
+# single steps from random states: edge cases of the eviction index
+# ---------------------------------------------------------------------------
+
+def _edge_workload(d, kind):
+    if kind == "kf":
+        return synth.Workload(f"edge{d}kf", 1, 1, 6, d, 64, 0, 32, 4, "keyformer", 1.0, 2.0, 64)
+    return synth.Workload(f"edge{d}pk", 1, 1, 6, d, 64, 0, 32, 4, "pyramid")
+
+
+def _forced(w, hh, n, cap, next_pos, target):
+    """Random state whose eviction is steered to row `target`.
+
+    Keyformer: the target gets score 0 and a Gumbel value far below any other.
+    H2O / PyramidKV: every stored row gains mass, so the new row (score 0)
+    always loses -- unless the target's key points so far away from the
+    incoming key that its softmax weight underflows to exactly 0 in fp32 on
+    both sides; then it ties the new row at 0 and the lower index goes."""
+    c = random_state(w, 0, hh, n, cap, next_pos, seed=hh + 17)
+    if target is not None and target < n:
+        c.s[target] = 0.0
+        if w.kind == "keyformer":
+            c.g[target] = -12.0
+        else:
+            knew = synth.token_kv(w, 0, hh, [next_pos])[0][0].view(np.float16).astype(np.float32)
+            c.k[target] = (-40.0 * knew).astype(np.float16).view(np.uint16)
+    return c
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("kind", ["kf", "pk"])
+@pytest.mark.parametrize("n,budget,n_sink,target", [
+    (0, 8, 2, None),          # bootstrap: first token only appended
+    (5, 8, 2, None),          # under budget: score + append, no eviction
+    (7, 8, 0, None),          # reaches budget exactly, no eviction
+    (8, 8, 0, 0),             # n_sink 0: row 0 is evictable
+    (8, 8, 3, 3),             # evict the first non-sink row
+    (40, 40, 4, 20),          # middle row
+    (40, 40, 4, 39),          # the newest stored row
+    (40, 40, 4, None),        # whatever the keys decide (new row included)
+    (300, 300, 4, 4),         # spans two score sweeps; every row after 4 moves
+    (1000, 1000, 4, 517),     # several sweeps and move chunks, ragged tails
+    (1000, 1000, 4, 998),
+])
+def test_single_step_edges(dev, d, kind, n, budget, n_sink, target):
+    import kv_cache_eviction_step_amd as kve
+    w = _edge_workload(d, kind)
+    w = synth.Workload(w.name, 1, 1, 6, d, 64, 0, budget, n_sink, w.kind, w.tau_init,
+                       w.tau_end, w.anneal_steps)
+    cap = budget + 5                                  # rows past budget + 1 are sentinels
+    next_pos = n if n < budget else 5000 + n
+    _say(f"[edge] d={d} kind={kind} n={n} budget={budget} n_sink={n_sink} target={target}")
+    bh = w.bh
+    samples = []
+    exact_tie = kind == "pk" and target is not None and n >= budget
+    for hh in range(bh):
+        c = _forced(w, hh, n, cap, next_pos, target)
+        init = c.snapshot()
+        tr = guarded_trajectory(w, 0, hh, budget, 1, cap=cap, t0=next_pos, cache=c,
+                                params=params_for(w, budget, hh),
+                                min_margin_rel=-1.0 if exact_tie else 1e-4)
+        samples.append(Sample(hh, budget, init, tr.ks, tr.vs, tr.evicted, tr.cache.snapshot(),
+                              int(tr.attempts.sum())))
+        if target is not None and n >= budget:
+            assert tr.evicted[0] == target
+    L = kve.Layer.empty(bh, cap, d, dev, gumbel=(kind == "kf"))
+    sentinel_k = torch.full((bh, cap, d), 12345.0, dtype=torch.float16, device=dev)
+    L.k.copy_(sentinel_k)
+    L.v.fill_(-7.0)
+    L.scores.fill_(-3.0)
+    L.positions.fill_(-99)
+    if L.gumbel is not None:
+        L.gumbel.fill_(99.0)
+    for s in samples:
+        load_state_into(L, s.hh, s.init)
+    nk = torch.stack([torch.from_numpy(s.ks[0].view(np.float16)) for s in samples]).to(dev)
+    nv = torch.stack([torch.from_numpy(s.vs[0].view(np.float16)) for s in samples]).to(dev)
+    ev = torch.full((bh,), -7, dtype=torch.int32, device=dev)
+    ctr = kve.Counters(n, next_pos, next_pos)
+    prm = params_for(w, budget, 0)
+    if kind == "kf":
+        kve.keyformer_step(L, nk, nv, ctr, budget, n_sink, prm.tau_init, prm.tau_end,
+                           prm.anneal_steps, w.rope_base, w.gumbel_seed, ev)
+    else:
+        kve.pyramid_step(L, nk, nv, ctr, budget, n_sink, w.rope_base, ev)
+    torch.cuda.synchronize()
+    evn = ev.cpu().numpy()[None, :]
+    _assert_parity(L, evn, samples, next_pos)
+    assert ctr.n_kept == min(n + 1, budget)
+    # nothing written past row n (the slot the new row may take) in any cache
+    assert torch.equal(L.k[:, n + 1:], sentinel_k[:, n + 1:])
+    assert bool((L.v[:, n + 1:] == -7.0).all())
+    assert bool((L.scores[:, n + 1:] == -3.0).all())
+    assert bool((L.positions[:, n + 1:] == -99).all())
+    if L.gumbel is not None:
+        assert bool((L.gumbel[:, n + 1:] == 99.0).all())
+
+
+# ---------------------------------------------------------------------------
+# whole trajectories at the Llama-3.2-3B shapes (8 caches, D = 128)
+# ---------------------------------------------------------------------------
+
+def test_keyformer_trajectory_llama_shape(dev):
+    w = synth.WORKLOADS[1]
+    T = 760                                            # 512 appends, then 248 evicting steps
+    _say(f"[traj] {w.name} layer 3 bh={w.bh} budget={w.budget} T={T}")
+    samples = oracle_samples(w, 3, range(w.bh), w.budget, T, w.budget + 1)
+    L, ev, _ = run_layer(w, 3, w.budget, T, samples, None, 0, dev)
+    _assert_parity(L, ev, samples, 0)
+    assert (ev[w.budget:] < w.budget).any()            # interior evictions happened
+
+
+@pytest.mark.parametrize("layer", [0, 27])
+def test_pyramid_trajectory_llama_shape(dev, layer):
+    w = synth.WORKLOADS[2]
+    budget = oracle.pyramid_budgets(w.layers, w.budget, w.n_sink, w.beta)[layer]
+    T = budget + 200
+    _say(f"[traj] {w.name} layer {layer} budget={budget} T={T}")
+    samples = oracle_samples(w, layer, range(w.bh), budget, T, budget + 1)
+    L, ev, _ = run_layer(w, layer, budget, T, samples, None, 0, dev)
+    _assert_parity(L, ev, samples, 0)
+
+
+def test_beta_one_pyramid_is_h2o_bit_for_bit(dev):
+    """PyramidKV at beta = 1 (every layer the average budget) and Keyformer at
+    tau = 0 are the same H2O step: identical GPU states, bit for bit."""
+    import kv_cache_eviction_step_amd as kve
+    w = synth.WORKLOADS[2]
+    budget = kve.pyramid_budgets(w.layers, w.budget, w.n_sink, 1.0)[5]
+    assert budget == w.budget
+    T = 700
+    _say(f"[beta1] bh={w.bh} budget={budget} T={T}")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    nk, nv = synth.bulk_kv_torch(w, 0, T, w.bh, gen, dev)
+    A = kve.Layer.empty(w.bh, budget + 1, w.d, dev, gumbel=False)
+    B = kve.Layer.empty(w.bh, budget + 1, w.d, dev, gumbel=True)
+    ca, cb = kve.Counters(0, 0, 0), kve.Counters(0, 0, 0)
+    eva = torch.empty((T, w.bh), dtype=torch.int32, device=dev)
+    evb = torch.empty_like(eva)
+    for t in range(T):
+        kve.pyramid_step(A, nk[t], nv[t], ca, budget, w.n_sink, w.rope_base, eva[t])
+        kve.keyformer_step(B, nk[t], nv[t], cb, budget, w.n_sink, 0.0, 0.0, 0, w.rope_base,
+                           123, evb[t])
+    torch.cuda.synchronize()
+    assert torch.equal(eva, evb)
+    n = ca.n_kept
+    for name in ("k", "v", "scores", "positions"):
+        assert torch.equal(getattr(A, name)[:, :n], getattr(B, name)[:, :n]), name
+
+
+# ---------------------------------------------------------------------------
+# full launch sizes: every cache of the layer stepped, sampled caches checked
+# ---------------------------------------------------------------------------
+
+def test_full_size_batched_late_riser(dev):
+    w = synth.WORKLOADS[3]                             # B*H = 256, budget 1024, D = 128
+    T, next_pos = 40, w.prompt
+    hhs = [0, 37, 128, 255]
+    _say(f"[full] {w.name} bh={w.bh} cap={w.budget + 1} sampled={hhs} T={T}")
+    samples = oracle_samples(w, 9, hhs, w.budget, T, w.budget + 1, init_n=w.budget,
+                             next_pos=next_pos)
+    L, ev, _ = run_layer(w, 9, w.budget, T, samples, w.budget, next_pos, dev)
+    _assert_parity(L, ev, samples, next_pos)
+    assert ((ev >= 0) & (ev < w.budget)).any()
+
+
+@pytest.mark.parametrize("layer", [0, 31])
+def test_full_size_long_context(dev, layer):
+    w = synth.WORKLOADS[4]                             # B*H = 512, budgets 6144 .. 2048
+    budget = oracle.pyramid_budgets(w.layers, w.budget, w.n_sink, w.beta)[layer]
+    T, next_pos = 16, w.prompt
+    hhs = [0, 311, 511]
+    _say(f"[full] {w.name} layer {layer} bh={w.bh} budget={budget} sampled={hhs} T={T}")
+    samples = oracle_samples(w, layer, hhs, budget, T, budget + 1, init_n=budget,
+                             next_pos=next_pos)
+    L, ev, _ = run_layer(w, layer, budget, T, samples, budget, next_pos, dev)
+    _assert_parity(L, ev, samples, next_pos)
+
+
+# ---------------------------------------------------------------------------
+# determinism and split launches
+# ---------------------------------------------------------------------------
+
+def test_deterministic_and_split_bh_launches(dev):
+    """Two identical runs give identical bits; splitting the B*H set into two
+    launches (hh_base offsets the Gumbel streams) gives the same result."""
+    import kv_cache_eviction_step_amd as kve
+    w = synth.TINY_ANNEALED
+    w = synth.Workload("split", 1, 1, 16, 128, 300, 0, 64, 4, "keyformer", 1.0, 2.0, 100)
+    T = 300
+    _say(f"[split] bh={w.bh} budget={w.budget} T={T}")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(3)
+    nk, nv = synth.bulk_kv_torch(w, 0, T, w.bh, gen, dev)
+
+    def run_whole():
+        L = kve.Layer.empty(w.bh, w.budget + 1, w.d, dev)
+        c = kve.Counters(0, 0, 0)
+        for t in range(T):
+            kve.keyformer_step(L, nk[t], nv[t], c, w.budget, w.n_sink, 1.0, 2.0, 100, 1e4, 9)
+        return L
+
+    a, b = run_whole(), run_whole()
+    halves = [kve.Layer.empty(8, w.budget + 1, w.d, dev, hh_base=8 * i) for i in range(2)]
+    cs = [kve.Counters(0, 0, 0), kve.Counters(0, 0, 0)]
+    for t in range(T):
+        for i in range(2):
+            kve.keyformer_step(halves[i], nk[t, 8 * i:8 * i + 8].contiguous(),
+                               nv[t, 8 * i:8 * i + 8].contiguous(), cs[i], w.budget, w.n_sink,
+                               1.0, 2.0, 100, 1e4, 9)
+    torch.cuda.synchronize()
+    for name in ("k", "v", "scores", "gumbel", "positions"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+        joined = torch.cat([getattr(halves[0], name), getattr(halves[1], name)])
+        assert torch.equal(getattr(a, name), joined), name

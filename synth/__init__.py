@@ -217,3 +217,27 @@ def bulk_kv_torch(w: Workload, t0: int, count: int, bh: int, gen, device,
     out_k.copy_(key)
     out_v.copy_(vraw)
     return out_k, out_v
+
+
+def bulk_state_torch(k, v, scores, gumbel, positions, n: int, w: Workload, gen) -> None:
+    """Fill rows [0, n) of every cache with a plausible mid-run state.
+
+    k, v: fp16 [bh, cap, d]; scores, gumbel: fp32 [bh, cap] (gumbel may be None);
+    positions: int32 [bh, cap].  Keys and values follow the recipe above at
+    positions 0..n-1; scores are positive (uniform in [1e-3, 3)); Gumbel values
+    are standard Gumbel draws (minus the log of a unit exponential draw);
+    positions equal the row index.
+    """
+    import torch
+    if n == 0:
+        return
+    dev = k.device
+    bh = k.shape[0]
+    kk, vv = bulk_kv_torch(w, 0, n, bh, gen, dev)          # [n, bh, d]
+    k[:, :n] = kk.transpose(0, 1)
+    v[:, :n] = vv.transpose(0, 1)
+    scores[:, :n] = torch.rand((bh, n), generator=gen, device=dev) * 3.0 + 1e-3
+    if gumbel is not None:
+        e = torch.empty((bh, n), device=dev, dtype=torch.float32).exponential_(generator=gen)
+        gumbel[:, :n] = -torch.log(e)
+    positions[:, :n] = torch.arange(n, device=dev, dtype=torch.int32)[None, :]

@@ -97,19 +97,9 @@ def load_state_into(layer, hh: int, st: dict) -> None:
 
 
 def bulk_state(layer, n: int, w: synth.Workload, gen) -> None:
-    """Fill rows [0, n) of every cache with a random plausible state."""
-    if n == 0:
-        return
-    dev = layer.k.device
-    bh = layer.bh
-    k, v = synth.bulk_kv_torch(w, 0, n, bh, gen, dev)          # [n, bh, d]
-    layer.k[:, :n] = k.transpose(0, 1)
-    layer.v[:, :n] = v.transpose(0, 1)
-    layer.scores[:, :n] = torch.rand((bh, n), generator=gen, device=dev) * 3.0 + 1e-3
-    if layer.gumbel is not None:
-        u = torch.rand((bh, n), generator=gen, device=dev, dtype=torch.float64)
-        layer.gumbel[:, :n] = (-torch.log(-torch.log(u.clamp(1e-12, 1 - 1e-12)))).float()
-    layer.positions[:, :n] = torch.arange(n, device=dev, dtype=torch.int32)[None, :]
+    """Fill rows [0, n) of every cache of a GPU layer with a random plausible state."""
+    synth.bulk_state_torch(layer.k, layer.v, layer.scores, layer.gumbel, layer.positions, n, w,
+                           gen)
 
 
 def ulp16(a: np.ndarray, b: np.ndarray) -> np.ndarray:

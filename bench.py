@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--fill", choices=["synthetic", "real"], default="synthetic",
                     help="reach the steady state by synthesising it (default) or by "
                          "stepping the prompt through the real step")
+    ap.add_argument("--batched", action="store_true",
+                    help="one launch per token for all layers (keyformer_step_layers / "
+                         "pyramid_step_layers) instead of one launch per layer")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the CPU oracle baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -62,10 +65,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(config: int):
+def measured_traffic(config: int, batched: bool):
     """HBM bytes per launch from the committed rocprofv3 counter summary of this
     workload, or None when it is missing or the kernel changed since."""
-    path = os.path.join(ROOT, "profiles", f"step_kernel_configs{config}_pmc_traffic.md")
+    kern = "step_layers_kernel" if batched else "step_kernel"
+    path = os.path.join(ROOT, "profiles", f"{kern}_configs{config}_pmc_traffic.md")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -209,17 +213,35 @@ def main():
     n_prev = [[0] * L for _ in range(args.steps)]
     torch.cuda.synchronize()
 
+    batch = None
+    if args.batched:
+        batch = kve.LayerBatch(layers, budgets, ctrs)
+
+    def step_all(s, evs=None):
+        """One token through every layer: one launch, or one per layer."""
+        if batch is not None:
+            if kf:
+                kve.keyformer_step_layers(batch, nk[s], nv[s], w.n_sink, w.tau_init, w.tau_end,
+                                          w.anneal_steps, w.rope_base, w.gumbel_seed, evs)
+            else:
+                kve.pyramid_step_layers(batch, nk[s], nv[s], w.n_sink, w.rope_base, evs)
+        else:
+            for l in range(L):
+                step_layer(l, nk[s, l], nv[s, l], evs[l] if evs is not None else None)
+
+    def counters(l):
+        return batch.ctrs[l] if batch is not None else ctrs[l]
+
     for s in range(args.warmup):
-        for l in range(L):
-            step_layer(l, nk[s, l], nv[s, l])
+        step_all(s)
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
     for s in range(args.steps):
         for l in range(L):
-            n_prev[s][l] = ctrs[l].n_kept
-            step_layer(l, nk[args.warmup + s, l], nv[args.warmup + s, l], ev[s, l])
+            n_prev[s][l] = counters(l).n_kept
+        step_all(args.warmup + s, ev[s])
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
@@ -233,7 +255,7 @@ def main():
             e = evn[s, l]
             m = np.where((e >= 0) & (e < n), n - e, 0).astype(np.int64)
             total_bytes += int(step_bytes(w.kind, n, d, m).sum())
-    launches = args.steps * L
+    launches = args.steps * (1 if batch is not None else L)
     sec = ms / 1e3
     updates = bh * L * args.steps
     avg_launch_s = sec / launches
@@ -267,11 +289,15 @@ def main():
             "kv_storage": "f16", "bh_per_launch": bh, "layers": L,
             "budgets": [budgets[0], budgets[-1]], "steady_state_fill": args.fill,
             "fill_seconds": round(t_fill, 1), "mean_rows_moved_per_cache_step": mean_m,
+            "launch": ("one launch per token over all layers (" +
+                       ("keyformer" if kf else "pyramid") + "_step_layers)") if batch is not None
+                      else "one launch per layer (" + ("keyformer" if kf else "pyramid") + "_step)",
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(args.config),
-            "kernel": "kve::step_kernel", "avg_launch_us": avg_launch_s * 1e6,
+            "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(args.config, args.batched),
+            "kernel": "kve::step_layers_kernel" if batch is not None else "kve::step_kernel",
+            "avg_launch_us": avg_launch_s * 1e6,
             "algorithmic_bytes_per_launch": bytes_per_launch,
         },
         "cpu_baseline": cpu,

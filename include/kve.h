@@ -30,8 +30,9 @@
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and the call returns without synchronising.  Results are visible to
  *     later work on the same stream; synchronise before reading elsewhere.
- *   - Per call the library allocates nothing and keeps no state besides
- *     small per-thread caches of rotation frequencies; calls are reentrant.
+ *   - The per-layer calls allocate nothing and keep no state besides small
+ *     per-thread caches of rotation frequencies; they are reentrant.  The
+ *     batched calls also use a per-device descriptor ring (see below).
  *   - Arguments are checked on the host before anything is enqueued.  A
  *     failing check returns KVE_EINVAL and leaves the counters and every
  *     tensor untouched.  A device fault is asynchronous and surfaces at the
@@ -92,7 +93,7 @@ typedef struct kve_counters {
  *   new_v      fp16 [bh][d] device: incoming values
  *   ctr        host counters; on success n_kept = min(n_kept + 1, budget),
  *              next_pos += 1, pos += 1
- *   budget     rows kept at most, sinks included; budget > n_sink
+ *   budget     rows kept at most, sinks included; n_sink < budget <= 12288
  *   n_sink     leading rows never evicted; >= 0
  *   tau_init, tau_end, anneal_steps
  *              temperature tau = tau_init + min(pos, anneal_steps) *
@@ -127,6 +128,45 @@ int keyformer_step(const kve_layer *L, const void *new_k, const void *new_v,
 int pyramid_step(const kve_layer *L, const void *new_k, const void *new_v,
                  kve_counters *ctr, int32_t budget, int32_t n_sink, double rope_base,
                  int32_t *evicted, void *stream);
+
+/*
+ * keyformer_step_layers / pyramid_step_layers -- the same step for several
+ * layers of one token in ONE launch: equivalent, bit for bit, to calling
+ * keyformer_step / pyramid_step once per layer (in any order; the layers are
+ * independent, as the PyramidKV page's "How it works" notes that layers never
+ * exchange data).  One launch over all layers keeps every compute unit busy
+ * while some caches finish their compaction, which per-layer launches of a
+ * few hundred caches cannot.
+ *
+ *   n_layers   1 .. 128
+ *   layers     HOST array [n_layers] of layer descriptors (all with the same d;
+ *              bh, cap and hh_base may differ); the layers must not overlap
+ *   new_k,new_v  HOST arrays [n_layers] of device pointers, fp16 [bh_l][d]
+ *   ctrs       HOST array [n_layers] of counters, each updated as by the
+ *              per-layer call
+ *   budgets    HOST array [n_layers]: budget of each layer (for example from
+ *              pyramid_budgets)
+ *   evicted    HOST array [n_layers] of device i32 [bh_l] outputs (entries may
+ *              be NULL), or NULL
+ *   n_sink, tau_*, anneal_steps, rope_base, seed, stream: as per layer, shared
+ * Every layer is checked before anything is enqueued; on KVE_EINVAL no
+ * counter changes.  The descriptors reach the device through a ring of 64
+ * pinned host / device slots per device, allocated on the first batched call
+ * on that device (a failed allocation returns KVE_ELAUNCH); a call blocks
+ * the host only if the device is 64 batched calls behind.  Calls from several
+ * threads are serialised on that ring.  Not for use under stream capture
+ * (the descriptor copies read the ring at replay time).
+ */
+int keyformer_step_layers(int32_t n_layers, const kve_layer *layers, const void *const *new_k,
+                          const void *const *new_v, kve_counters *ctrs, const int32_t *budgets,
+                          int32_t n_sink, double tau_init, double tau_end,
+                          int32_t anneal_steps, double rope_base, uint64_t seed,
+                          int32_t *const *evicted, void *stream);
+
+int pyramid_step_layers(int32_t n_layers, const kve_layer *layers, const void *const *new_k,
+                        const void *const *new_v, kve_counters *ctrs, const int32_t *budgets,
+                        int32_t n_sink, double rope_base, int32_t *const *evicted,
+                        void *stream);
 
 /*
  * pyramid_budgets -- per-layer budgets ("The budget schedule"): a linear taper

@@ -10,6 +10,10 @@ Calls (same names as the C ABI):
                    anneal_steps, rope_base, seed, evicted=None, stream=None)
     pyramid_step(layer, new_k, new_v, ctr, budget, n_sink, rope_base,
                  evicted=None, stream=None)
+    keyformer_step_layers(batch, new_k, new_v, n_sink, tau_init, tau_end,
+                          anneal_steps, rope_base, seed, evicted=None, stream=None)
+    pyramid_step_layers(batch, new_k, new_v, n_sink, rope_base, evicted=None,
+                        stream=None)
     pyramid_budgets(n_layers, avg_budget, n_sink, beta) -> list[int]
 """
 from __future__ import annotations
@@ -61,13 +65,24 @@ _lib.pyramid_step.restype = ctypes.c_int
 _lib.pyramid_step.argtypes = [
     ctypes.POINTER(KveLayer), ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(Counters),
     ctypes.c_int32, ctypes.c_int32, ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p]
+_lib.keyformer_step_layers.restype = ctypes.c_int
+_lib.keyformer_step_layers.argtypes = [
+    ctypes.c_int32, ctypes.POINTER(KveLayer), ctypes.c_void_p, ctypes.c_void_p,
+    ctypes.POINTER(Counters), ctypes.c_void_p, ctypes.c_int32, ctypes.c_double, ctypes.c_double,
+    ctypes.c_int32, ctypes.c_double, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+_lib.pyramid_step_layers.restype = ctypes.c_int
+_lib.pyramid_step_layers.argtypes = [
+    ctypes.c_int32, ctypes.POINTER(KveLayer), ctypes.c_void_p, ctypes.c_void_p,
+    ctypes.POINTER(Counters), ctypes.c_void_p, ctypes.c_int32, ctypes.c_double, ctypes.c_void_p,
+    ctypes.c_void_p]
 _lib.pyramid_budgets.restype = ctypes.c_int
 _lib.pyramid_budgets.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                  ctypes.c_double, ctypes.c_void_p]
 _lib.kve_strerror.restype = ctypes.c_char_p
 _lib.kve_strerror.argtypes = [ctypes.c_int]
 
-EXPORTED = ("keyformer_step", "pyramid_step", "pyramid_budgets", "kve_strerror")
+EXPORTED = ("keyformer_step", "pyramid_step", "keyformer_step_layers", "pyramid_step_layers",
+            "pyramid_budgets", "kve_strerror")
 
 
 def lib() -> ctypes.CDLL:
@@ -183,6 +198,94 @@ def pyramid_step(layer: Layer, new_k, new_v, ctr: Counters, budget: int, n_sink:
                            _rows(new_v, layer, "new_v"), ctypes.byref(ctr), budget, n_sink,
                            rope_base, _evicted_ptr(evicted, layer), _stream_ptr(stream, layer))
     _check(rc, "pyramid_step")
+
+
+class LayerBatch:
+    """Several layers stepped together by keyformer_step_layers / pyramid_step_layers.
+
+    Holds the host arrays the batched C calls take: layer descriptors, per-layer
+    budgets and per-layer counters (``ctrs[l]``, updated by every call).
+    """
+
+    def __init__(self, layers: list[Layer], budgets: list[int],
+                 counters: list[Counters] | None = None):
+        if not layers or len(layers) != len(budgets):
+            raise ValueError("one budget per layer")
+        n = len(layers)
+        self.layers = layers
+        self.n = n
+        self.c_layers = (KveLayer * n)(*[x.c_struct() for x in layers])
+        self.budgets = (ctypes.c_int32 * n)(*budgets)
+        self.ctrs = (Counters * n)()
+        for i, c in enumerate(counters or []):
+            self.ctrs[i] = c
+        self._pk = (ctypes.c_void_p * n)()
+        self._pv = (ctypes.c_void_p * n)()
+        self._pe = (ctypes.c_void_p * n)()
+        dev = layers[0].k.device
+        if any(x.k.device != dev for x in layers):
+            raise ValueError("all layers must be on one device")
+        self.device = dev
+
+    def _fill(self, new_k, new_v, evicted):
+        """Pointer arrays for this call.  new_k / new_v: a list of [bh_l, d]
+        tensors, or one contiguous [n_layers, bh, d] tensor; evicted: None, a
+        list of [bh_l] int32 tensors, or one contiguous [n_layers, bh] tensor."""
+        n = self.n
+        for arr, src, name in ((self._pk, new_k, "new_k"), (self._pv, new_v, "new_v")):
+            if isinstance(src, torch.Tensor):
+                L0 = self.layers[0]
+                if (src.dtype != torch.float16 or src.dim() != 3 or src.shape[0] != n or
+                        not src.is_contiguous() or src.device != self.device or
+                        any(tuple(src.shape[1:]) != (x.bh, x.d) for x in self.layers)):
+                    raise ValueError(f"{name} must be contiguous float16 [{n}, {L0.bh}, {L0.d}]")
+                base, step = src.data_ptr(), src.stride(0) * 2
+                for i in range(n):
+                    arr[i] = base + i * step
+            else:
+                if len(src) != n:
+                    raise ValueError(f"{name}: one tensor per layer")
+                for i in range(n):
+                    arr[i] = _rows(src[i], self.layers[i], name)
+        if evicted is None:
+            return None
+        if isinstance(evicted, torch.Tensor):
+            if (evicted.dtype != torch.int32 or evicted.dim() != 2 or evicted.shape[0] != n or
+                    not evicted.is_contiguous() or evicted.device != self.device or
+                    any(evicted.shape[1] != x.bh for x in self.layers)):
+                raise ValueError("evicted must be contiguous int32 [n_layers, bh]")
+            base, step = evicted.data_ptr(), evicted.stride(0) * 4
+            for i in range(n):
+                self._pe[i] = base + i * step
+        else:
+            if len(evicted) != n:
+                raise ValueError("evicted: one tensor (or None) per layer")
+            for i in range(n):
+                self._pe[i] = (_evicted_ptr(evicted[i], self.layers[i])
+                               if evicted[i] is not None else None)
+        return self._pe
+
+
+def keyformer_step_layers(batch: LayerBatch, new_k, new_v, n_sink: int, tau_init: float,
+                          tau_end: float, anneal_steps: int, rope_base: float, seed: int,
+                          evicted=None, stream=None) -> None:
+    """One token into every cache of every layer of `batch`, in one launch."""
+    pe = batch._fill(new_k, new_v, evicted)
+    rc = _lib.keyformer_step_layers(batch.n, batch.c_layers, batch._pk, batch._pv, batch.ctrs,
+                                    batch.budgets, n_sink, tau_init, tau_end, anneal_steps,
+                                    rope_base, seed & 0xFFFFFFFFFFFFFFFF, pe,
+                                    _stream_ptr(stream, batch.layers[0]))
+    _check(rc, "keyformer_step_layers")
+
+
+def pyramid_step_layers(batch: LayerBatch, new_k, new_v, n_sink: int, rope_base: float,
+                        evicted=None, stream=None) -> None:
+    """One token into every cache of every layer of `batch` (H2O / PyramidKV), one launch."""
+    pe = batch._fill(new_k, new_v, evicted)
+    rc = _lib.pyramid_step_layers(batch.n, batch.c_layers, batch._pk, batch._pv, batch.ctrs,
+                                  batch.budgets, n_sink, rope_base, pe,
+                                  _stream_ptr(stream, batch.layers[0]))
+    _check(rc, "pyramid_step_layers")
 
 
 def pyramid_budgets(n_layers: int, avg_budget: int, n_sink: int, beta: float) -> list[int]:

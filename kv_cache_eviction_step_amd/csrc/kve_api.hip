@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "kve.h"
 #include "kve_step.h"
@@ -15,9 +16,9 @@
 
 namespace {
 
-// Largest budget a cache may have: the kernel keeps two fp32 values per
-// stored row in LDS (at most 128 KiB of gfx950's 160 KiB).
-constexpr int32_t kMaxBudget = 16384;
+// Largest budget a cache may have: the kernel keeps three fp32 values per
+// stored row in LDS (logit, score, gumbel): at most ~145 KiB of gfx950's 160 KiB.
+constexpr int32_t kMaxBudget = 12288;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -61,11 +62,10 @@ int check_device() {
   return s == 1 ? KVE_OK : KVE_ENODEV;
 }
 
-int step_impl(const kve_layer *L, const void *new_k, const void *new_v, kve_counters *ctr,
-              int32_t budget, int32_t n_sink, double tau_init, double tau_end,
-              int32_t anneal_steps, double rope_base, uint64_t seed, int32_t *evicted,
-              void *stream, bool gumbel) {
-  // ---- host-side checks (init_keyformer_state's guards and the layout) ----
+// Host-side checks shared by every entry point (init_keyformer_state's guards
+// and the layout); returns KVE_OK or KVE_EINVAL.
+int check_layer(const kve_layer *L, const void *new_k, const void *new_v,
+                const kve_counters *ctr, int32_t budget, int32_t n_sink, bool gumbel) {
   if (!L || !ctr || !new_k || !new_v) return KVE_EINVAL;
   if (!L->k || !L->v || !L->scores || !L->positions) return KVE_EINVAL;
   if (gumbel && !L->gumbel) return KVE_EINVAL;
@@ -75,22 +75,27 @@ int step_impl(const kve_layer *L, const void *new_k, const void *new_v, kve_coun
   if (L->bh < 1 || L->hh_base < 0 || (int64_t)L->hh_base + L->bh > INT32_MAX) return KVE_EINVAL;
   if (n_sink < 0 || budget <= n_sink || budget > kMaxBudget) return KVE_EINVAL;
   if (L->cap < budget + 1) return KVE_EINVAL;
-  if (!(tau_init >= 0.0) || !(tau_end >= 0.0) || !std::isfinite(tau_init) ||
-      !std::isfinite(tau_end) || anneal_steps < 0)
-    return KVE_EINVAL;
-  if (!(rope_base > 0.0) || !std::isfinite(rope_base)) return KVE_EINVAL;
   const int32_t n = ctr->n_kept;
   if (n < 0 || n > budget) return KVE_EINVAL;
   if (ctr->pos < 0 || ctr->next_pos < n || ctr->next_pos == INT32_MAX || ctr->pos == INT32_MAX)
     return KVE_EINVAL;
-  const bool over = n + 1 > budget;
   // without an eviction the new row keeps next_pos, which must equal its slot
-  if (!over && ctr->next_pos != n) return KVE_EINVAL;
+  if (n + 1 <= budget && ctr->next_pos != n) return KVE_EINVAL;
+  return KVE_OK;
+}
 
-  const int dev = check_device();
-  if (dev != KVE_OK) return dev;
+int check_shared(double tau_init, double tau_end, int32_t anneal_steps, double rope_base) {
+  if (!(tau_init >= 0.0) || !(tau_end >= 0.0) || !std::isfinite(tau_init) ||
+      !std::isfinite(tau_end) || anneal_steps < 0)
+    return KVE_EINVAL;
+  if (!(rope_base > 0.0) || !std::isfinite(rope_base)) return KVE_EINVAL;
+  return KVE_OK;
+}
 
-  kve::StepArgs a;
+kve::LayerArgs layer_args(const kve_layer *L, const void *new_k, const void *new_v,
+                          const kve_counters *ctr, int32_t budget, int32_t *evicted,
+                          bool gumbel) {
+  kve::LayerArgs a;
   std::memset(&a, 0, sizeof(a));
   a.k = L->k;
   a.v = L->v;
@@ -101,38 +106,183 @@ int step_impl(const kve_layer *L, const void *new_k, const void *new_v, kve_coun
   a.new_v = new_v;
   a.evicted = evicted;
   a.cap = L->cap;
-  a.n_prev = n;
+  a.n_prev = ctr->n_kept;
   a.budget = budget;
-  a.n_sink = n_sink;
   a.next_pos = ctr->next_pos;
   a.pos = ctr->pos;
-  a.anneal_steps = anneal_steps;
   a.hh_base = L->hh_base;
-  a.tau_init = gumbel ? tau_init : 0.0;
-  a.tau_end = gumbel ? tau_end : 0.0;
-  a.seed = seed;
-  a.scale = (float)(1.0 / std::sqrt((double)L->d));
-  if (over) {
-    // keyformer FIXED GAP #2: moved rows go back one position; the incoming
-    // row, if it survives an older row's eviction, goes from next_pos to n-1
-    const FreqCache &fc = freqs(L->d, rope_base);
-    const double delta_new = (double)(n - 1) - (double)ctr->next_pos;
-    for (int j = 0; j < L->d / 2; ++j) {
-      a.rope.cos_m1[j] = fc.cos_m1[j];
-      a.rope.sin_m1[j] = fc.sin_m1[j];
-      const double th = delta_new * fc.freq[j];
-      a.rope.cos_new[j] = (float)std::cos(th);
-      a.rope.sin_new[j] = (float)std::sin(th);
-    }
+  return a;
+}
+
+kve::SharedArgs shared_args(int d, int32_t n_sink, double tau_init, double tau_end,
+                            int32_t anneal_steps, double rope_base, uint64_t seed, bool gumbel) {
+  kve::SharedArgs sa;
+  std::memset(&sa, 0, sizeof(sa));
+  sa.n_sink = n_sink;
+  sa.anneal_steps = anneal_steps;
+  sa.tau_init = gumbel ? tau_init : 0.0;
+  sa.tau_end = gumbel ? tau_end : 0.0;
+  sa.seed = seed;
+  sa.scale = (float)(1.0 / std::sqrt((double)d));
+  // keyformer FIXED GAP #2: moved stored rows go back one position
+  const FreqCache &fc = freqs(d, rope_base);
+  for (int j = 0; j < d / 2; ++j) {
+    sa.back1.c[j] = fc.cos_m1[j];
+    sa.back1.s[j] = fc.sin_m1[j];
   }
+  return sa;
+}
 
-  const hipError_t err =
-      kve::launch_step(a, L->bh, L->d, gumbel, reinterpret_cast<hipStream_t>(stream));
-  if (err != hipSuccess) return KVE_ELAUNCH;
+// The incoming row, if it survives an older row's eviction, goes from
+// next_pos to slot n-1: one rotation by n - 1 - next_pos positions.
+void incoming_table(int d, double rope_base, int32_t n, int32_t next_pos, kve::RopeTable *t) {
+  const FreqCache &fc = freqs(d, rope_base);
+  const double delta = (double)(n - 1) - (double)next_pos;
+  for (int j = 0; j < d / 2; ++j) {
+    const double th = delta * fc.freq[j];
+    t->c[j] = (float)std::cos(th);
+    t->s[j] = (float)std::sin(th);
+  }
+}
 
-  ctr->n_kept = over ? budget : n + 1;
+void advance(kve_counters *ctr, int32_t budget) {
+  ctr->n_kept = ctr->n_kept + 1 > budget ? budget : ctr->n_kept + 1;
   ctr->next_pos += 1;
   ctr->pos += 1;
+}
+
+int step_impl(const kve_layer *L, const void *new_k, const void *new_v, kve_counters *ctr,
+              int32_t budget, int32_t n_sink, double tau_init, double tau_end,
+              int32_t anneal_steps, double rope_base, uint64_t seed, int32_t *evicted,
+              void *stream, bool gumbel) {
+  if (check_layer(L, new_k, new_v, ctr, budget, n_sink, gumbel) != KVE_OK) return KVE_EINVAL;
+  if (check_shared(tau_init, tau_end, anneal_steps, rope_base) != KVE_OK) return KVE_EINVAL;
+  const int dev = check_device();
+  if (dev != KVE_OK) return dev;
+
+  const kve::LayerArgs la = layer_args(L, new_k, new_v, ctr, budget, evicted, gumbel);
+  const kve::SharedArgs sa =
+      shared_args(L->d, n_sink, tau_init, tau_end, anneal_steps, rope_base, seed, gumbel);
+  kve::RopeTable rnew;
+  std::memset(&rnew, 0, sizeof(rnew));
+  if (ctr->n_kept + 1 > budget) incoming_table(L->d, rope_base, ctr->n_kept, ctr->next_pos, &rnew);
+
+  const hipError_t err =
+      kve::launch_step(la, sa, rnew, L->bh, L->d, gumbel, reinterpret_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return KVE_ELAUNCH;
+  advance(ctr, budget);
+  return KVE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// batched calls: per-layer descriptors travel to the device through a ring of
+// pinned host slots and device slots (one slot per call, reused once the
+// launch that read it has finished)
+// ---------------------------------------------------------------------------
+
+struct Ring {
+  static constexpr int kSlots = 64;
+  static constexpr size_t kSlotBytes =
+      sizeof(kve::LayerArgs) * kve::kMaxBatchLayers + sizeof(kve::RopeTable) * kve::kMaxBatchLayers;
+  std::mutex mu;
+  bool ready = false;
+  char *host = nullptr;
+  char *dev = nullptr;
+  hipEvent_t done[kSlots];
+  bool pending[kSlots] = {};
+  int next = 0;
+};
+
+Ring g_rings[128];
+
+int ring_init(Ring &r) {
+  if (r.ready) return KVE_OK;
+  if (hipHostMalloc(reinterpret_cast<void **>(&r.host), Ring::kSlotBytes * Ring::kSlots,
+                    hipHostMallocDefault) != hipSuccess)
+    return KVE_ELAUNCH;
+  if (hipMalloc(reinterpret_cast<void **>(&r.dev), Ring::kSlotBytes * Ring::kSlots) !=
+      hipSuccess)
+    return KVE_ELAUNCH;
+  for (int i = 0; i < Ring::kSlots; ++i)
+    if (hipEventCreateWithFlags(&r.done[i], hipEventDisableTiming) != hipSuccess)
+      return KVE_ELAUNCH;
+  r.ready = true;
+  return KVE_OK;
+}
+
+int batch_impl(int32_t n_layers, const kve_layer *layers, const void *const *new_k,
+               const void *const *new_v, kve_counters *ctrs, const int32_t *budgets,
+               int32_t n_sink, double tau_init, double tau_end, int32_t anneal_steps,
+               double rope_base, uint64_t seed, int32_t *const *evicted, void *stream,
+               bool gumbel) {
+  if (n_layers < 1 || n_layers > kve::kMaxBatchLayers) return KVE_EINVAL;
+  if (!layers || !new_k || !new_v || !ctrs || !budgets) return KVE_EINVAL;
+  if (check_shared(tau_init, tau_end, anneal_steps, rope_base) != KVE_OK) return KVE_EINVAL;
+  const int d = layers[0].d;
+  int64_t blocks = 0;
+  int max_n = 0;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    if (check_layer(&layers[l], new_k[l], new_v[l], &ctrs[l], budgets[l], n_sink, gumbel) !=
+        KVE_OK)
+      return KVE_EINVAL;
+    if (layers[l].d != d) return KVE_EINVAL;
+    blocks += layers[l].bh;
+    if (ctrs[l].n_kept > max_n) max_n = ctrs[l].n_kept;
+  }
+  if (blocks > INT32_MAX) return KVE_EINVAL;
+  const int dev_state = check_device();
+  if (dev_state != KVE_OK) return dev_state;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 128) return KVE_ENODEV;
+
+  Ring &r = g_rings[dev];
+  std::lock_guard<std::mutex> lock(r.mu);
+  if (ring_init(r) != KVE_OK) return KVE_ELAUNCH;
+  const int slot = r.next;
+  r.next = (r.next + 1) % Ring::kSlots;
+  if (r.pending[slot] && hipEventSynchronize(r.done[slot]) != hipSuccess) return KVE_ELAUNCH;
+  r.pending[slot] = false;
+
+  char *hslot = r.host + (size_t)slot * Ring::kSlotBytes;
+  char *dslot = r.dev + (size_t)slot * Ring::kSlotBytes;
+  kve::LayerArgs *hl = reinterpret_cast<kve::LayerArgs *>(hslot);
+  kve::RopeTable *ht =
+      reinterpret_cast<kve::RopeTable *>(hslot + sizeof(kve::LayerArgs) * kve::kMaxBatchLayers);
+  int n_tables = 0;
+  int32_t block0 = 0;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    hl[l] = layer_args(&layers[l], new_k[l], new_v[l], &ctrs[l], budgets[l],
+                       evicted ? evicted[l] : nullptr, gumbel);
+    hl[l].block0 = block0;
+    block0 += layers[l].bh;
+    // one incoming-row table per distinct (n_kept, next_pos)
+    int t = -1;
+    for (int32_t m = 0; m < l && t < 0; ++m)
+      if (ctrs[m].n_kept == ctrs[l].n_kept && ctrs[m].next_pos == ctrs[l].next_pos)
+        t = hl[m].table;
+    if (t < 0) {
+      t = n_tables++;
+      incoming_table(d, rope_base, ctrs[l].n_kept, ctrs[l].next_pos, &ht[t]);
+    }
+    hl[l].table = t;
+  }
+  const kve::SharedArgs sa =
+      shared_args(d, n_sink, tau_init, tau_end, anneal_steps, rope_base, seed, gumbel);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t layer_bytes = sizeof(kve::LayerArgs) * n_layers;
+  const size_t table_off = sizeof(kve::LayerArgs) * kve::kMaxBatchLayers;
+  if (hipMemcpyAsync(dslot, hslot, layer_bytes, hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipMemcpyAsync(dslot + table_off, hslot + table_off, sizeof(kve::RopeTable) * n_tables,
+                     hipMemcpyHostToDevice, s) != hipSuccess)
+    return KVE_ELAUNCH;
+  const hipError_t err = kve::launch_step_layers(
+      reinterpret_cast<const kve::LayerArgs *>(dslot),
+      reinterpret_cast<const kve::RopeTable *>(dslot + table_off), n_layers, (int)blocks, max_n,
+      sa, d, gumbel, s);
+  if (err != hipSuccess) return KVE_ELAUNCH;
+  if (hipEventRecord(r.done[slot], s) != hipSuccess) return KVE_ELAUNCH;
+  r.pending[slot] = true;
+  for (int32_t l = 0; l < n_layers; ++l) advance(&ctrs[l], budgets[l]);
   return KVE_OK;
 }
 
@@ -152,6 +302,24 @@ KVE_EXPORT int pyramid_step(const kve_layer *L, const void *new_k, const void *n
                             double rope_base, int32_t *evicted, void *stream) {
   return step_impl(L, new_k, new_v, ctr, budget, n_sink, 0.0, 0.0, 0, rope_base, 0, evicted,
                    stream, false);
+}
+
+KVE_EXPORT int keyformer_step_layers(int32_t n_layers, const kve_layer *layers,
+                                     const void *const *new_k, const void *const *new_v,
+                                     kve_counters *ctrs, const int32_t *budgets, int32_t n_sink,
+                                     double tau_init, double tau_end, int32_t anneal_steps,
+                                     double rope_base, uint64_t seed, int32_t *const *evicted,
+                                     void *stream) {
+  return batch_impl(n_layers, layers, new_k, new_v, ctrs, budgets, n_sink, tau_init, tau_end,
+                    anneal_steps, rope_base, seed, evicted, stream, true);
+}
+
+KVE_EXPORT int pyramid_step_layers(int32_t n_layers, const kve_layer *layers,
+                                   const void *const *new_k, const void *const *new_v,
+                                   kve_counters *ctrs, const int32_t *budgets, int32_t n_sink,
+                                   double rope_base, int32_t *const *evicted, void *stream) {
+  return batch_impl(n_layers, layers, new_k, new_v, ctrs, budgets, n_sink, 0.0, 0.0, 0,
+                    rope_base, 0, evicted, stream, false);
 }
 
 // "The budget schedule": linear taper, mean avg_budget, floor n_sink + 1.

@@ -1,5 +1,5 @@
 // kve_step.h -- internal interface between the C ABI (kve_api.hip) and the
-// gfx950 kernel (kve_step.hip).  Not installed; callers use include/kve.h.
+// gfx950 kernels (kve_step.hip).  Not installed; callers use include/kve.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -7,19 +7,18 @@
 
 namespace kve {
 
-constexpr int kMaxHalfD = 64;   // d <= 128
+constexpr int kMaxHalfD = 64;        // d <= 128
+constexpr int kMaxBatchLayers = 128; // layers in one batched call
 
-// fp32 cosine / sine of the rotation angles the step may need, computed on
-// the host in fp64 and rounded once: rotating a moved row back by one
-// position, and rotating the incoming row from next_pos to its final slot.
-struct RopeTables {
-  float cos_m1[kMaxHalfD];
-  float sin_m1[kMaxHalfD];
-  float cos_new[kMaxHalfD];
-  float sin_new[kMaxHalfD];
+// fp32 cosine / sine of one rotation angle per RoPE pair, computed on the
+// host in fp64 and rounded once.
+struct RopeTable {
+  float c[kMaxHalfD];
+  float s[kMaxHalfD];
 };
 
-struct StepArgs {
+// One layer of a step: its B*H caches and where the incoming rows are.
+struct LayerArgs {
   void *k;                 // fp16 [bh][cap][d]
   void *v;                 // fp16 [bh][cap][d]
   float *scores;           // [bh][cap]
@@ -31,18 +30,31 @@ struct StepArgs {
   int32_t cap;
   int32_t n_prev;
   int32_t budget;
-  int32_t n_sink;
   int32_t next_pos;
   int32_t pos;
+  int32_t hh_base;         // Gumbel stream of cache 0
+  int32_t block0;          // first workgroup of this layer in a batched launch
+  int32_t table;           // index of this layer's incoming-row rotation table
+};
+
+// What every layer of a launch shares.
+struct SharedArgs {
+  int32_t n_sink;
   int32_t anneal_steps;
-  int32_t hh_base;
   double tau_init;
   double tau_end;
   uint64_t seed;
   float scale;             // 1 / sqrt(d) in fp32
-  RopeTables rope;
+  RopeTable back1;         // rotation by -1 position (moved stored rows)
 };
 
-hipError_t launch_step(const StepArgs &a, int bh, int d, bool gumbel, hipStream_t stream);
+// One layer per launch: everything by value.
+hipError_t launch_step(const LayerArgs &la, const SharedArgs &sa, const RopeTable &rnew, int bh,
+                       int d, bool gumbel, hipStream_t stream);
+
+// Several layers per launch: `layers` and `tables` are device memory.
+hipError_t launch_step_layers(const LayerArgs *layers, const RopeTable *tables, int n_layers,
+                              int total_blocks, int max_n_prev, const SharedArgs &sa, int d,
+                              bool gumbel, hipStream_t stream);
 
 }  // namespace kve

@@ -15,6 +15,10 @@
 //      ascending chunks (load all, barrier, store), keys re-rotated by -1
 //      position in fp32; the new row lands at its final slot.
 //
+// Two entry kernels share the body: one layer per launch (everything passed
+// by value), or several layers per launch (descriptors in device memory, the
+// workgroups of each layer contiguous in the grid).
+//
 // Method (VeloxQuant-MLX pages): "veloxquant_mlx.quantizers.keyformer
 // module" -- keyformer_update steps 1-3, KeyformerState, FIXED GAP #1/#2,
 // FUSED METAL KERNEL; "PyramidKV -- Layer-Adaptive Budget Attention-Mass
@@ -165,19 +169,34 @@ __device__ __forceinline__ void wave_argmin(float &v, int &i) {
 // the kernel
 // ---------------------------------------------------------------------------
 
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding (gfx9 encoding; expcnt and lgkmcnt left unconstrained).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// One dword per lane from global memory straight into LDS (no registers):
+// lane l of the wave writes lds_wave_base[l].  lds_wave_base must be uniform.
+__device__ __forceinline__ void load_dword_to_lds(const float *src, float *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                   (__attribute__((address_space(3))) void *)lds_wave_base, 4,
+                                   0, 0);
+}
+
+// The whole step for cache `hh` of layer `la` (one workgroup).
 template <int D, int NT, int U, bool GUMBEL>
-__global__ __launch_bounds__(NT) void step_kernel(StepArgs a) {
+__device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs &sa,
+                                          const RopeTable &rnew, const int hh) {
   constexpr int V16 = D / 8;        // 16-byte chunks per row
   constexpr int LPR = D / 8;        // score pass: lanes per row (one chunk each)
   constexpr int RPS = NT / LPR;     // score pass: rows per sweep
-  constexpr int HALF = D / 2;
+  constexpr int ROWS_IT = RPS * U;  // score pass: rows per batch of loads
   constexpr int LPM = D / 16;       // move pass: lanes per row (one chunk of each half)
   constexpr int RPM = NT / LPM;     // move pass: rows per sweep
-  constexpr int UM = 2;             // move pass: sweeps per chunk
+  constexpr int UM = 4;             // move pass: sweeps per chunk
   constexpr int NWAVE = NT / 64;
   static_assert(NT % 64 == 0 && RPS * LPR == NT && RPM * LPM == NT, "launch shape");
 
-  extern __shared__ float lds[];    // [n] logits -> weights -> new scores ; [n] gumbel
+  // LDS: logits -> weights [np] ; scores -> new scores [np] ; gumbel [np]
+  extern __shared__ float lds[];
   __shared__ float red_v[NWAVE];
   __shared__ int red_i[NWAVE];
   __shared__ float bc_v;
@@ -186,40 +205,80 @@ __global__ __launch_bounds__(NT) void step_kernel(StepArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int hh = blockIdx.x;
-  const int n = a.n_prev;
-  const size_t row0 = (size_t)hh * (size_t)a.cap;     // first row of this cache
+  const int n = la.n_prev;
+  const int np = (n + 63) & ~63;
+  const bool over = n + 1 > la.budget;
+  const size_t row0 = (size_t)hh * (size_t)la.cap;     // first row of this cache
+  float *__restrict__ lds_x = lds;
+  float *__restrict__ lds_s = lds + np;
+  float *__restrict__ lds_g = lds + 2 * np;
+  float *__restrict__ scores = la.scores;
+  float *__restrict__ gumbel = la.gumbel;
 
-  const u32x4 *__restrict__ K4 = reinterpret_cast<const u32x4 *>(a.k) + row0 * V16;
-  float *__restrict__ lds_s = lds;
-  float *__restrict__ lds_g = lds + n;
+  // ---- prefetch scores (and, when evicting, gumbel) into LDS ---------------
+  // Every lane issues a load (the tail clamps to row n-1 and lands in padding).
+  for (int base = wave * 64; base < n; base += NT) {
+    const int i = min(base + lane, n - 1);
+    load_dword_to_lds(scores + row0 + i, lds_s + base);
+    if (GUMBEL && over) load_dword_to_lds(gumbel + row0 + i, lds_g + base);
+  }
 
   // ---- A: logits of every stored row against the incoming key -------------
+  // Two batches of U loads in flight: batch it+1 is issued before batch it
+  // is consumed.  Rows past n are clamped to row n-1 (a cache hit) and dropped.
+  const u32x4 *__restrict__ K4 = reinterpret_cast<const u32x4 *>(la.k) + row0 * V16;
   const int lr = tid % LPR;
   const int rr = tid / LPR;
-  const u32x4 q = reinterpret_cast<const u32x4 *>(a.new_k)[(size_t)hh * V16 + lr];
+  const u32x4 q = reinterpret_cast<const u32x4 *>(la.new_k)[(size_t)hh * V16 + lr];
+  const float scale = sa.scale;
   float mx = -INFINITY;
-  for (int base = 0; base < n; base += RPS * U) {
-    u32x4 kr[U];
+  const int iters = (n + ROWS_IT - 1) / ROWS_IT;
+  u32x4 bufa[U], bufb[U];
+  auto load_batch = [&](int it, u32x4 *buf) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int r = base + rr + u * RPS;
-      kr[u] = r < n ? K4[(size_t)r * V16 + lr] : u32x4(0u);
+      const int r = min(it * ROWS_IT + u * RPS + rr, n - 1);
+      buf[u] = K4[(size_t)r * V16 + lr];
     }
+  };
+  auto consume = [&](int it, const u32x4 *buf) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int r = base + rr + u * RPS;
-      const float x = group_sum<LPR>(dot8(kr[u], q)) * a.scale;
+      const int r = it * ROWS_IT + u * RPS + rr;
+      const float x = group_sum<LPR>(dot8(buf[u], q)) * scale;
       if (r < n) {
-        if (lr == 0) lds_s[r] = x;
+        if (lr == 0) lds_x[r] = x;
         mx = fmaxf(mx, x);
       }
+    }
+  };
+  // Two register buffers take turns (no copies, so the compiler waits only
+  // for the batch being consumed while the next one is in flight).  The LDS
+  // prefetch above must land before the first LDS write: wait for it right
+  // after issuing the first batch, so the two latencies overlap.
+  if (iters > 0) {
+    load_batch(0, bufa);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(U));
+    int it = 0;
+    for (; it + 2 < iters; it += 2) {
+      load_batch(it + 1, bufb);
+      consume(it, bufa);
+      load_batch(it + 2, bufa);
+      consume(it + 1, bufb);
+    }
+    if (it + 1 < iters) {
+      load_batch(it + 1, bufb);
+      consume(it, bufa);
+      consume(it + 1, bufb);
+    } else {
+      consume(it, bufa);
     }
   }
 
   // ---- B: softmax normaliser ------------------------------------------------
   mx = wave_max(mx);
   if (lane == 0) red_v[wave] = mx;
+  __builtin_amdgcn_s_waitcnt(0);                // prefetched scores / gumbel have landed
   __syncthreads();
   if (wave == 0) {
     float m = lane < NWAVE ? red_v[lane] : -INFINITY;
@@ -230,8 +289,8 @@ __global__ __launch_bounds__(NT) void step_kernel(StepArgs a) {
   mx = bc_v;
   float sum = 0.f;
   for (int i = tid; i < n; i += NT) {
-    const float w = expf(lds_s[i] - mx);
-    lds_s[i] = w;
+    const float w = expf(lds_x[i] - mx);
+    lds_x[i] = w;
     sum += w;
   }
   sum = wave_sum(sum);
@@ -247,24 +306,19 @@ __global__ __launch_bounds__(NT) void step_kernel(StepArgs a) {
   const float rz = 1.0f / bc_v;
 
   // ---- C: new scores and the eviction choice --------------------------------
-  const bool over = n + 1 > a.budget;
-  const float tau = (GUMBEL && over) ? anneal_tau(a.tau_init, a.tau_end, a.anneal_steps, a.pos)
+  const float tau = (GUMBEL && over) ? anneal_tau(sa.tau_init, sa.tau_end, sa.anneal_steps, la.pos)
                                      : 0.f;
-  const float g_new = GUMBEL ? gumbel_at(a.seed, (uint64_t)(int64_t)(a.hh_base + hh),
-                                         (uint64_t)(int64_t)a.pos)
+  const float g_new = GUMBEL ? gumbel_at(sa.seed, (uint64_t)(int64_t)(la.hh_base + hh),
+                                         (uint64_t)(int64_t)la.pos)
                              : 0.f;
+  const int n_sink = sa.n_sink;
   float bv = INFINITY;
   int bi = 0x7fffffff;
   for (int i = tid; i < n; i += NT) {
-    const float s = a.scores[row0 + i] + lds_s[i] * rz;
+    const float s = lds_s[i] + lds_x[i] * rz;
     lds_s[i] = s;
-    if (over && i >= a.n_sink) {
-      float key = s;
-      if constexpr (GUMBEL) {
-        const float g = a.gumbel[row0 + i];
-        lds_g[i] = g;
-        key = fmaf(tau, g, s);
-      }
+    if (over && i >= n_sink) {
+      const float key = GUMBEL ? fmaf(tau, lds_g[i], s) : s;
       if (key < bv) {                      // rows visited in increasing order
         bv = key;
         bi = i;
@@ -290,21 +344,22 @@ __global__ __launch_bounds__(NT) void step_kernel(StepArgs a) {
   }
   __syncthreads();
   const int e = bc_e;
-  if (tid == 0 && a.evicted) a.evicted[hh] = e;
+  if (tid == 0 && la.evicted) la.evicted[hh] = e;
 
   // ---- D: write-back ----------------------------------------------------------
+  int32_t *__restrict__ positions = la.positions;
   for (int i = tid; i < n; i += NT) {
     if (e < 0 || i < e) {
-      a.scores[row0 + i] = lds_s[i];
+      scores[row0 + i] = lds_s[i];
     } else if (i > e) {
-      a.scores[row0 + i - 1] = lds_s[i];
-      if constexpr (GUMBEL) a.gumbel[row0 + i - 1] = lds_g[i];
-      a.positions[row0 + i - 1] = i - 1;
+      scores[row0 + i - 1] = lds_s[i];
+      if constexpr (GUMBEL) gumbel[row0 + i - 1] = lds_g[i];
+      positions[row0 + i - 1] = i - 1;
     }
   }
 
-  u32x4 *__restrict__ Kw = reinterpret_cast<u32x4 *>(a.k) + row0 * V16;
-  u32x4 *__restrict__ Vw = reinterpret_cast<u32x4 *>(a.v) + row0 * V16;
+  u32x4 *__restrict__ Kw = reinterpret_cast<u32x4 *>(la.k) + row0 * V16;
+  u32x4 *__restrict__ Vw = reinterpret_cast<u32x4 *>(la.v) + row0 * V16;
   const int lm = tid % LPM;                     // chunk lm of the first half, lm of the second
   const int rm = tid / LPM;
 
@@ -313,8 +368,8 @@ __global__ __launch_bounds__(NT) void step_kernel(StepArgs a) {
     float cs[8], sn[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      cs[j] = a.rope.cos_m1[lm * 8 + j];
-      sn[j] = a.rope.sin_m1[lm * 8 + j];
+      cs[j] = sa.back1.c[lm * 8 + j];
+      sn[j] = sa.back1.s[lm * 8 + j];
     }
     for (int d0 = e; d0 < n - 1; d0 += RPM * UM) {
       u32x4 k1[UM], k2[UM], v1[UM], v2[UM];
@@ -354,15 +409,15 @@ __global__ __launch_bounds__(NT) void step_kernel(StepArgs a) {
   // or nowhere (it was the one evicted)
   const int f = e < 0 ? n : (e < n ? n - 1 : -1);
   if (f >= 0 && tid < LPM) {
-    const u32x4 *nk = reinterpret_cast<const u32x4 *>(a.new_k) + (size_t)hh * V16;
-    const u32x4 *nv = reinterpret_cast<const u32x4 *>(a.new_v) + (size_t)hh * V16;
+    const u32x4 *nk = reinterpret_cast<const u32x4 *>(la.new_k) + (size_t)hh * V16;
+    const u32x4 *nv = reinterpret_cast<const u32x4 *>(la.new_v) + (size_t)hh * V16;
     u32x4 k1 = nk[lm], k2 = nk[lm + V16 / 2];
     if (e >= 0) {                                // moved: rotate to position f
       float cs[8], sn[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        cs[j] = a.rope.cos_new[lm * 8 + j];
-        sn[j] = a.rope.sin_new[lm * 8 + j];
+        cs[j] = rnew.c[lm * 8 + j];
+        sn[j] = rnew.s[lm * 8 + j];
       }
       rotate_chunk(k1, k2, cs, sn);
     }
@@ -372,37 +427,103 @@ __global__ __launch_bounds__(NT) void step_kernel(StepArgs a) {
     Vw[o + lm] = nv[lm];
     Vw[o + lm + V16 / 2] = nv[lm + V16 / 2];
     if (tid == 0) {
-      a.scores[row0 + f] = 0.0f;
-      if constexpr (GUMBEL) a.gumbel[row0 + f] = g_new;
-      a.positions[row0 + f] = e < 0 ? a.next_pos : f;
+      scores[row0 + f] = 0.0f;
+      if constexpr (GUMBEL) gumbel[row0 + f] = g_new;
+      positions[row0 + f] = e < 0 ? la.next_pos : f;
     }
   }
-  (void)HALF;
+}
+
+// One layer per launch: workgroup hh owns cache hh.
+template <int D, int NT, int U, bool GUMBEL>
+__global__ __launch_bounds__(NT) void step_kernel(LayerArgs la, SharedArgs sa, RopeTable rnew) {
+  step_body<D, NT, U, GUMBEL>(la, sa, rnew, blockIdx.x);
+}
+
+// Several layers per launch: the workgroups of layer l are block0(l) ..
+// block0(l+1)-1; layer descriptors and rotation tables live in device memory.
+template <int D, int NT, int U, bool GUMBEL>
+__global__ __launch_bounds__(NT) void step_layers_kernel(const LayerArgs *__restrict__ layers,
+                                                         const RopeTable *__restrict__ tables,
+                                                         int n_layers, SharedArgs sa) {
+  // layer of this workgroup: the number of layers starting at or before it,
+  // counted with one load per lane and a ballot (at most 128 layers)
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  int count = 0;
+  for (int base = 0; base < n_layers; base += 64) {
+    const int i = base + lane;
+    const bool starts = i < n_layers && layers[i].block0 <= b;
+    count += __popcll(__ballot(starts));
+  }
+  const LayerArgs &la = layers[count - 1];
+  step_body<D, NT, U, GUMBEL>(la, sa, tables[la.table], b - la.block0);
 }
 
 // ---------------------------------------------------------------------------
 // launch
 // ---------------------------------------------------------------------------
 
+constexpr int kThreads = 512;
+constexpr int kUnroll = 8;
+
+static size_t lds_bytes_for(int n_prev, bool gumbel) {
+  const size_t np = (size_t)((n_prev + 63) & ~63) + 64;
+  return (gumbel ? 3 : 2) * np * sizeof(float);
+}
+
+template <typename K>
+static hipError_t allow_lds(K kern, size_t bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
 template <int D, bool GUMBEL>
-static hipError_t launch_d(const StepArgs &a, int bh, hipStream_t stream) {
-  constexpr int NT = 512;
-  constexpr int U = 8;
-  auto kern = step_kernel<D, NT, U, GUMBEL>;
-  const size_t lds_bytes = (size_t)2 * (size_t)(a.n_prev > 0 ? a.n_prev : 1) * sizeof(float);
-  if (lds_bytes > 64 * 1024) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)lds_bytes);
-    if (err != hipSuccess) return err;
-  }
-  hipLaunchKernelGGL(kern, dim3(bh), dim3(NT), lds_bytes, stream, a);
+static hipError_t launch_d(const LayerArgs &la, const SharedArgs &sa, const RopeTable &rnew,
+                           int bh, hipStream_t stream) {
+  auto kern = step_kernel<D, kThreads, kUnroll, GUMBEL>;
+  const size_t lds = lds_bytes_for(la.n_prev, GUMBEL);
+  hipError_t err = allow_lds(kern, lds);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(kern, dim3(bh), dim3(kThreads), lds, stream, la, sa, rnew);
   return hipGetLastError();
 }
 
-hipError_t launch_step(const StepArgs &a, int bh, int d, bool gumbel, hipStream_t stream) {
-  if (d == 128) return gumbel ? launch_d<128, true>(a, bh, stream) : launch_d<128, false>(a, bh, stream);
-  return gumbel ? launch_d<64, true>(a, bh, stream) : launch_d<64, false>(a, bh, stream);
+template <int D, bool GUMBEL>
+static hipError_t launch_layers_d(const LayerArgs *layers, const RopeTable *tables, int n_layers,
+                                  int total_blocks, int max_n_prev, const SharedArgs &sa,
+                                  hipStream_t stream) {
+  auto kern = step_layers_kernel<D, kThreads, kUnroll, GUMBEL>;
+  const size_t lds = lds_bytes_for(max_n_prev, GUMBEL);
+  hipError_t err = allow_lds(kern, lds);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(kern, dim3(total_blocks), dim3(kThreads), lds, stream, layers, tables,
+                     n_layers, sa);
+  return hipGetLastError();
+}
+
+hipError_t launch_step(const LayerArgs &la, const SharedArgs &sa, const RopeTable &rnew, int bh,
+                       int d, bool gumbel, hipStream_t stream) {
+  if (d == 128)
+    return gumbel ? launch_d<128, true>(la, sa, rnew, bh, stream)
+                  : launch_d<128, false>(la, sa, rnew, bh, stream);
+  return gumbel ? launch_d<64, true>(la, sa, rnew, bh, stream)
+                : launch_d<64, false>(la, sa, rnew, bh, stream);
+}
+
+hipError_t launch_step_layers(const LayerArgs *layers, const RopeTable *tables, int n_layers,
+                              int total_blocks, int max_n_prev, const SharedArgs &sa, int d,
+                              bool gumbel, hipStream_t stream) {
+  if (d == 128)
+    return gumbel ? launch_layers_d<128, true>(layers, tables, n_layers, total_blocks,
+                                               max_n_prev, sa, stream)
+                  : launch_layers_d<128, false>(layers, tables, n_layers, total_blocks,
+                                                max_n_prev, sa, stream);
+  return gumbel ? launch_layers_d<64, true>(layers, tables, n_layers, total_blocks, max_n_prev,
+                                            sa, stream)
+                : launch_layers_d<64, false>(layers, tables, n_layers, total_blocks, max_n_prev,
+                                             sa, stream);
 }
 
 }  // namespace kve

@@ -198,3 +198,44 @@ def run_layer(w: synth.Workload, layer_idx: int, budget: int, T: int, samples: l
                              c_layer=cl)
     torch.cuda.synchronize(device)
     return L, ev.cpu().numpy(), ctr
+
+
+def run_batched(w: synth.Workload, layer_ids, budgets, T: int, samples: dict, init_n, next_pos,
+                device, gen_seed: int = 99):
+    """Step several layers together (one batched launch per token) on the GPU.
+    samples[l] lists the oracle samples of layer position l.  Returns
+    (layers, evicted log [T, L, bh] numpy)."""
+    import kv_cache_eviction_step_amd as kve
+    kf = w.kind == "keyformer"
+    gen = torch.Generator(device=device)
+    gen.manual_seed(gen_seed)
+    layers = []
+    for li, b in enumerate(budgets):
+        L = kve.Layer.empty(w.bh, b + 1, w.d, device, gumbel=kf)
+        n0 = b if init_n is not None else 0
+        bulk_state(L, n0, w, gen)
+        for s in samples.get(li, []):
+            if s.init is not None:
+                load_state_into(L, s.hh, s.init)
+        layers.append(L)
+    n0s = [b if init_n is not None else 0 for b in budgets]
+    batch = kve.LayerBatch(layers, budgets, [kve.Counters(n, next_pos, next_pos) for n in n0s])
+    nk = torch.empty((T, len(budgets), w.bh, w.d), dtype=torch.float16, device=device)
+    nv = torch.empty_like(nk)
+    for li in range(len(budgets)):
+        k, v = synth.bulk_kv_torch(w, next_pos, T, w.bh, gen, device)
+        nk[:, li], nv[:, li] = k, v
+        for s in samples.get(li, []):
+            nk[:, li, s.hh] = torch.from_numpy(s.ks.view(np.float16)).to(device)
+            nv[:, li, s.hh] = torch.from_numpy(s.vs.view(np.float16)).to(device)
+    ev = torch.full((T, len(budgets), w.bh), -7, dtype=torch.int32, device=device)
+    prm = params_for(w, budgets[0], 0)
+    for t in range(T):
+        if kf:
+            kve.keyformer_step_layers(batch, nk[t], nv[t], w.n_sink, prm.tau_init, prm.tau_end,
+                                      prm.anneal_steps, w.rope_base, w.gumbel_seed, ev[t])
+        else:
+            kve.pyramid_step_layers(batch, nk[t], nv[t], w.n_sink, w.rope_base, ev[t])
+    torch.cuda.synchronize(device)
+    _ = layer_ids
+    return layers, ev.cpu().numpy(), batch

@@ -27,8 +27,8 @@ def _declared() -> list[str]:
 
 
 def test_header_declares_the_abi():
-    assert set(_declared()) == {"keyformer_step", "pyramid_step", "pyramid_budgets",
-                                "kve_strerror"}
+    assert set(_declared()) == {"keyformer_step", "pyramid_step", "keyformer_step_layers",
+                                "pyramid_step_layers", "pyramid_budgets", "kve_strerror"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -115,7 +115,7 @@ BAD_CASES = {
     "cap_too_small": dict(layer_kw=dict(cap=32)),
     "budget_le_sink": dict(call_kw=dict(budget=4, n_sink=4)),
     "negative_sink": dict(call_kw=dict(n_sink=-1)),
-    "budget_over_max": dict(call_kw=dict(budget=20000), layer_kw=dict(cap=20001)),
+    "budget_over_max": dict(call_kw=dict(budget=12289), layer_kw=dict(cap=12290)),
     "negative_tau": dict(call_kw=dict(tau_init=-0.1)),
     "nan_tau": dict(call_kw=dict(tau_end=float("nan"))),
     "negative_anneal": dict(call_kw=dict(anneal=-1)),
@@ -162,3 +162,55 @@ def test_python_binding_validates_tensors():
         kve.Layer(torch.zeros(2, 9, 64, dtype=torch.float32), L.v, L.scores, L.gumbel,
                   L.positions)
     _ = np
+
+
+# ---------------------------------------------------------------------------
+# batched calls: every layer is checked before anything is enqueued
+# ---------------------------------------------------------------------------
+
+def _batch_call(layers, ctrs, budgets, n=None, kf=True):
+    n = len(layers) if n is None else n
+    arr = (KveLayer * max(len(layers), 1))(*layers)
+    cs = (Counters * max(len(ctrs), 1))(*ctrs)
+    bs = (ctypes.c_int32 * max(len(budgets), 1))(*budgets)
+    ptrs = (ctypes.c_void_p * max(len(layers), 1))(*([FAKE] * len(layers)))
+    if kf:
+        rc = kve.lib().keyformer_step_layers(n, arr, ptrs, ptrs, cs, bs, 4, 1.0, 2.0, 64, 1e4, 0,
+                                             None, None)
+    else:
+        rc = kve.lib().pyramid_step_layers(n, arr, ptrs, ptrs, cs, bs, 4, 1e4, None, None)
+    return rc, [(c.n_kept, c.next_pos, c.pos) for c in cs]
+
+
+@pytest.mark.parametrize("case", ["zero_layers", "too_many", "mixed_d", "one_bad_budget",
+                                  "one_bad_counter", "one_null_gumbel"])
+def test_batched_rejects_before_any_launch(case):
+    layers = [_layer() for _ in range(3)]
+    ctrs = [Counters(32, 100, 100) for _ in range(3)]
+    budgets = [32, 32, 32]
+    n = None
+    if case == "zero_layers":
+        n = 0
+    elif case == "too_many":
+        layers, ctrs, budgets = [_layer()] * 129, [Counters(32, 100, 100)] * 129, [32] * 129
+    elif case == "mixed_d":
+        layers[1] = _layer(d=128)
+    elif case == "one_bad_budget":
+        budgets[2] = 40                                   # cap 33 < budget + 1
+    elif case == "one_bad_counter":
+        ctrs[1] = Counters(10, 50, 50)
+    elif case == "one_null_gumbel":
+        layers[0] = _layer(gumbel=None)
+    before = [(c.n_kept, c.next_pos, c.pos) for c in ctrs]
+    rc, after = _batch_call(layers, ctrs, budgets, n)
+    assert rc == kve.KVE_EINVAL
+    assert after == before
+
+
+def test_batched_pyramid_null_gumbel_passes_host_checks():
+    layers = [_layer(gumbel=None) for _ in range(2)]
+    rc, after = _batch_call(layers, [Counters(32, 100, 100)] * 2, [32, 32], kf=False)
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; the no-device path is not reachable")
+    assert rc == kve.KVE_ENODEV
+    assert after == [(32, 100, 100)] * 2

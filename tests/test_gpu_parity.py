@@ -15,7 +15,7 @@ import torch
 import oracle
 import synth
 from gpu_harness import (Sample, compare_cache, load_state_into, oracle_samples, random_state,
-                         run_layer)
+                         run_batched, run_layer)
 from oracle.guard import guarded_trajectory, params_for
 
 pytestmark = pytest.mark.gpu
@@ -270,3 +270,94 @@ def test_deterministic_and_split_bh_launches(dev):
         assert torch.equal(getattr(a, name), getattr(b, name)), name
         joined = torch.cat([getattr(halves[0], name), getattr(halves[1], name)])
         assert torch.equal(getattr(a, name), joined), name
+
+
+# ---------------------------------------------------------------------------
+# batched calls: several layers per launch
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["kf", "pk"])
+def test_batched_equals_per_layer_calls(dev, kind):
+    """keyformer_step_layers / pyramid_step_layers give the same bits as one
+    per-layer call per layer (layers of different B*H, cap and budget)."""
+    import kv_cache_eviction_step_amd as kve
+    kf = kind == "kf"
+    shapes = [(8, 64, 65), (5, 40, 50), (12, 64, 67), (3, 9, 10)]     # (bh, budget, cap)
+    T, d = 200, 128
+    _say(f"[batched==per-layer] kind={kind} shapes={shapes} T={T}")
+    w = synth.Workload("mix", 1, 1, 1, d, T, 0, 64, 4, "keyformer" if kf else "pyramid",
+                       1.0 if kf else 0.0, 2.0 if kf else 0.0, 100 if kf else 0)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    ins = [synth.bulk_kv_torch(w, 0, T, bh, gen, dev) for bh, _, _ in shapes]
+    A = [kve.Layer.empty(bh, cap, d, dev, gumbel=kf, hh_base=7 * i)
+         for i, (bh, _, cap) in enumerate(shapes)]
+    B = [kve.Layer.empty(bh, cap, d, dev, gumbel=kf, hh_base=7 * i)
+         for i, (bh, _, cap) in enumerate(shapes)]
+    ca = [kve.Counters(0, 0, 0) for _ in shapes]
+    batch = kve.LayerBatch(B, [b for _, b, _ in shapes])
+    eva = [torch.empty((T, bh), dtype=torch.int32, device=dev) for bh, _, _ in shapes]
+    evb = [torch.empty((T, bh), dtype=torch.int32, device=dev) for bh, _, _ in shapes]
+    for t in range(T):
+        for i, (bh, budget, cap) in enumerate(shapes):
+            if kf:
+                kve.keyformer_step(A[i], ins[i][0][t], ins[i][1][t], ca[i], budget, 4, 1.0, 2.0,
+                                   100, 1e4, 3, eva[i][t])
+            else:
+                kve.pyramid_step(A[i], ins[i][0][t], ins[i][1][t], ca[i], budget, 4, 1e4,
+                                 eva[i][t])
+        ks = [ins[i][0][t] for i in range(len(shapes))]
+        vs = [ins[i][1][t] for i in range(len(shapes))]
+        evs = [evb[i][t] for i in range(len(shapes))]
+        if kf:
+            kve.keyformer_step_layers(batch, ks, vs, 4, 1.0, 2.0, 100, 1e4, 3, evs)
+        else:
+            kve.pyramid_step_layers(batch, ks, vs, 4, 1e4, evs)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        assert (ca[i].n_kept, ca[i].next_pos, ca[i].pos) == \
+            (batch.ctrs[i].n_kept, batch.ctrs[i].next_pos, batch.ctrs[i].pos)
+        assert torch.equal(eva[i], evb[i])
+        n = ca[i].n_kept
+        for name in ("k", "v", "scores", "positions") + (("gumbel",) if kf else ()):
+            assert torch.equal(getattr(A[i], name)[:, :n], getattr(B[i], name)[:, :n]), (i, name)
+    if kf:
+        assert any(bool(((e >= 0) & (e < b)).any()) for e, (_, b, _) in zip(eva, shapes))
+
+
+def test_full_size_batched_all_layers_late_riser(dev):
+    """The 8B-shaped workload with all 32 layers in one launch per token."""
+    w = synth.WORKLOADS[3]
+    T, next_pos = 24, w.prompt
+    picks = {0: [0, 255], 17: [100], 31: [31, 200]}
+    _say(f"[full-batched] {w.name} layers={w.layers} bh={w.bh} sampled={picks} T={T}")
+    samples = {l: oracle_samples(w, l, hhs, w.budget, T, w.budget + 1, init_n=w.budget,
+                                 next_pos=next_pos) for l, hhs in picks.items()}
+    layers, ev, _ = run_batched(w, list(range(w.layers)), [w.budget] * w.layers, T, samples,
+                                w.budget, next_pos, dev)
+    errs = []
+    for l, ss in samples.items():
+        for s in ss:
+            errs += compare_cache(layers[l], s.hh, s, ev[:, l, s.hh], next_pos)
+    assert not errs, "\n".join(errs[:20])
+
+
+def test_full_size_batched_long_context_pyramid(dev):
+    """The long-context PyramidKV workload, 8 of its layers (budgets 6144 ..
+    2048 spread) in one launch per token."""
+    w = synth.WORKLOADS[4]
+    allb = oracle.pyramid_budgets(w.layers, w.budget, w.n_sink, w.beta)
+    lids = [0, 5, 10, 15, 20, 25, 30, 31]
+    budgets = [allb[l] for l in lids]
+    T, next_pos = 8, w.prompt
+    picks = {0: [0, 511], 7: [77]}
+    _say(f"[full-batched] {w.name} layers={lids} budgets={budgets} sampled={picks} T={T}")
+    samples = {li: oracle_samples(w, lids[li], hhs, budgets[li], T, budgets[li] + 1,
+                                  init_n=budgets[li], next_pos=next_pos)
+               for li, hhs in picks.items()}
+    layers, ev, _ = run_batched(w, lids, budgets, T, samples, 1, next_pos, dev)
+    errs = []
+    for li, ss in samples.items():
+        for s in ss:
+            errs += compare_cache(layers[li], s.hh, s, ev[:, li, s.hh], next_pos)
+    assert not errs, "\n".join(errs[:20])

@@ -192,13 +192,30 @@ def main():
             synth.bulk_state_torch(x.k, x.v, x.scores, x.gumbel, x.positions, budgets[l], w, gen)
             ctrs[l] = kve.Counters(budgets[l], pos0, pos0)
     else:
+        # the prompt, token by token, through the same entry point as the timed steps
         chunk = 64
+        fill_batch = kve.LayerBatch(layers, budgets, ctrs) if args.batched else None
         for t0 in range(0, w.prompt, chunk):
             cnt = min(chunk, w.prompt - t0)
-            ins = [synth.bulk_kv_torch(w, t0, cnt, bh, gen, dev) for _ in range(L)]
+            ins_k = torch.empty((cnt, L, bh, d), dtype=torch.float16, device=dev)
+            ins_v = torch.empty_like(ins_k)
+            for l in range(L):
+                k, v = synth.bulk_kv_torch(w, t0, cnt, bh, gen, dev)
+                ins_k[:, l], ins_v[:, l] = k, v
             for t in range(cnt):
-                for l in range(L):
-                    step_layer(l, ins[l][0][t], ins[l][1][t])
+                if fill_batch is not None:
+                    if kf:
+                        kve.keyformer_step_layers(fill_batch, ins_k[t], ins_v[t], w.n_sink,
+                                                  w.tau_init, w.tau_end, w.anneal_steps,
+                                                  w.rope_base, w.gumbel_seed)
+                    else:
+                        kve.pyramid_step_layers(fill_batch, ins_k[t], ins_v[t], w.n_sink,
+                                                w.rope_base)
+                else:
+                    for l in range(L):
+                        step_layer(l, ins_k[t, l], ins_v[t, l])
+        if fill_batch is not None:
+            ctrs = [fill_batch.ctrs[l] for l in range(L)]
     torch.cuda.synchronize()
     t_fill = time.time() - t_fill
 

@@ -3,7 +3,7 @@
 // One workgroup owns one cache (one (batch, kv-head) of the layer) for the
 // whole step, so no cross-workgroup synchronisation or scratch memory is
 // needed.  Phases inside the workgroup:
-//   A  score pass: coalesced 128-bit loads of the stored keys, fp16 dot2
+//   A  score pass: coalesced non-temporal 128-bit loads of the stored keys, fp16 dot2
 //      products against the incoming key, 16-lane DPP reduction per row,
 //      logits to LDS (a matrix-vector product: bandwidth bound, no MFMA);
 //   B  softmax: block max, exponentials and block sum over LDS;
@@ -169,6 +169,12 @@ __device__ __forceinline__ void wave_argmin(float &v, int &i) {
 // the kernel
 // ---------------------------------------------------------------------------
 
+// Rows each thread moves per chunk of the compaction (tuning builds may
+// override with -D).
+#ifndef KVE_MOVE_UNROLL
+#define KVE_MOVE_UNROLL 4
+#endif
+
 // s_waitcnt immediate that waits until at most n vector-memory operations are
 // outstanding (gfx9 encoding; expcnt and lgkmcnt left unconstrained).
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
@@ -191,7 +197,7 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   constexpr int ROWS_IT = RPS * U;  // score pass: rows per batch of loads
   constexpr int LPM = D / 16;       // move pass: lanes per row (one chunk of each half)
   constexpr int RPM = NT / LPM;     // move pass: rows per sweep
-  constexpr int UM = 4;             // move pass: sweeps per chunk
+  constexpr int UM = KVE_MOVE_UNROLL; // move pass: sweeps per chunk
   constexpr int NWAVE = NT / 64;
   static_assert(NT % 64 == 0 && RPS * LPR == NT && RPM * LPM == NT, "launch shape");
 
@@ -234,11 +240,13 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   float mx = -INFINITY;
   const int iters = (n + ROWS_IT - 1) / ROWS_IT;
   u32x4 bufa[U], bufb[U];
+  // Non-temporal loads: the key stream is read once per step and must not
+  // push the scores (written back at the end of the step) out of the caches.
   auto load_batch = [&](int it, u32x4 *buf) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int r = min(it * ROWS_IT + u * RPS + rr, n - 1);
-      buf[u] = K4[(size_t)r * V16 + lr];
+      buf[u] = __builtin_nontemporal_load(K4 + (size_t)r * V16 + lr);
     }
   };
   auto consume = [&](int it, const u32x4 *buf) {
@@ -464,8 +472,15 @@ __global__ __launch_bounds__(NT) void step_layers_kernel(const LayerArgs *__rest
 // launch
 // ---------------------------------------------------------------------------
 
-constexpr int kThreads = 512;
-constexpr int kUnroll = 8;
+// Launch shape (tuning builds may override these two with -D).
+#ifndef KVE_THREADS
+#define KVE_THREADS 512
+#endif
+#ifndef KVE_UNROLL
+#define KVE_UNROLL 8
+#endif
+constexpr int kThreads = KVE_THREADS;
+constexpr int kUnroll = KVE_UNROLL;
 
 static size_t lds_bytes_for(int n_prev, bool gumbel) {
   const size_t np = (size_t)((n_prev + 63) & ~63) + 64;

@@ -151,11 +151,13 @@ int pyramid_step(const kve_layer *L, const void *new_k, const void *new_v,
  *   n_sink, tau_*, anneal_steps, rope_base, seed, stream: as per layer, shared
  * Every layer is checked before anything is enqueued; on KVE_EINVAL no
  * counter changes.  The descriptors reach the device through a ring of 64
- * pinned host / device slots per device, allocated on the first batched call
- * on that device (a failed allocation returns KVE_ELAUNCH); a call blocks
- * the host only if the device is 64 batched calls behind.  Calls from several
- * threads are serialised on that ring.  Not for use under stream capture
- * (the descriptor copies read the ring at replay time).
+ * pinned host / device slots per device, allocated (with one non-blocking
+ * copy stream) on the first batched call on that device (a failed
+ * allocation returns KVE_ELAUNCH); each call copies its slot on that stream
+ * and makes `stream` wait for the copy, then launches on `stream`.  A call
+ * blocks the host only if the device is 64 batched calls behind.  Calls from
+ * several threads are serialised on that ring.  Not for use under stream
+ * capture (the descriptor copies read the ring at replay time).
  */
 int keyformer_step_layers(int32_t n_layers, const kve_layer *layers, const void *const *new_k,
                           const void *const *new_v, kve_counters *ctrs, const int32_t *budgets,

@@ -188,7 +188,9 @@ struct Ring {
   bool ready = false;
   char *host = nullptr;
   char *dev = nullptr;
-  hipEvent_t done[kSlots];
+  hipStream_t copy_stream = nullptr;   // descriptor copies overlap the caller's previous work
+  hipEvent_t copied[kSlots];           // slot's copy landed (the launch waits on it)
+  hipEvent_t done[kSlots];             // launch that read the slot finished
   bool pending[kSlots] = {};
   int next = 0;
 };
@@ -203,8 +205,11 @@ int ring_init(Ring &r) {
   if (hipMalloc(reinterpret_cast<void **>(&r.dev), Ring::kSlotBytes * Ring::kSlots) !=
       hipSuccess)
     return KVE_ELAUNCH;
+  if (hipStreamCreateWithFlags(&r.copy_stream, hipStreamNonBlocking) != hipSuccess)
+    return KVE_ELAUNCH;
   for (int i = 0; i < Ring::kSlots; ++i)
-    if (hipEventCreateWithFlags(&r.done[i], hipEventDisableTiming) != hipSuccess)
+    if (hipEventCreateWithFlags(&r.done[i], hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&r.copied[i], hipEventDisableTiming) != hipSuccess)
       return KVE_ELAUNCH;
   r.ready = true;
   return KVE_OK;
@@ -271,9 +276,15 @@ int batch_impl(int32_t n_layers, const kve_layer *layers, const void *const *new
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const size_t layer_bytes = sizeof(kve::LayerArgs) * n_layers;
   const size_t table_off = sizeof(kve::LayerArgs) * kve::kMaxBatchLayers;
-  if (hipMemcpyAsync(dslot, hslot, layer_bytes, hipMemcpyHostToDevice, s) != hipSuccess ||
+  // The copy runs on the library's own stream (it touches only this slot, which
+  // no queued launch reads any more), so it overlaps the caller's earlier work;
+  // the launch on the caller's stream waits for it.
+  if (hipMemcpyAsync(dslot, hslot, layer_bytes, hipMemcpyHostToDevice, r.copy_stream) !=
+          hipSuccess ||
       hipMemcpyAsync(dslot + table_off, hslot + table_off, sizeof(kve::RopeTable) * n_tables,
-                     hipMemcpyHostToDevice, s) != hipSuccess)
+                     hipMemcpyHostToDevice, r.copy_stream) != hipSuccess ||
+      hipEventRecord(r.copied[slot], r.copy_stream) != hipSuccess ||
+      hipStreamWaitEvent(s, r.copied[slot], 0) != hipSuccess)
     return KVE_ELAUNCH;
   const hipError_t err = kve::launch_step_layers(
       reinterpret_cast<const kve::LayerArgs *>(dslot),

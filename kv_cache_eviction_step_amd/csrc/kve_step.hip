@@ -172,7 +172,7 @@ __device__ __forceinline__ void wave_argmin(float &v, int &i) {
 // Rows each thread moves per chunk of the compaction (tuning builds may
 // override with -D).
 #ifndef KVE_MOVE_UNROLL
-#define KVE_MOVE_UNROLL 4
+#define KVE_MOVE_UNROLL 1
 #endif
 
 // s_waitcnt immediate that waits until at most n vector-memory operations are
@@ -371,38 +371,43 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   const int lm = tid % LPM;                     // chunk lm of the first half, lm of the second
   const int rm = tid / LPM;
 
-  // old rows e+1 .. n-1 move to e .. n-2, keys rotated by one position back
+  // old rows e+1 .. n-1 move to e .. n-2, keys rotated by one position back.
+  // Chunks of CH destination rows, software-pipelined: chunk c+1's loads are
+  // in flight while chunk c is rotated and stored.  In place and safe: chunk
+  // c+1 reads only rows after every row chunk c writes, and chunk c is stored
+  // only after every wave's loads of chunk c have landed (wait + barrier).
+  // Loads are issued unconditionally (row index clamped to the last source
+  // row) so that the explicit wait counts are exact.
   if (e >= 0 && e < n - 1) {
+    constexpr int CH = RPM * UM;
+    constexpr int LOADS = 4 * UM;               // per thread per chunk
+    const int last = n - 2;                     // last destination row
     float cs[8], sn[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       cs[j] = sa.back1.c[lm * 8 + j];
       sn[j] = sa.back1.s[lm * 8 + j];
     }
-    for (int d0 = e; d0 < n - 1; d0 += RPM * UM) {
-      u32x4 k1[UM], k2[UM], v1[UM], v2[UM];
+    u32x4 ak1[UM], ak2[UM], av1[UM], av2[UM];
+    u32x4 bk1[UM], bk2[UM], bv1[UM], bv2[UM];
+    auto load_chunk = [&](int d0, u32x4 *k1, u32x4 *k2, u32x4 *v1, u32x4 *v2) {
 #pragma unroll
       for (int u = 0; u < UM; ++u) {
-        const int dst = d0 + rm + u * RPM;
-        if (dst < n - 1) {
-          const size_t src = (size_t)(dst + 1) * V16;
-          k1[u] = Kw[src + lm];
-          k2[u] = Kw[src + lm + V16 / 2];
-          v1[u] = Vw[src + lm];
-          v2[u] = Vw[src + lm + V16 / 2];
-        }
+        const size_t src = (size_t)(min(d0 + rm + u * RPM, last) + 1) * V16;
+        k1[u] = Kw[src + lm];
+        k2[u] = Kw[src + lm + V16 / 2];
+        v1[u] = Vw[src + lm];
+        v2[u] = Vw[src + lm + V16 / 2];
       }
+    };
+    auto store_chunk = [&](int d0, u32x4 *k1, u32x4 *k2, const u32x4 *v1, const u32x4 *v2) {
+#pragma unroll
+      for (int u = 0; u < UM; ++u) rotate_chunk(k1[u], k2[u], cs, sn);
+      __syncthreads();                          // every wave's loads of this chunk landed
 #pragma unroll
       for (int u = 0; u < UM; ++u) {
         const int dst = d0 + rm + u * RPM;
-        if (dst < n - 1) rotate_chunk(k1[u], k2[u], cs, sn);
-      }
-      __builtin_amdgcn_s_waitcnt(0);            // every load of this chunk has landed
-      __syncthreads();
-#pragma unroll
-      for (int u = 0; u < UM; ++u) {
-        const int dst = d0 + rm + u * RPM;
-        if (dst < n - 1) {
+        if (dst <= last) {
           const size_t o = (size_t)dst * V16;
           Kw[o + lm] = k1[u];
           Kw[o + lm + V16 / 2] = k2[u];
@@ -410,6 +415,30 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
           Vw[o + lm + V16 / 2] = v2[u];
         }
       }
+    };
+    int d0 = e;
+    load_chunk(d0, ak1, ak2, av1, av2);
+    while (true) {
+      if (d0 + CH <= last) {
+        load_chunk(d0 + CH, bk1, bk2, bv1, bv2);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));   // chunk d0 landed, next in flight
+        store_chunk(d0, ak1, ak2, av1, av2);
+      } else {
+        __builtin_amdgcn_s_waitcnt(0);
+        store_chunk(d0, ak1, ak2, av1, av2);
+        break;
+      }
+      d0 += CH;
+      if (d0 + CH <= last) {
+        load_chunk(d0 + CH, ak1, ak2, av1, av2);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
+        store_chunk(d0, bk1, bk2, bv1, bv2);
+      } else {
+        __builtin_amdgcn_s_waitcnt(0);
+        store_chunk(d0, bk1, bk2, bv1, bv2);
+        break;
+      }
+      d0 += CH;
     }
   }
 

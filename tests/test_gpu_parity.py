@@ -361,3 +361,87 @@ def test_full_size_batched_long_context_pyramid(dev):
         for s in ss:
             errs += compare_cache(layers[li], s.hh, s, ev[:, li, s.hh], next_pos)
     assert not errs, "\n".join(errs[:20])
+
+
+# ---------------------------------------------------------------------------
+# limits and degenerate shapes
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,kind", [(128, "kf"), (64, "kf"), (128, "pk")])
+def test_maximum_budget_single_steps(dev, d, kind):
+    """Budget 12288, the largest the library accepts (LDS past 64 KiB): a
+    step whose eviction moves almost every row, and a bootstrap-free step."""
+    budget, n_sink, bh = 12288, 4, 3
+    w = synth.Workload(f"max{d}{kind}", 1, 1, bh, d, 64, 0, budget, n_sink,
+                       "keyformer" if kind == "kf" else "pyramid",
+                       1.0 if kind == "kf" else 0.0, 2.0 if kind == "kf" else 0.0,
+                       64 if kind == "kf" else 0)
+    cap, next_pos = budget + 1, 20000
+    _say(f"[max] d={d} kind={kind} budget={budget} bh={bh}")
+    samples = []
+    for hh in range(bh):
+        c = _forced(w, hh, budget, cap, next_pos, n_sink + 1 if hh == 0 else None)
+        init = c.snapshot()
+        tr = guarded_trajectory(w, 0, hh, budget, 2, cap=cap, t0=next_pos, cache=c,
+                                params=params_for(w, budget, hh),
+                                min_margin_rel=-1.0 if kind == "pk" and hh == 0 else 1e-4)
+        samples.append(Sample(hh, budget, init, tr.ks, tr.vs, tr.evicted, tr.cache.snapshot(),
+                              int(tr.attempts.sum())))
+    if kind == "kf":
+        assert samples[0].evicted[0] == n_sink + 1            # a move of ~12k rows
+    L, ev, _ = run_layer(w, 0, budget, 2, samples, budget, next_pos, dev, bh=bh)
+    _assert_parity(L, ev, samples, next_pos)
+
+
+@pytest.mark.parametrize("kind", ["kf", "pk"])
+def test_single_evictable_slot(dev, kind):
+    """budget = n_sink + 1: one non-sink row competes with the incoming one."""
+    w = synth.Workload(f"slot1{kind}", 1, 1, 8, 128, 300, 0, 5, 4,
+                       "keyformer" if kind == "kf" else "pyramid",
+                       0.5 if kind == "kf" else 0.0, 1.5 if kind == "kf" else 0.0,
+                       100 if kind == "kf" else 0)
+    T = 300
+    _say(f"[slot1] kind={kind} budget=5 n_sink=4 T={T}")
+    samples = oracle_samples(w, 0, range(w.bh), w.budget, T, w.budget + 1, workers=1)
+    L, ev, _ = run_layer(w, 0, w.budget, T, samples, None, 0, dev)
+    _assert_parity(L, ev, samples, 0)
+
+
+# ---------------------------------------------------------------------------
+# whole trajectories through the prompt -> decode boundary
+# ---------------------------------------------------------------------------
+
+def test_full_trajectory_llama_keyformer(dev):
+    """Llama-3.2-3B-shaped Keyformer: the full 2048 + 1024 tokens, every cache
+    of one layer."""
+    w = synth.WORKLOADS[1]
+    _say(f"[full-traj] {w.name} layer 11 bh={w.bh} T={w.tokens}")
+    samples = oracle_samples(w, 11, range(w.bh), w.budget, w.tokens, w.budget + 1)
+    L, ev, ctr = run_layer(w, 11, w.budget, w.tokens, samples, None, 0, dev)
+    _assert_parity(L, ev, samples, 0)
+    assert (ctr.n_kept, ctr.next_pos) == (w.budget, w.tokens)
+
+
+@pytest.mark.parametrize("beta,layer", [(2.0, 3), (1.0, 20)])
+def test_full_trajectory_llama_pyramid(dev, beta, layer):
+    """Llama-3.2-3B-shaped PyramidKV: the full 3072 tokens at one layer's budget."""
+    w = synth.Workload(f"pk-beta{beta}", 1, 28, 8, 128, 2048, 1024, 512, 4, "pyramid",
+                       beta=beta)
+    budget = oracle.pyramid_budgets(w.layers, w.budget, w.n_sink, beta)[layer]
+    _say(f"[full-traj] pyramid beta={beta} layer {layer} budget={budget} T={w.tokens}")
+    samples = oracle_samples(w, layer, range(w.bh), budget, w.tokens, budget + 1)
+    L, ev, _ = run_layer(w, layer, budget, w.tokens, samples, None, 0, dev)
+    _assert_parity(L, ev, samples, 0)
+
+
+def test_full_trajectory_8b_late_riser(dev):
+    """8B-shaped late-riser Keyformer: 4096 + 512 tokens through one full
+    256-cache layer launch, four caches checked."""
+    w = synth.WORKLOADS[3]
+    hhs = [0, 99, 200, 255]
+    _say(f"[full-traj] {w.name} layer 7 bh={w.bh} sampled={hhs} T={w.tokens}")
+    samples = oracle_samples(w, 7, hhs, w.budget, w.tokens, w.budget + 1)
+    L, ev, _ = run_layer(w, 7, w.budget, w.tokens, samples, None, 0, dev)
+    _assert_parity(L, ev, samples, 0)
+    moved = [(ev[w.budget:, s.hh] < w.budget).mean() for s in samples]
+    assert max(moved) > 0.02                               # interior evictions happened

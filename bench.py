@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--batched", action="store_true",
                     help="one launch per token for all layers (keyformer_step_layers / "
                          "pyramid_step_layers) instead of one launch per layer")
+    ap.add_argument("--tokens-per-call", type=int, default=1,
+                    help="S > 1: one launch per layer steps S tokens (keyformer_step_tokens / "
+                         "pyramid_step_tokens); --steps must be a multiple of S")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the CPU oracle baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -220,12 +223,24 @@ def main():
     t_fill = time.time() - t_fill
 
     # ---- inputs for warmup + timed steps, resident in HBM ----------------------
+    TPC = args.tokens_per_call
+    if TPC > 1 and (args.batched or args.steps % TPC or args.warmup % TPC):
+        print("--tokens-per-call needs per-layer launches and steps/warmup multiples of it",
+              file=sys.stderr)
+        sys.exit(2)
     S = args.warmup + args.steps
-    nk = torch.empty((S, L, bh, d), dtype=torch.float16, device=dev)
-    nv = torch.empty_like(nk)
-    for l in range(L):
-        k, v = synth.bulk_kv_torch(w, pos0, S, bh, gen, dev)
-        nk[:, l], nv[:, l] = k, v
+    if TPC > 1:          # token-major per layer: [L, S, bh, d]
+        nk = torch.empty((L, S, bh, d), dtype=torch.float16, device=dev)
+        nv = torch.empty_like(nk)
+        for l in range(L):
+            nk[l], nv[l] = synth.bulk_kv_torch(w, pos0, S, bh, gen, dev)
+        ev_tok = torch.full((L, args.steps, bh), -9, dtype=torch.int32, device=dev)
+    else:                # layer-major per token: [S, L, bh, d]
+        nk = torch.empty((S, L, bh, d), dtype=torch.float16, device=dev)
+        nv = torch.empty_like(nk)
+        for l in range(L):
+            k, v = synth.bulk_kv_torch(w, pos0, S, bh, gen, dev)
+            nk[:, l], nv[:, l] = k, v
     ev = torch.full((args.steps, L, bh), -9, dtype=torch.int32, device=dev)
     n_prev = [[0] * L for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -249,19 +264,46 @@ def main():
     def counters(l):
         return batch.ctrs[l] if batch is not None else ctrs[l]
 
-    for s in range(args.warmup):
-        step_all(s)
+    def step_tokens(s0, evs=None):
+        """TPC tokens starting at input s0 through every layer, one launch per layer."""
+        for l in range(L):
+            e_l = evs[l] if evs is not None else None
+            if kf:
+                kve.keyformer_step_tokens(layers[l], nk[l, s0:s0 + TPC], nv[l, s0:s0 + TPC],
+                                          ctrs[l], budgets[l], w.n_sink, w.tau_init, w.tau_end,
+                                          w.anneal_steps, w.rope_base, w.gumbel_seed, e_l,
+                                          c_layer=cls[l])
+            else:
+                kve.pyramid_step_tokens(layers[l], nk[l, s0:s0 + TPC], nv[l, s0:s0 + TPC],
+                                        ctrs[l], budgets[l], w.n_sink, w.rope_base, e_l,
+                                        c_layer=cls[l])
+
+    if TPC > 1:
+        for s0 in range(0, args.warmup, TPC):
+            step_tokens(s0)
+    else:
+        for s in range(args.warmup):
+            step_all(s)
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
-    for s in range(args.steps):
-        for l in range(L):
-            n_prev[s][l] = counters(l).n_kept
-        step_all(args.warmup + s, ev[s])
+    if TPC > 1:
+        for s0 in range(0, args.steps, TPC):
+            for l in range(L):
+                for i in range(TPC):
+                    n_prev[s0 + i][l] = min(ctrs[l].n_kept + i, budgets[l])
+            step_tokens(args.warmup + s0, [ev_tok[l, s0:s0 + TPC] for l in range(L)])
+    else:
+        for s in range(args.steps):
+            for l in range(L):
+                n_prev[s][l] = counters(l).n_kept
+            step_all(args.warmup + s, ev[s])
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
+    if TPC > 1:
+        ev = ev_tok.permute(1, 0, 2)
 
     # ---- algorithmic bytes from the eviction log --------------------------------
     evn = ev.cpu().numpy()
@@ -272,7 +314,7 @@ def main():
             e = evn[s, l]
             m = np.where((e >= 0) & (e < n), n - e, 0).astype(np.int64)
             total_bytes += int(step_bytes(w.kind, n, d, m).sum())
-    launches = args.steps * (1 if batch is not None else L)
+    launches = args.steps * (1 if batch is not None else L) // TPC
     sec = ms / 1e3
     updates = bh * L * args.steps
     avg_launch_s = sec / launches
@@ -308,12 +350,16 @@ def main():
             "fill_seconds": round(t_fill, 1), "mean_rows_moved_per_cache_step": mean_m,
             "launch": ("one launch per token over all layers (" +
                        ("keyformer" if kf else "pyramid") + "_step_layers)") if batch is not None
+                      else (f"one launch per layer per {TPC} tokens (" +
+                            ("keyformer" if kf else "pyramid") + "_step_tokens)") if TPC > 1
                       else "one launch per layer (" + ("keyformer" if kf else "pyramid") + "_step)",
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(args.config, args.batched),
-            "kernel": "kve::step_layers_kernel" if batch is not None else "kve::step_kernel",
+            "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(args.config, args.batched or TPC > 1)
+            if TPC == 1 else None,
+            "kernel": ("kve::step_layers_kernel" if batch is not None or TPC > 1
+                       else "kve::step_kernel"),
             "avg_launch_us": avg_launch_s * 1e6,
             "algorithmic_bytes_per_launch": bytes_per_launch,
         },

@@ -171,6 +171,33 @@ int pyramid_step_layers(int32_t n_layers, const kve_layer *layers, const void *c
                         void *stream);
 
 /*
+ * keyformer_step_tokens / pyramid_step_tokens -- S consecutive tokens into
+ * every cache of one layer in ONE launch (keyformer_update absorbs S tokens
+ * one after the other): bit for bit the same as S calls of keyformer_step /
+ * pyramid_step.  Each cache's workgroup steps through the S tokens on its
+ * own, so a cache that must move many rows for one token does not hold up
+ * the others.
+ *
+ *   n_tokens   S, 1 .. 128
+ *   new_k,new_v  device fp16 [S][bh][d]: token t's incoming rows at
+ *              new_k + t*bh*d (already RoPE'd at next_pos + t)
+ *   evicted    optional device i32 [S][bh]: token t's evicted index per cache
+ *   ctr        advanced by S tokens on success
+ *   other arguments as keyformer_step / pyramid_step.
+ * Checked as one per-layer call (the first token's counters), plus
+ * 1 <= n_tokens <= 128.  Uses the batched calls' descriptor ring (one
+ * rotation table per token); not for use under stream capture.
+ */
+int keyformer_step_tokens(const kve_layer *L, int32_t n_tokens, const void *new_k,
+                          const void *new_v, kve_counters *ctr, int32_t budget, int32_t n_sink,
+                          double tau_init, double tau_end, int32_t anneal_steps,
+                          double rope_base, uint64_t seed, int32_t *evicted, void *stream);
+
+int pyramid_step_tokens(const kve_layer *L, int32_t n_tokens, const void *new_k,
+                        const void *new_v, kve_counters *ctr, int32_t budget, int32_t n_sink,
+                        double rope_base, int32_t *evicted, void *stream);
+
+/*
  * pyramid_budgets -- per-layer budgets ("The budget schedule"): a linear taper
  * from the largest budget at layer 0 to the smallest at the last layer, mean
  * avg_budget, every entry at least n_sink + 1.  The smallest is

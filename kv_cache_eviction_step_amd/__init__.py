@@ -14,6 +14,10 @@ Calls (same names as the C ABI):
                           anneal_steps, rope_base, seed, evicted=None, stream=None)
     pyramid_step_layers(batch, new_k, new_v, n_sink, rope_base, evicted=None,
                         stream=None)
+    keyformer_step_tokens(layer, new_k[S], new_v[S], ctr, budget, n_sink, tau_init,
+                          tau_end, anneal_steps, rope_base, seed, evicted=None, stream=None)
+    pyramid_step_tokens(layer, new_k[S], new_v[S], ctr, budget, n_sink, rope_base,
+                        evicted=None, stream=None)
     pyramid_budgets(n_layers, avg_budget, n_sink, beta) -> list[int]
 """
 from __future__ import annotations
@@ -75,6 +79,16 @@ _lib.pyramid_step_layers.argtypes = [
     ctypes.c_int32, ctypes.POINTER(KveLayer), ctypes.c_void_p, ctypes.c_void_p,
     ctypes.POINTER(Counters), ctypes.c_void_p, ctypes.c_int32, ctypes.c_double, ctypes.c_void_p,
     ctypes.c_void_p]
+_lib.keyformer_step_tokens.restype = ctypes.c_int
+_lib.keyformer_step_tokens.argtypes = [
+    ctypes.POINTER(KveLayer), ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+    ctypes.POINTER(Counters), ctypes.c_int32, ctypes.c_int32, ctypes.c_double, ctypes.c_double,
+    ctypes.c_int32, ctypes.c_double, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+_lib.pyramid_step_tokens.restype = ctypes.c_int
+_lib.pyramid_step_tokens.argtypes = [
+    ctypes.POINTER(KveLayer), ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+    ctypes.POINTER(Counters), ctypes.c_int32, ctypes.c_int32, ctypes.c_double, ctypes.c_void_p,
+    ctypes.c_void_p]
 _lib.pyramid_budgets.restype = ctypes.c_int
 _lib.pyramid_budgets.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                  ctypes.c_double, ctypes.c_void_p]
@@ -82,7 +96,7 @@ _lib.kve_strerror.restype = ctypes.c_char_p
 _lib.kve_strerror.argtypes = [ctypes.c_int]
 
 EXPORTED = ("keyformer_step", "pyramid_step", "keyformer_step_layers", "pyramid_step_layers",
-            "pyramid_budgets", "kve_strerror")
+            "keyformer_step_tokens", "pyramid_step_tokens", "pyramid_budgets", "kve_strerror")
 
 
 def lib() -> ctypes.CDLL:
@@ -286,6 +300,55 @@ def pyramid_step_layers(batch: LayerBatch, new_k, new_v, n_sink: int, rope_base:
                                   batch.budgets, n_sink, rope_base, pe,
                                   _stream_ptr(stream, batch.layers[0]))
     _check(rc, "pyramid_step_layers")
+
+
+def _tokens(t, layer: Layer, name: str):
+    if (t.dtype != torch.float16 or t.dim() != 3 or tuple(t.shape[1:]) != (layer.bh, layer.d)
+            or not t.is_contiguous() or t.device != layer.k.device):
+        raise ValueError(f"{name} must be contiguous float16 [S, {layer.bh}, {layer.d}] on "
+                         f"{layer.k.device}")
+    return t.data_ptr()
+
+
+def _evicted_tokens(evicted, layer: Layer, n: int):
+    if evicted is None:
+        return None
+    if (evicted.dtype != torch.int32 or tuple(evicted.shape) != (n, layer.bh) or
+            not evicted.is_contiguous() or evicted.device != layer.k.device):
+        raise ValueError(f"evicted must be contiguous int32 [{n}, {layer.bh}]")
+    return evicted.data_ptr()
+
+
+def keyformer_step_tokens(layer: Layer, new_k, new_v, ctr: Counters, budget: int, n_sink: int,
+                          tau_init: float, tau_end: float, anneal_steps: int, rope_base: float,
+                          seed: int, evicted=None, stream=None,
+                          c_layer: KveLayer | None = None) -> None:
+    """new_k.shape[0] consecutive tokens into every cache of `layer`, one launch."""
+    n = new_k.shape[0]
+    cl = c_layer if c_layer is not None else layer.c_struct()
+    pk, pv = _tokens(new_k, layer, "new_k"), _tokens(new_v, layer, "new_v")
+    if new_v.shape[0] != n:
+        raise ValueError("new_k and new_v must hold the same number of tokens")
+    rc = _lib.keyformer_step_tokens(ctypes.byref(cl), n, pk, pv, ctypes.byref(ctr), budget,
+                                    n_sink, tau_init, tau_end, anneal_steps, rope_base,
+                                    seed & 0xFFFFFFFFFFFFFFFF, _evicted_tokens(evicted, layer, n),
+                                    _stream_ptr(stream, layer))
+    _check(rc, "keyformer_step_tokens")
+
+
+def pyramid_step_tokens(layer: Layer, new_k, new_v, ctr: Counters, budget: int, n_sink: int,
+                        rope_base: float, evicted=None, stream=None,
+                        c_layer: KveLayer | None = None) -> None:
+    """new_k.shape[0] consecutive tokens into every cache of `layer` (H2O / PyramidKV)."""
+    n = new_k.shape[0]
+    cl = c_layer if c_layer is not None else layer.c_struct()
+    pk, pv = _tokens(new_k, layer, "new_k"), _tokens(new_v, layer, "new_v")
+    if new_v.shape[0] != n:
+        raise ValueError("new_k and new_v must hold the same number of tokens")
+    rc = _lib.pyramid_step_tokens(ctypes.byref(cl), n, pk, pv, ctypes.byref(ctr), budget, n_sink,
+                                  rope_base, _evicted_tokens(evicted, layer, n),
+                                  _stream_ptr(stream, layer))
+    _check(rc, "pyramid_step_tokens")
 
 
 def pyramid_budgets(n_layers: int, avg_budget: int, n_sink: int, beta: float) -> list[int]:

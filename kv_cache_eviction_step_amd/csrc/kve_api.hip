@@ -6,6 +6,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 
@@ -183,7 +184,7 @@ int step_impl(const kve_layer *L, const void *new_k, const void *new_v, kve_coun
 struct Ring {
   static constexpr int kSlots = 64;
   static constexpr size_t kSlotBytes =
-      sizeof(kve::LayerArgs) * kve::kMaxBatchLayers + sizeof(kve::RopeTable) * kve::kMaxBatchLayers;
+      sizeof(kve::LayerArgs) * kve::kMaxBatchLayers + sizeof(kve::RopeTable) * kve::kMaxTables;
   std::mutex mu;
   bool ready = false;
   char *host = nullptr;
@@ -215,12 +216,16 @@ int ring_init(Ring &r) {
   return KVE_OK;
 }
 
-int batch_impl(int32_t n_layers, const kve_layer *layers, const void *const *new_k,
-               const void *const *new_v, kve_counters *ctrs, const int32_t *budgets,
-               int32_t n_sink, double tau_init, double tau_end, int32_t anneal_steps,
-               double rope_base, uint64_t seed, int32_t *const *evicted, void *stream,
-               bool gumbel) {
+// One descriptor-driven launch: n_layers layers, each stepped n_tokens tokens
+// (n_tokens > 1 only with a single layer).  Checks every layer first.
+int batch_impl(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
+               const void *const *new_k, const void *const *new_v, kve_counters *ctrs,
+               const int32_t *budgets, int32_t n_sink, double tau_init, double tau_end,
+               int32_t anneal_steps, double rope_base, uint64_t seed, int32_t *const *evicted,
+               void *stream, bool gumbel) {
   if (n_layers < 1 || n_layers > kve::kMaxBatchLayers) return KVE_EINVAL;
+  if (n_tokens < 1 || n_tokens > kve::kMaxTokens || (n_tokens > 1 && n_layers != 1))
+    return KVE_EINVAL;
   if (!layers || !new_k || !new_v || !ctrs || !budgets) return KVE_EINVAL;
   if (check_shared(tau_init, tau_end, anneal_steps, rope_base) != KVE_OK) return KVE_EINVAL;
   const int d = layers[0].d;
@@ -231,8 +236,12 @@ int batch_impl(int32_t n_layers, const kve_layer *layers, const void *const *new
         KVE_OK)
       return KVE_EINVAL;
     if (layers[l].d != d) return KVE_EINVAL;
+    if ((int64_t)ctrs[l].next_pos + n_tokens >= INT32_MAX ||
+        (int64_t)ctrs[l].pos + n_tokens >= INT32_MAX)
+      return KVE_EINVAL;
     blocks += layers[l].bh;
-    if (ctrs[l].n_kept > max_n) max_n = ctrs[l].n_kept;
+    const int32_t n_last = std::min(ctrs[l].n_kept + n_tokens - 1, budgets[l]);
+    if (n_last > max_n) max_n = n_last;
   }
   if (blocks > INT32_MAX) return KVE_EINVAL;
   const int dev_state = check_device();
@@ -250,16 +259,26 @@ int batch_impl(int32_t n_layers, const kve_layer *layers, const void *const *new
 
   char *hslot = r.host + (size_t)slot * Ring::kSlotBytes;
   char *dslot = r.dev + (size_t)slot * Ring::kSlotBytes;
+  const size_t table_off = sizeof(kve::LayerArgs) * kve::kMaxBatchLayers;
   kve::LayerArgs *hl = reinterpret_cast<kve::LayerArgs *>(hslot);
-  kve::RopeTable *ht =
-      reinterpret_cast<kve::RopeTable *>(hslot + sizeof(kve::LayerArgs) * kve::kMaxBatchLayers);
+  kve::RopeTable *ht = reinterpret_cast<kve::RopeTable *>(hslot + table_off);
   int n_tables = 0;
   int32_t block0 = 0;
   for (int32_t l = 0; l < n_layers; ++l) {
     hl[l] = layer_args(&layers[l], new_k[l], new_v[l], &ctrs[l], budgets[l],
                        evicted ? evicted[l] : nullptr, gumbel);
     hl[l].block0 = block0;
+    hl[l].n_tokens = n_tokens;
     block0 += layers[l].bh;
+    if (n_tokens > 1) {
+      // one incoming-row table per token (the rows it moves to depend on it)
+      hl[l].table = n_tables;
+      for (int32_t t = 0; t < n_tokens; ++t) {
+        const int32_t n_t = std::min(ctrs[l].n_kept + t, budgets[l]);
+        incoming_table(d, rope_base, n_t, ctrs[l].next_pos + t, &ht[n_tables++]);
+      }
+      continue;
+    }
     // one incoming-row table per distinct (n_kept, next_pos)
     int t = -1;
     for (int32_t m = 0; m < l && t < 0; ++m)
@@ -275,7 +294,6 @@ int batch_impl(int32_t n_layers, const kve_layer *layers, const void *const *new
       shared_args(d, n_sink, tau_init, tau_end, anneal_steps, rope_base, seed, gumbel);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const size_t layer_bytes = sizeof(kve::LayerArgs) * n_layers;
-  const size_t table_off = sizeof(kve::LayerArgs) * kve::kMaxBatchLayers;
   // The copy runs on the library's own stream (it touches only this slot, which
   // no queued launch reads any more), so it overlaps the caller's earlier work;
   // the launch on the caller's stream waits for it.
@@ -293,7 +311,8 @@ int batch_impl(int32_t n_layers, const kve_layer *layers, const void *const *new
   if (err != hipSuccess) return KVE_ELAUNCH;
   if (hipEventRecord(r.done[slot], s) != hipSuccess) return KVE_ELAUNCH;
   r.pending[slot] = true;
-  for (int32_t l = 0; l < n_layers; ++l) advance(&ctrs[l], budgets[l]);
+  for (int32_t l = 0; l < n_layers; ++l)
+    for (int32_t t = 0; t < n_tokens; ++t) advance(&ctrs[l], budgets[l]);
   return KVE_OK;
 }
 
@@ -321,15 +340,36 @@ KVE_EXPORT int keyformer_step_layers(int32_t n_layers, const kve_layer *layers,
                                      double tau_init, double tau_end, int32_t anneal_steps,
                                      double rope_base, uint64_t seed, int32_t *const *evicted,
                                      void *stream) {
-  return batch_impl(n_layers, layers, new_k, new_v, ctrs, budgets, n_sink, tau_init, tau_end,
+  return batch_impl(n_layers, 1, layers, new_k, new_v, ctrs, budgets, n_sink, tau_init, tau_end,
                     anneal_steps, rope_base, seed, evicted, stream, true);
+}
+
+KVE_EXPORT int keyformer_step_tokens(const kve_layer *L, int32_t n_tokens, const void *new_k,
+                                     const void *new_v, kve_counters *ctr, int32_t budget,
+                                     int32_t n_sink, double tau_init, double tau_end,
+                                     int32_t anneal_steps, double rope_base, uint64_t seed,
+                                     int32_t *evicted, void *stream) {
+  if (!L) return KVE_EINVAL;
+  int32_t *ev[1] = {evicted};
+  return batch_impl(1, n_tokens, L, &new_k, &new_v, ctr, &budget, n_sink, tau_init, tau_end,
+                    anneal_steps, rope_base, seed, ev, stream, true);
+}
+
+KVE_EXPORT int pyramid_step_tokens(const kve_layer *L, int32_t n_tokens, const void *new_k,
+                                   const void *new_v, kve_counters *ctr, int32_t budget,
+                                   int32_t n_sink, double rope_base, int32_t *evicted,
+                                   void *stream) {
+  if (!L) return KVE_EINVAL;
+  int32_t *ev[1] = {evicted};
+  return batch_impl(1, n_tokens, L, &new_k, &new_v, ctr, &budget, n_sink, 0.0, 0.0, 0,
+                    rope_base, 0, ev, stream, false);
 }
 
 KVE_EXPORT int pyramid_step_layers(int32_t n_layers, const kve_layer *layers,
                                    const void *const *new_k, const void *const *new_v,
                                    kve_counters *ctrs, const int32_t *budgets, int32_t n_sink,
                                    double rope_base, int32_t *const *evicted, void *stream) {
-  return batch_impl(n_layers, layers, new_k, new_v, ctrs, budgets, n_sink, 0.0, 0.0, 0,
+  return batch_impl(n_layers, 1, layers, new_k, new_v, ctrs, budgets, n_sink, 0.0, 0.0, 0,
                     rope_base, 0, evicted, stream, false);
 }
 

@@ -9,6 +9,8 @@ namespace kve {
 
 constexpr int kMaxHalfD = 64;        // d <= 128
 constexpr int kMaxBatchLayers = 128; // layers in one batched call
+constexpr int kMaxTables = 128;      // incoming-row tables in one descriptor-driven launch
+constexpr int kMaxTokens = 128;      // tokens in one multi-token call
 
 // fp32 cosine / sine of one rotation angle per RoPE pair, computed on the
 // host in fp64 and rounded once.
@@ -34,7 +36,9 @@ struct LayerArgs {
   int32_t pos;
   int32_t hh_base;         // Gumbel stream of cache 0
   int32_t block0;          // first workgroup of this layer in a batched launch
-  int32_t table;           // index of this layer's incoming-row rotation table
+  int32_t table;           // incoming-row rotation table of this layer's first token
+  int32_t n_tokens;        // tokens stepped by this launch (descriptor-driven kernel)
+  int32_t pad_;
 };
 
 // What every layer of a launch shares.
@@ -52,7 +56,9 @@ struct SharedArgs {
 hipError_t launch_step(const LayerArgs &la, const SharedArgs &sa, const RopeTable &rnew, int bh,
                        int d, bool gumbel, hipStream_t stream);
 
-// Several layers per launch: `layers` and `tables` are device memory.
+// Several layers and/or several tokens per launch: `layers` and `tables` are
+// device memory; layer l steps layers[l].n_tokens tokens, token t using table
+// layers[l].table + t, incoming rows new_k + t*bh*d, outputs evicted + t*bh.
 hipError_t launch_step_layers(const LayerArgs *layers, const RopeTable *tables, int n_layers,
                               int total_blocks, int max_n_prev, const SharedArgs &sa, int d,
                               bool gumbel, hipStream_t stream);

@@ -477,8 +477,12 @@ __global__ __launch_bounds__(NT) void step_kernel(LayerArgs la, SharedArgs sa, R
   step_body<D, NT, U, GUMBEL>(la, sa, rnew, blockIdx.x);
 }
 
-// Several layers per launch: the workgroups of layer l are block0(l) ..
-// block0(l+1)-1; layer descriptors and rotation tables live in device memory.
+// Several layers and/or tokens per launch: the workgroups of layer l are
+// block0(l) .. block0(l+1)-1; layer descriptors and rotation tables live in
+// device memory.  A workgroup steps its cache through the layer's tokens one
+// after the other (keyformer_update absorbs S tokens as S steps); between
+// tokens every store of the workgroup has landed and every wave has arrived,
+// so the next token reads the state the previous one left.
 template <int D, int NT, int U, bool GUMBEL>
 __global__ __launch_bounds__(NT) void step_layers_kernel(const LayerArgs *__restrict__ layers,
                                                          const RopeTable *__restrict__ tables,
@@ -494,7 +498,21 @@ __global__ __launch_bounds__(NT) void step_layers_kernel(const LayerArgs *__rest
     count += __popcll(__ballot(starts));
   }
   const LayerArgs &la = layers[count - 1];
-  step_body<D, NT, U, GUMBEL>(la, sa, tables[la.table], b - la.block0);
+  const int hh = b - la.block0;
+  const int n_tokens = la.n_tokens;
+  const int bh = (count < n_layers ? layers[count].block0 : (int)gridDim.x) - la.block0;
+  LayerArgs lt = la;
+  for (int t = 0; t < n_tokens; ++t) {
+    lt.n_prev = min(la.n_prev + t, la.budget);
+    lt.next_pos = la.next_pos + t;
+    lt.pos = la.pos + t;
+    lt.new_k = reinterpret_cast<const char *>(la.new_k) + (size_t)t * bh * D * 2;
+    lt.new_v = reinterpret_cast<const char *>(la.new_v) + (size_t)t * bh * D * 2;
+    lt.evicted = la.evicted ? la.evicted + (size_t)t * bh : nullptr;
+    step_body<D, NT, U, GUMBEL>(lt, sa, tables[la.table + t], hh);
+    __builtin_amdgcn_s_waitcnt(0);              // this token's stores have landed
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -28,7 +28,8 @@ def _declared() -> list[str]:
 
 def test_header_declares_the_abi():
     assert set(_declared()) == {"keyformer_step", "pyramid_step", "keyformer_step_layers",
-                                "pyramid_step_layers", "pyramid_budgets", "kve_strerror"}
+                                "pyramid_step_layers", "keyformer_step_tokens",
+                                "pyramid_step_tokens", "pyramid_budgets", "kve_strerror"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -214,3 +215,16 @@ def test_batched_pyramid_null_gumbel_passes_host_checks():
         pytest.skip("a GPU is present; the no-device path is not reachable")
     assert rc == kve.KVE_ENODEV
     assert after == [(32, 100, 100)] * 2
+
+
+@pytest.mark.parametrize("n_tokens,ctr", [(0, (32, 100, 100)), (129, (32, 100, 100)),
+                                          (4, (10, 50, 50)), (4, (40, 100, 100))])
+def test_multi_token_rejects_before_any_launch(n_tokens, ctr):
+    layer = _layer()
+    c = Counters(*ctr)
+    rc = kve.lib().keyformer_step_tokens(ctypes.byref(layer), n_tokens, FAKE, FAKE, ctypes.byref(c),
+                                         32, 4, 1.0, 2.0, 64, 1e4, 0, None, None)
+    assert rc == kve.KVE_EINVAL
+    assert (c.n_kept, c.next_pos, c.pos) == ctr
+    assert kve.lib().pyramid_step_tokens(None, 4, FAKE, FAKE, ctypes.byref(c), 32, 4, 1e4, None,
+                                         None) == kve.KVE_EINVAL

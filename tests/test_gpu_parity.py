@@ -445,3 +445,72 @@ def test_full_trajectory_8b_late_riser(dev):
     _assert_parity(L, ev, samples, 0)
     moved = [(ev[w.budget:, s.hh] < w.budget).mean() for s in samples]
     assert max(moved) > 0.02                               # interior evictions happened
+
+
+
+# ---------------------------------------------------------------------------
+# multi-token calls: S tokens per launch
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["kf", "pk"])
+@pytest.mark.parametrize("d,S", [(128, 7), (64, 64), (128, 1)])
+def test_multi_token_equals_single_calls(dev, kind, d, S):
+    """keyformer_step_tokens / pyramid_step_tokens of S tokens give the same
+    bits as S single-token calls, across the budget boundary and with interior
+    evictions."""
+    import kv_cache_eviction_step_amd as kve
+    kf = kind == "kf"
+    bh, budget, cap, T = 12, 48, 53, 200
+    _say(f"[tokens==single] kind={kind} d={d} S={S} T={T}")
+    w = synth.Workload("mt", 1, 1, 1, d, T, 0, budget, 4, "keyformer" if kf else "pyramid",
+                       1.0 if kf else 0.0, 2.0 if kf else 0.0, 80 if kf else 0)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    nk, nv = synth.bulk_kv_torch(w, 0, T, bh, gen, dev)
+    A = kve.Layer.empty(bh, cap, d, dev, gumbel=kf, hh_base=3)
+    B = kve.Layer.empty(bh, cap, d, dev, gumbel=kf, hh_base=3)
+    ca, cb = kve.Counters(0, 0, 0), kve.Counters(0, 0, 0)
+    eva = torch.empty((T, bh), dtype=torch.int32, device=dev)
+    evb = torch.empty((T, bh), dtype=torch.int32, device=dev)
+    for t in range(T):
+        if kf:
+            kve.keyformer_step(A, nk[t], nv[t], ca, budget, 4, 1.0, 2.0, 80, 1e4, 5, eva[t])
+        else:
+            kve.pyramid_step(A, nk[t], nv[t], ca, budget, 4, 1e4, eva[t])
+    for t0 in range(0, T, S):
+        t1 = min(T, t0 + S)
+        if kf:
+            kve.keyformer_step_tokens(B, nk[t0:t1], nv[t0:t1], cb, budget, 4, 1.0, 2.0, 80, 1e4, 5,
+                                      evb[t0:t1])
+        else:
+            kve.pyramid_step_tokens(B, nk[t0:t1], nv[t0:t1], cb, budget, 4, 1e4, evb[t0:t1])
+    torch.cuda.synchronize()
+    assert (ca.n_kept, ca.next_pos, ca.pos) == (cb.n_kept, cb.next_pos, cb.pos)
+    assert torch.equal(eva, evb)
+    n = ca.n_kept
+    for name in ("k", "v", "scores", "positions") + (("gumbel",) if kf else ()):
+        assert torch.equal(getattr(A, name)[:, :n], getattr(B, name)[:, :n]), name
+    if kf:
+        assert bool(((eva >= 0) & (eva < budget)).any())
+
+
+def test_multi_token_full_trajectory_oracle(dev):
+    """The Llama-3.2-3B-shaped Keyformer trajectory (3072 tokens) in calls of
+    64 tokens, against the oracle for every cache of the layer."""
+    import kv_cache_eviction_step_amd as kve
+    w = synth.WORKLOADS[1]
+    S, T = 64, w.tokens
+    _say(f"[tokens-oracle] {w.name} layer 2 S={S} T={T}")
+    samples = oracle_samples(w, 2, range(w.bh), w.budget, T, w.budget + 1)
+    L = kve.Layer.empty(w.bh, w.budget + 1, w.d, dev)
+    nk = torch.stack([torch.from_numpy(s.ks.view(np.float16)) for s in samples], 1).to(dev)
+    nv = torch.stack([torch.from_numpy(s.vs.view(np.float16)) for s in samples], 1).to(dev)
+    ev = torch.full((T, w.bh), -7, dtype=torch.int32, device=dev)
+    ctr = kve.Counters(0, 0, 0)
+    prm = params_for(w, w.budget, 0)
+    for t0 in range(0, T, S):
+        kve.keyformer_step_tokens(L, nk[t0:t0 + S].contiguous(), nv[t0:t0 + S].contiguous(), ctr,
+                                  w.budget, w.n_sink, prm.tau_init, prm.tau_end,
+                                  prm.anneal_steps, w.rope_base, w.gumbel_seed, ev[t0:t0 + S])
+    torch.cuda.synchronize()
+    _assert_parity(L, ev.cpu().numpy(), samples, 0)

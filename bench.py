@@ -1,10 +1,12 @@
 #!/usr/bin/env python3
 """Throughput of the KV-cache eviction step on one MI355X.
 
-A step is one decode token through every layer: L launches (one per layer),
-each stepping all B*H caches of that layer through keyformer_step or
-pyramid_step.  Inputs are resident in HBM before the timed region.  Timing is
-bracketed by HIP events on the stream the kernels run on.
+A step is one decode token through every layer.  By default that is L
+launches (one per layer), each stepping all B*H caches of that layer through
+keyformer_step or pyramid_step; --batched puts all layers in one launch and
+--tokens-per-call S steps S tokens per launch.  Inputs are resident in HBM
+before the timed region.  Timing is bracketed by HIP events on the stream the
+kernels run on.
 
 Prints ONE JSON line: cache-row updates/s (B*L*H*tokens per second) as
 `value`, the achieved algorithmic HBM bandwidth of the step kernel against
@@ -45,8 +47,9 @@ def parse():
                     help="one launch per token for all layers (keyformer_step_layers / "
                          "pyramid_step_layers) instead of one launch per layer")
     ap.add_argument("--tokens-per-call", type=int, default=1,
-                    help="S > 1: one launch per layer steps S tokens (keyformer_step_tokens / "
-                         "pyramid_step_tokens); --steps must be a multiple of S")
+                    help="S > 1: each launch steps S tokens (*_step_tokens per layer, or "
+                         "*_step_layers_tokens with --batched); S must divide --steps and "
+                         "--warmup")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the CPU oracle baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -68,11 +71,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(config: int, batched: bool):
+def launch_mode(batched: bool, tokens_per_call: int) -> str:
+    return ("all-layers" if batched else "per-layer") + f"_x{tokens_per_call}tok"
+
+
+def measured_traffic(workload: str, kernel: str, mode: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary of this
-    workload, or None when it is missing or the kernel changed since."""
-    kern = "step_layers_kernel" if batched else "step_kernel"
-    path = os.path.join(ROOT, "profiles", f"{kern}_configs{config}_pmc_traffic.md")
+    workload and launch mode, or None when it is missing or the kernel changed
+    since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_{mode}_pmc_traffic.md")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -224,105 +231,99 @@ def main():
 
     # ---- inputs for warmup + timed steps, resident in HBM ----------------------
     TPC = args.tokens_per_call
-    if TPC > 1 and (args.batched or args.steps % TPC or args.warmup % TPC):
-        print("--tokens-per-call needs per-layer launches and steps/warmup multiples of it",
+    if TPC < 1 or TPC > 128 or args.steps % TPC or args.warmup % TPC:
+        print("--tokens-per-call must be 1..128 and divide --steps and --warmup",
               file=sys.stderr)
         sys.exit(2)
     S = args.warmup + args.steps
-    if TPC > 1:          # token-major per layer: [L, S, bh, d]
-        nk = torch.empty((L, S, bh, d), dtype=torch.float16, device=dev)
-        nv = torch.empty_like(nk)
-        for l in range(L):
-            nk[l], nv[l] = synth.bulk_kv_torch(w, pos0, S, bh, gen, dev)
-        ev_tok = torch.full((L, args.steps, bh), -9, dtype=torch.int32, device=dev)
-    else:                # layer-major per token: [S, L, bh, d]
-        nk = torch.empty((S, L, bh, d), dtype=torch.float16, device=dev)
-        nv = torch.empty_like(nk)
-        for l in range(L):
-            k, v = synth.bulk_kv_torch(w, pos0, S, bh, gen, dev)
-            nk[:, l], nv[:, l] = k, v
-    ev = torch.full((args.steps, L, bh), -9, dtype=torch.int32, device=dev)
-    n_prev = [[0] * L for _ in range(args.steps)]
+    # [L, S, bh, d]: each layer's tokens contiguous, so that any run of TPC
+    # tokens of a layer is one contiguous [TPC, bh, d] block
+    nk = torch.empty((L, S, bh, d), dtype=torch.float16, device=dev)
+    nv = torch.empty_like(nk)
+    for l in range(L):
+        nk[l], nv[l] = synth.bulk_kv_torch(w, pos0, S, bh, gen, dev)
+    ev = torch.full((L, args.steps, bh), -9, dtype=torch.int32, device=dev)
+    n_prev = np.zeros((args.steps, L), dtype=np.int64)
     torch.cuda.synchronize()
 
-    batch = None
-    if args.batched:
-        batch = kve.LayerBatch(layers, budgets, ctrs)
-
-    def step_all(s, evs=None):
-        """One token through every layer: one launch, or one per layer."""
-        if batch is not None:
-            if kf:
-                kve.keyformer_step_layers(batch, nk[s], nv[s], w.n_sink, w.tau_init, w.tau_end,
-                                          w.anneal_steps, w.rope_base, w.gumbel_seed, evs)
-            else:
-                kve.pyramid_step_layers(batch, nk[s], nv[s], w.n_sink, w.rope_base, evs)
-        else:
-            for l in range(L):
-                step_layer(l, nk[s, l], nv[s, l], evs[l] if evs is not None else None)
-
-    def counters(l):
-        return batch.ctrs[l] if batch is not None else ctrs[l]
-
-    def step_tokens(s0, evs=None):
-        """TPC tokens starting at input s0 through every layer, one launch per layer."""
-        for l in range(L):
-            e_l = evs[l] if evs is not None else None
-            if kf:
-                kve.keyformer_step_tokens(layers[l], nk[l, s0:s0 + TPC], nv[l, s0:s0 + TPC],
-                                          ctrs[l], budgets[l], w.n_sink, w.tau_init, w.tau_end,
-                                          w.anneal_steps, w.rope_base, w.gumbel_seed, e_l,
-                                          c_layer=cls[l])
-            else:
-                kve.pyramid_step_tokens(layers[l], nk[l, s0:s0 + TPC], nv[l, s0:s0 + TPC],
-                                        ctrs[l], budgets[l], w.n_sink, w.rope_base, e_l,
-                                        c_layer=cls[l])
-
-    if TPC > 1:
-        for s0 in range(0, args.warmup, TPC):
-            step_tokens(s0)
+    batch = kve.LayerBatch(layers, budgets, ctrs) if args.batched else None
+    counters = (lambda l: batch.ctrs[l]) if batch is not None else (lambda l: ctrs[l])
+    name = "keyformer" if kf else "pyramid"
+    if batch is not None:
+        entry = f"{name}_step_layers" + ("_tokens" if TPC > 1 else "")
     else:
-        for s in range(args.warmup):
-            step_all(s)
+        entry = f"{name}_step" + ("_tokens" if TPC > 1 else "")
+
+    def call(s0, ev_out=None):
+        """Tokens s0 .. s0+TPC-1 (input index) through every layer."""
+        if batch is not None:
+            if TPC > 1:
+                ks, vs = nk[:, s0:s0 + TPC], nv[:, s0:s0 + TPC]
+                if kf:
+                    kve.keyformer_step_layers_tokens(batch, ks, vs, w.n_sink, w.tau_init,
+                                                     w.tau_end, w.anneal_steps, w.rope_base,
+                                                     w.gumbel_seed, ev_out, n_tokens=TPC)
+                else:
+                    kve.pyramid_step_layers_tokens(batch, ks, vs, w.n_sink, w.rope_base, ev_out,
+                                                   n_tokens=TPC)
+            elif kf:
+                kve.keyformer_step_layers(batch, nk[:, s0], nv[:, s0], w.n_sink, w.tau_init,
+                                          w.tau_end, w.anneal_steps, w.rope_base, w.gumbel_seed,
+                                          ev_out[:, 0] if ev_out is not None else None)
+            else:
+                kve.pyramid_step_layers(batch, nk[:, s0], nv[:, s0], w.n_sink, w.rope_base,
+                                        ev_out[:, 0] if ev_out is not None else None)
+            return
+        for l in range(L):
+            e_l = ev_out[l] if ev_out is not None else None
+            if TPC > 1:
+                if kf:
+                    kve.keyformer_step_tokens(layers[l], nk[l, s0:s0 + TPC], nv[l, s0:s0 + TPC],
+                                              ctrs[l], budgets[l], w.n_sink, w.tau_init,
+                                              w.tau_end, w.anneal_steps, w.rope_base,
+                                              w.gumbel_seed, e_l, c_layer=cls[l])
+                else:
+                    kve.pyramid_step_tokens(layers[l], nk[l, s0:s0 + TPC], nv[l, s0:s0 + TPC],
+                                            ctrs[l], budgets[l], w.n_sink, w.rope_base, e_l,
+                                            c_layer=cls[l])
+            else:
+                step_layer(l, nk[l, s0], nv[l, s0], e_l[0] if e_l is not None else None)
+
+    for s0 in range(0, args.warmup, TPC):
+        call(s0)
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
-    if TPC > 1:
-        for s0 in range(0, args.steps, TPC):
-            for l in range(L):
-                for i in range(TPC):
-                    n_prev[s0 + i][l] = min(ctrs[l].n_kept + i, budgets[l])
-            step_tokens(args.warmup + s0, [ev_tok[l, s0:s0 + TPC] for l in range(L)])
-    else:
-        for s in range(args.steps):
-            for l in range(L):
-                n_prev[s][l] = counters(l).n_kept
-            step_all(args.warmup + s, ev[s])
+    for s0 in range(0, args.steps, TPC):
+        for l in range(L):
+            nk0 = counters(l).n_kept
+            for i in range(TPC):
+                n_prev[s0 + i, l] = min(nk0 + i, budgets[l])
+        call(args.warmup + s0, ev[:, s0:s0 + TPC])
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
-    if TPC > 1:
-        ev = ev_tok.permute(1, 0, 2)
 
     # ---- algorithmic bytes from the eviction log --------------------------------
-    evn = ev.cpu().numpy()
+    evn = ev.cpu().numpy().transpose(1, 0, 2)              # [steps, L, bh]
     total_bytes = 0
     for s in range(args.steps):
         for l in range(L):
-            n = n_prev[s][l]
+            n = int(n_prev[s, l])
             e = evn[s, l]
             m = np.where((e >= 0) & (e < n), n - e, 0).astype(np.int64)
             total_bytes += int(step_bytes(w.kind, n, d, m).sum())
-    launches = args.steps * (1 if batch is not None else L) // TPC
+    launches = (args.steps // TPC) * (1 if batch is not None else L)
     sec = ms / 1e3
     updates = bh * L * args.steps
     avg_launch_s = sec / launches
     bytes_per_launch = total_bytes / launches
     achieved = bytes_per_launch / avg_launch_s / 1e9
-    mean_m = float(np.where((evn >= 0), np.maximum(0, np.array(n_prev)[:, :, None] - evn),
-                            0).mean())
+    mean_m = float(np.where(evn >= 0, np.maximum(0, n_prev[:, :, None] - evn), 0).mean())
 
+    kernel = "step_layers_kernel" if batch is not None or TPC > 1 else "step_kernel"
+    mode = launch_mode(args.batched, TPC)
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(w, budgets, args.cpu_seconds)
@@ -341,25 +342,21 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"configs[{args.config}] {w.name}: B={w.batch} layers={L} "
+            "workload": f"{w.name}: B={w.batch} layers={L} "
                         f"kv_heads={w.kv_heads} D={d} {w.kind} budget="
                         f"{'pyramid avg ' if w.kind == 'pyramid' else ''}{w.budget} "
                         f"n_sink={w.n_sink}",
             "kv_storage": "f16", "bh_per_launch": bh, "layers": L,
             "budgets": [budgets[0], budgets[-1]], "steady_state_fill": args.fill,
             "fill_seconds": round(t_fill, 1), "mean_rows_moved_per_cache_step": mean_m,
-            "launch": ("one launch per token over all layers (" +
-                       ("keyformer" if kf else "pyramid") + "_step_layers)") if batch is not None
-                      else (f"one launch per layer per {TPC} tokens (" +
-                            ("keyformer" if kf else "pyramid") + "_step_tokens)") if TPC > 1
-                      else "one launch per layer (" + ("keyformer" if kf else "pyramid") + "_step)",
+            "launch": (f"one launch per {TPC} token(s) "
+                       f"{'over all layers' if batch is not None else 'per layer'} ({entry})"),
+            "tokens_per_launch": TPC, "layers_per_launch": L if batch is not None else 1,
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(args.config, args.batched or TPC > 1)
-            if TPC == 1 else None,
-            "kernel": ("kve::step_layers_kernel" if batch is not None or TPC > 1
-                       else "kve::step_kernel"),
+            "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(w.name, kernel, mode),
+            "kernel": "kve::" + kernel,
             "avg_launch_us": avg_launch_s * 1e6,
             "algorithmic_bytes_per_launch": bytes_per_launch,
         },

@@ -185,8 +185,8 @@ int pyramid_step_layers(int32_t n_layers, const kve_layer *layers, const void *c
  *   ctr        advanced by S tokens on success
  *   other arguments as keyformer_step / pyramid_step.
  * Checked as one per-layer call (the first token's counters), plus
- * 1 <= n_tokens <= 128.  Uses the batched calls' descriptor ring (one
- * rotation table per token); not for use under stream capture.
+ * 1 <= n_tokens <= 128.  Uses the batched calls' descriptor ring; not for use
+ * under stream capture.
  */
 int keyformer_step_tokens(const kve_layer *L, int32_t n_tokens, const void *new_k,
                           const void *new_v, kve_counters *ctr, int32_t budget, int32_t n_sink,
@@ -196,6 +196,37 @@ int keyformer_step_tokens(const kve_layer *L, int32_t n_tokens, const void *new_
 int pyramid_step_tokens(const kve_layer *L, int32_t n_tokens, const void *new_k,
                         const void *new_v, kve_counters *ctr, int32_t budget, int32_t n_sink,
                         double rope_base, int32_t *evicted, void *stream);
+
+/*
+ * keyformer_step_layers_tokens / pyramid_step_layers_tokens -- both of the
+ * above at once: S consecutive tokens into every cache of n_layers layers in
+ * ONE launch, bit for bit the same as S calls of the *_step_layers form (or
+ * n_layers * S per-layer calls).  Each layer's workgroups walk its caches
+ * through the S tokens; layers never wait for one another.  This is the form
+ * that fills the device when each layer has few caches (small batch).
+ *
+ *   n_layers   1 .. 128;  n_tokens  S, 1 .. 128
+ *   layers, ctrs, budgets, n_sink, tau_*, anneal_steps, rope_base, seed,
+ *   stream     as keyformer_step_layers; each ctrs[l] advances by S tokens
+ *   new_k,new_v  HOST arrays [n_layers] of device pointers, fp16
+ *              [S][bh_l][d]: token t's incoming rows of layer l at
+ *              new_k[l] + t*bh_l*d
+ *   evicted    HOST array [n_layers] of device i32 [S][bh_l] (entries may be
+ *              NULL), or NULL
+ * Checked and queued as keyformer_step_layers (same descriptor ring; not for
+ * use under stream capture).
+ */
+int keyformer_step_layers_tokens(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
+                                 const void *const *new_k, const void *const *new_v,
+                                 kve_counters *ctrs, const int32_t *budgets, int32_t n_sink,
+                                 double tau_init, double tau_end, int32_t anneal_steps,
+                                 double rope_base, uint64_t seed, int32_t *const *evicted,
+                                 void *stream);
+
+int pyramid_step_layers_tokens(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
+                               const void *const *new_k, const void *const *new_v,
+                               kve_counters *ctrs, const int32_t *budgets, int32_t n_sink,
+                               double rope_base, int32_t *const *evicted, void *stream);
 
 /*
  * pyramid_budgets -- per-layer budgets ("The budget schedule"): a linear taper

@@ -89,6 +89,16 @@ _lib.pyramid_step_tokens.argtypes = [
     ctypes.POINTER(KveLayer), ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
     ctypes.POINTER(Counters), ctypes.c_int32, ctypes.c_int32, ctypes.c_double, ctypes.c_void_p,
     ctypes.c_void_p]
+_lib.keyformer_step_layers_tokens.restype = ctypes.c_int
+_lib.keyformer_step_layers_tokens.argtypes = [
+    ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(KveLayer), ctypes.c_void_p, ctypes.c_void_p,
+    ctypes.POINTER(Counters), ctypes.c_void_p, ctypes.c_int32, ctypes.c_double, ctypes.c_double,
+    ctypes.c_int32, ctypes.c_double, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+_lib.pyramid_step_layers_tokens.restype = ctypes.c_int
+_lib.pyramid_step_layers_tokens.argtypes = [
+    ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(KveLayer), ctypes.c_void_p, ctypes.c_void_p,
+    ctypes.POINTER(Counters), ctypes.c_void_p, ctypes.c_int32, ctypes.c_double, ctypes.c_void_p,
+    ctypes.c_void_p]
 _lib.pyramid_budgets.restype = ctypes.c_int
 _lib.pyramid_budgets.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                  ctypes.c_double, ctypes.c_void_p]
@@ -96,7 +106,8 @@ _lib.kve_strerror.restype = ctypes.c_char_p
 _lib.kve_strerror.argtypes = [ctypes.c_int]
 
 EXPORTED = ("keyformer_step", "pyramid_step", "keyformer_step_layers", "pyramid_step_layers",
-            "keyformer_step_tokens", "pyramid_step_tokens", "pyramid_budgets", "kve_strerror")
+            "keyformer_step_tokens", "pyramid_step_tokens", "keyformer_step_layers_tokens",
+            "pyramid_step_layers_tokens", "pyramid_budgets", "kve_strerror")
 
 
 def lib() -> ctypes.CDLL:
@@ -214,6 +225,16 @@ def pyramid_step(layer: Layer, new_k, new_v, ctr: Counters, budget: int, n_sink:
     _check(rc, "pyramid_step")
 
 
+def _blocks_contiguous(t) -> bool:
+    """Every t[i] is contiguous (any stride along dimension 0)."""
+    expect = 1
+    for size, stride in zip(reversed(t.shape[1:]), reversed(t.stride()[1:])):
+        if size != 1 and stride != expect:
+            return False
+        expect *= size
+    return t.stride(0) >= 0
+
+
 class LayerBatch:
     """Several layers stepped together by keyformer_step_layers / pyramid_step_layers.
 
@@ -241,18 +262,28 @@ class LayerBatch:
             raise ValueError("all layers must be on one device")
         self.device = dev
 
-    def _fill(self, new_k, new_v, evicted):
-        """Pointer arrays for this call.  new_k / new_v: a list of [bh_l, d]
-        tensors, or one contiguous [n_layers, bh, d] tensor; evicted: None, a
-        list of [bh_l] int32 tensors, or one contiguous [n_layers, bh] tensor."""
+    def _fill(self, new_k, new_v, evicted, n_tokens: int | None = None):
+        """Pointer arrays for this call.
+
+        One token (n_tokens None): new_k / new_v are a list of [bh_l, d]
+        tensors or one [n_layers, bh, d] tensor; evicted is None, a list of
+        [bh_l] int32 tensors or one [n_layers, bh] tensor.  S tokens
+        (n_tokens S): the same with a token axis after the layer axis:
+        [S, bh_l, d] per layer or [n_layers, S, bh, d]; evicted [S, bh_l] per
+        layer or [n_layers, S, bh].  A single tensor may have any stride along
+        the layer axis (a slice of a longer token axis, say) as long as each
+        layer's block is contiguous."""
         n = self.n
+        tok = () if n_tokens is None else (n_tokens,)
         for arr, src, name in ((self._pk, new_k, "new_k"), (self._pv, new_v, "new_v")):
             if isinstance(src, torch.Tensor):
                 L0 = self.layers[0]
-                if (src.dtype != torch.float16 or src.dim() != 3 or src.shape[0] != n or
-                        not src.is_contiguous() or src.device != self.device or
-                        any(tuple(src.shape[1:]) != (x.bh, x.d) for x in self.layers)):
-                    raise ValueError(f"{name} must be contiguous float16 [{n}, {L0.bh}, {L0.d}]")
+                if (src.dtype != torch.float16 or src.dim() != 3 + len(tok) or
+                        src.shape[0] != n or not _blocks_contiguous(src) or
+                        src.device != self.device or
+                        any(tuple(src.shape[1:]) != tok + (x.bh, x.d) for x in self.layers)):
+                    raise ValueError(f"{name} must be float16 {[n, *tok, L0.bh, L0.d]} "
+                                     "with contiguous per-layer blocks")
                 base, step = src.data_ptr(), src.stride(0) * 2
                 for i in range(n):
                     arr[i] = base + i * step
@@ -260,14 +291,21 @@ class LayerBatch:
                 if len(src) != n:
                     raise ValueError(f"{name}: one tensor per layer")
                 for i in range(n):
-                    arr[i] = _rows(src[i], self.layers[i], name)
+                    if n_tokens is None:
+                        arr[i] = _rows(src[i], self.layers[i], name)
+                    else:
+                        if src[i].shape[0] != n_tokens:
+                            raise ValueError(f"{name}[{i}]: {n_tokens} tokens expected")
+                        arr[i] = _tokens(src[i], self.layers[i], name)
         if evicted is None:
             return None
         if isinstance(evicted, torch.Tensor):
-            if (evicted.dtype != torch.int32 or evicted.dim() != 2 or evicted.shape[0] != n or
-                    not evicted.is_contiguous() or evicted.device != self.device or
-                    any(evicted.shape[1] != x.bh for x in self.layers)):
-                raise ValueError("evicted must be contiguous int32 [n_layers, bh]")
+            if (evicted.dtype != torch.int32 or evicted.dim() != 2 + len(tok) or
+                    evicted.shape[0] != n or not _blocks_contiguous(evicted) or
+                    evicted.device != self.device or
+                    any(tuple(evicted.shape[1:]) != tok + (x.bh,) for x in self.layers)):
+                raise ValueError(f"evicted must be int32 {[n, *tok, 'bh']} with contiguous "
+                                 "per-layer blocks")
             base, step = evicted.data_ptr(), evicted.stride(0) * 4
             for i in range(n):
                 self._pe[i] = base + i * step
@@ -275,8 +313,13 @@ class LayerBatch:
             if len(evicted) != n:
                 raise ValueError("evicted: one tensor (or None) per layer")
             for i in range(n):
-                self._pe[i] = (_evicted_ptr(evicted[i], self.layers[i])
-                               if evicted[i] is not None else None)
+                e = evicted[i]
+                if e is None:
+                    self._pe[i] = None
+                elif n_tokens is None:
+                    self._pe[i] = _evicted_ptr(e, self.layers[i])
+                else:
+                    self._pe[i] = _evicted_tokens(e, self.layers[i], n_tokens)
         return self._pe
 
 
@@ -349,6 +392,33 @@ def pyramid_step_tokens(layer: Layer, new_k, new_v, ctr: Counters, budget: int, 
                                   rope_base, _evicted_tokens(evicted, layer, n),
                                   _stream_ptr(stream, layer))
     _check(rc, "pyramid_step_tokens")
+
+
+def keyformer_step_layers_tokens(batch: LayerBatch, new_k, new_v, n_sink: int, tau_init: float,
+                                 tau_end: float, anneal_steps: int, rope_base: float, seed: int,
+                                 evicted=None, stream=None, n_tokens: int | None = None) -> None:
+    """S consecutive tokens into every cache of every layer of `batch`, one launch.
+
+    new_k / new_v: [n_layers, S, bh, d] or a list of [S, bh_l, d]; evicted:
+    None, [n_layers, S, bh] or a list of [S, bh_l] (or None entries)."""
+    S = n_tokens if n_tokens is not None else new_k[0].shape[0]
+    pe = batch._fill(new_k, new_v, evicted, S)
+    rc = _lib.keyformer_step_layers_tokens(batch.n, S, batch.c_layers, batch._pk, batch._pv,
+                                           batch.ctrs, batch.budgets, n_sink, tau_init, tau_end,
+                                           anneal_steps, rope_base, seed & 0xFFFFFFFFFFFFFFFF,
+                                           pe, _stream_ptr(stream, batch.layers[0]))
+    _check(rc, "keyformer_step_layers_tokens")
+
+
+def pyramid_step_layers_tokens(batch: LayerBatch, new_k, new_v, n_sink: int, rope_base: float,
+                               evicted=None, stream=None, n_tokens: int | None = None) -> None:
+    """S consecutive tokens into every cache of every layer of `batch` (H2O / PyramidKV)."""
+    S = n_tokens if n_tokens is not None else new_k[0].shape[0]
+    pe = batch._fill(new_k, new_v, evicted, S)
+    rc = _lib.pyramid_step_layers_tokens(batch.n, S, batch.c_layers, batch._pk, batch._pv,
+                                         batch.ctrs, batch.budgets, n_sink, rope_base, pe,
+                                         _stream_ptr(stream, batch.layers[0]))
+    _check(rc, "pyramid_step_layers_tokens")
 
 
 def pyramid_budgets(n_layers: int, avg_budget: int, n_sink: int, beta: float) -> list[int]:

@@ -130,20 +130,12 @@ kve::SharedArgs shared_args(int d, int32_t n_sink, double tau_init, double tau_e
   for (int j = 0; j < d / 2; ++j) {
     sa.back1.c[j] = fc.cos_m1[j];
     sa.back1.s[j] = fc.sin_m1[j];
+    // The incoming row, if it survives an older row's eviction, goes from
+    // next_pos to slot n-1: the device rotates it by (n-1-next_pos) * freq[j]
+    // with an fp64 sincos rounded once to fp32.
+    sa.freq[j] = fc.freq[j];
   }
   return sa;
-}
-
-// The incoming row, if it survives an older row's eviction, goes from
-// next_pos to slot n-1: one rotation by n - 1 - next_pos positions.
-void incoming_table(int d, double rope_base, int32_t n, int32_t next_pos, kve::RopeTable *t) {
-  const FreqCache &fc = freqs(d, rope_base);
-  const double delta = (double)(n - 1) - (double)next_pos;
-  for (int j = 0; j < d / 2; ++j) {
-    const double th = delta * fc.freq[j];
-    t->c[j] = (float)std::cos(th);
-    t->s[j] = (float)std::sin(th);
-  }
 }
 
 void advance(kve_counters *ctr, int32_t budget) {
@@ -164,12 +156,8 @@ int step_impl(const kve_layer *L, const void *new_k, const void *new_v, kve_coun
   const kve::LayerArgs la = layer_args(L, new_k, new_v, ctr, budget, evicted, gumbel);
   const kve::SharedArgs sa =
       shared_args(L->d, n_sink, tau_init, tau_end, anneal_steps, rope_base, seed, gumbel);
-  kve::RopeTable rnew;
-  std::memset(&rnew, 0, sizeof(rnew));
-  if (ctr->n_kept + 1 > budget) incoming_table(L->d, rope_base, ctr->n_kept, ctr->next_pos, &rnew);
-
   const hipError_t err =
-      kve::launch_step(la, sa, rnew, L->bh, L->d, gumbel, reinterpret_cast<hipStream_t>(stream));
+      kve::launch_step(la, sa, L->bh, L->d, gumbel, reinterpret_cast<hipStream_t>(stream));
   if (err != hipSuccess) return KVE_ELAUNCH;
   advance(ctr, budget);
   return KVE_OK;
@@ -183,8 +171,7 @@ int step_impl(const kve_layer *L, const void *new_k, const void *new_v, kve_coun
 
 struct Ring {
   static constexpr int kSlots = 64;
-  static constexpr size_t kSlotBytes =
-      sizeof(kve::LayerArgs) * kve::kMaxBatchLayers + sizeof(kve::RopeTable) * kve::kMaxTables;
+  static constexpr size_t kSlotBytes = sizeof(kve::LayerArgs) * kve::kMaxBatchLayers;
   std::mutex mu;
   bool ready = false;
   char *host = nullptr;
@@ -216,16 +203,15 @@ int ring_init(Ring &r) {
   return KVE_OK;
 }
 
-// One descriptor-driven launch: n_layers layers, each stepped n_tokens tokens
-// (n_tokens > 1 only with a single layer).  Checks every layer first.
+// One descriptor-driven launch: n_layers layers, each stepped n_tokens tokens.
+// Checks every layer first.
 int batch_impl(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
                const void *const *new_k, const void *const *new_v, kve_counters *ctrs,
                const int32_t *budgets, int32_t n_sink, double tau_init, double tau_end,
                int32_t anneal_steps, double rope_base, uint64_t seed, int32_t *const *evicted,
                void *stream, bool gumbel) {
   if (n_layers < 1 || n_layers > kve::kMaxBatchLayers) return KVE_EINVAL;
-  if (n_tokens < 1 || n_tokens > kve::kMaxTokens || (n_tokens > 1 && n_layers != 1))
-    return KVE_EINVAL;
+  if (n_tokens < 1 || n_tokens > kve::kMaxTokens) return KVE_EINVAL;
   if (!layers || !new_k || !new_v || !ctrs || !budgets) return KVE_EINVAL;
   if (check_shared(tau_init, tau_end, anneal_steps, rope_base) != KVE_OK) return KVE_EINVAL;
   const int d = layers[0].d;
@@ -259,10 +245,7 @@ int batch_impl(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
 
   char *hslot = r.host + (size_t)slot * Ring::kSlotBytes;
   char *dslot = r.dev + (size_t)slot * Ring::kSlotBytes;
-  const size_t table_off = sizeof(kve::LayerArgs) * kve::kMaxBatchLayers;
   kve::LayerArgs *hl = reinterpret_cast<kve::LayerArgs *>(hslot);
-  kve::RopeTable *ht = reinterpret_cast<kve::RopeTable *>(hslot + table_off);
-  int n_tables = 0;
   int32_t block0 = 0;
   for (int32_t l = 0; l < n_layers; ++l) {
     hl[l] = layer_args(&layers[l], new_k[l], new_v[l], &ctrs[l], budgets[l],
@@ -270,25 +253,6 @@ int batch_impl(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
     hl[l].block0 = block0;
     hl[l].n_tokens = n_tokens;
     block0 += layers[l].bh;
-    if (n_tokens > 1) {
-      // one incoming-row table per token (the rows it moves to depend on it)
-      hl[l].table = n_tables;
-      for (int32_t t = 0; t < n_tokens; ++t) {
-        const int32_t n_t = std::min(ctrs[l].n_kept + t, budgets[l]);
-        incoming_table(d, rope_base, n_t, ctrs[l].next_pos + t, &ht[n_tables++]);
-      }
-      continue;
-    }
-    // one incoming-row table per distinct (n_kept, next_pos)
-    int t = -1;
-    for (int32_t m = 0; m < l && t < 0; ++m)
-      if (ctrs[m].n_kept == ctrs[l].n_kept && ctrs[m].next_pos == ctrs[l].next_pos)
-        t = hl[m].table;
-    if (t < 0) {
-      t = n_tables++;
-      incoming_table(d, rope_base, ctrs[l].n_kept, ctrs[l].next_pos, &ht[t]);
-    }
-    hl[l].table = t;
   }
   const kve::SharedArgs sa =
       shared_args(d, n_sink, tau_init, tau_end, anneal_steps, rope_base, seed, gumbel);
@@ -299,15 +263,12 @@ int batch_impl(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
   // the launch on the caller's stream waits for it.
   if (hipMemcpyAsync(dslot, hslot, layer_bytes, hipMemcpyHostToDevice, r.copy_stream) !=
           hipSuccess ||
-      hipMemcpyAsync(dslot + table_off, hslot + table_off, sizeof(kve::RopeTable) * n_tables,
-                     hipMemcpyHostToDevice, r.copy_stream) != hipSuccess ||
       hipEventRecord(r.copied[slot], r.copy_stream) != hipSuccess ||
       hipStreamWaitEvent(s, r.copied[slot], 0) != hipSuccess)
     return KVE_ELAUNCH;
-  const hipError_t err = kve::launch_step_layers(
-      reinterpret_cast<const kve::LayerArgs *>(dslot),
-      reinterpret_cast<const kve::RopeTable *>(dslot + table_off), n_layers, (int)blocks, max_n,
-      sa, d, gumbel, s);
+  const hipError_t err =
+      kve::launch_step_layers(reinterpret_cast<const kve::LayerArgs *>(dslot), n_layers,
+                              (int)blocks, max_n, sa, d, gumbel, s);
   if (err != hipSuccess) return KVE_ELAUNCH;
   if (hipEventRecord(r.done[slot], s) != hipSuccess) return KVE_ELAUNCH;
   r.pending[slot] = true;
@@ -371,6 +332,28 @@ KVE_EXPORT int pyramid_step_layers(int32_t n_layers, const kve_layer *layers,
                                    double rope_base, int32_t *const *evicted, void *stream) {
   return batch_impl(n_layers, 1, layers, new_k, new_v, ctrs, budgets, n_sink, 0.0, 0.0, 0,
                     rope_base, 0, evicted, stream, false);
+}
+
+KVE_EXPORT int keyformer_step_layers_tokens(int32_t n_layers, int32_t n_tokens,
+                                            const kve_layer *layers, const void *const *new_k,
+                                            const void *const *new_v, kve_counters *ctrs,
+                                            const int32_t *budgets, int32_t n_sink,
+                                            double tau_init, double tau_end,
+                                            int32_t anneal_steps, double rope_base,
+                                            uint64_t seed, int32_t *const *evicted,
+                                            void *stream) {
+  return batch_impl(n_layers, n_tokens, layers, new_k, new_v, ctrs, budgets, n_sink, tau_init,
+                    tau_end, anneal_steps, rope_base, seed, evicted, stream, true);
+}
+
+KVE_EXPORT int pyramid_step_layers_tokens(int32_t n_layers, int32_t n_tokens,
+                                          const kve_layer *layers, const void *const *new_k,
+                                          const void *const *new_v, kve_counters *ctrs,
+                                          const int32_t *budgets, int32_t n_sink,
+                                          double rope_base, int32_t *const *evicted,
+                                          void *stream) {
+  return batch_impl(n_layers, n_tokens, layers, new_k, new_v, ctrs, budgets, n_sink, 0.0, 0.0,
+                    0, rope_base, 0, evicted, stream, false);
 }
 
 // "The budget schedule": linear taper, mean avg_budget, floor n_sink + 1.

@@ -9,11 +9,10 @@ namespace kve {
 
 constexpr int kMaxHalfD = 64;        // d <= 128
 constexpr int kMaxBatchLayers = 128; // layers in one batched call
-constexpr int kMaxTables = 128;      // incoming-row tables in one descriptor-driven launch
 constexpr int kMaxTokens = 128;      // tokens in one multi-token call
 
-// fp32 cosine / sine of one rotation angle per RoPE pair, computed on the
-// host in fp64 and rounded once.
+// fp32 cosine / sine of one rotation angle per RoPE pair, computed in fp64
+// and rounded once.
 struct RopeTable {
   float c[kMaxHalfD];
   float s[kMaxHalfD];
@@ -36,9 +35,7 @@ struct LayerArgs {
   int32_t pos;
   int32_t hh_base;         // Gumbel stream of cache 0
   int32_t block0;          // first workgroup of this layer in a batched launch
-  int32_t table;           // incoming-row rotation table of this layer's first token
   int32_t n_tokens;        // tokens stepped by this launch (descriptor-driven kernel)
-  int32_t pad_;
 };
 
 // What every layer of a launch shares.
@@ -50,17 +47,19 @@ struct SharedArgs {
   uint64_t seed;
   float scale;             // 1 / sqrt(d) in fp32
   RopeTable back1;         // rotation by -1 position (moved stored rows)
+  double freq[kMaxHalfD];  // RoPE pair frequencies base^(-2j/d), fp64 from the host; the
+                           // incoming row's rotation is evaluated from them on the device
 };
 
 // One layer per launch: everything by value.
-hipError_t launch_step(const LayerArgs &la, const SharedArgs &sa, const RopeTable &rnew, int bh,
-                       int d, bool gumbel, hipStream_t stream);
+hipError_t launch_step(const LayerArgs &la, const SharedArgs &sa, int bh, int d, bool gumbel,
+                       hipStream_t stream);
 
-// Several layers and/or several tokens per launch: `layers` and `tables` are
-// device memory; layer l steps layers[l].n_tokens tokens, token t using table
-// layers[l].table + t, incoming rows new_k + t*bh*d, outputs evicted + t*bh.
-hipError_t launch_step_layers(const LayerArgs *layers, const RopeTable *tables, int n_layers,
-                              int total_blocks, int max_n_prev, const SharedArgs &sa, int d,
-                              bool gumbel, hipStream_t stream);
+// Several layers and/or several tokens per launch: `layers` is device memory;
+// layer l steps layers[l].n_tokens tokens, token t reading its incoming rows at
+// new_k + t*bh*d and writing evicted + t*bh.
+hipError_t launch_step_layers(const LayerArgs *layers, int n_layers, int total_blocks,
+                              int max_n_prev, const SharedArgs &sa, int d, bool gumbel,
+                              hipStream_t stream);
 
 }  // namespace kve

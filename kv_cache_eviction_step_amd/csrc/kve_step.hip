@@ -32,6 +32,19 @@ namespace kve {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // one 16-byte chunk
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Global-memory pointer.  The layer descriptors of the batched kernel are read
+// from memory, so the compiler cannot tell on its own that their pointers are
+// global; without this every access would be a flat one (64-bit address per
+// lane, and counted against the LDS wait counter too).
+template <typename T>
+using gptr = __attribute__((address_space(1))) T *;
+
+template <typename T>
+__device__ __forceinline__ gptr<T> global(T *p) {
+  return (gptr<T>)p;
+}
 
 // ---------------------------------------------------------------------------
 // device helpers
@@ -51,6 +64,19 @@ __device__ __noinline__ float gumbel_at(uint64_t seed, uint64_t stream, uint64_t
   uint64_t h = splitmix64_out(splitmix64_out(splitmix64_out(seed) ^ stream) ^ pos);
   double u = ((double)(h >> 11) + 0.5) * 0x1p-53;
   return (float)(-log(-log(u)));
+}
+
+// cos and sin of delta * freq: fp64 sincos, each rounded once to fp32 (the
+// incoming row's rotation, keyformer FIXED GAP #2).  Not inlined: its
+// polynomial constants would otherwise be hoisted out of the token loop of
+// the batched kernel and held in registers for the whole launch.
+__device__ __noinline__ f32x2 rotation_at(int32_t delta, double freq) {
+  double sv, cv;
+  sincos((double)delta * freq, &sv, &cv);
+  f32x2 r;
+  r.x = (float)cv;
+  r.y = (float)sv;
+  return r;
 }
 
 // Annealed temperature (keyformer FIXED GAP #1), fp64, rounded once.
@@ -187,10 +213,37 @@ __device__ __forceinline__ void load_dword_to_lds(const float *src, float *lds_w
                                    0, 0);
 }
 
-// The whole step for cache `hh` of layer `la` (one workgroup).
+// x, unchanged, through an empty asm: the optimiser can no longer treat it
+// as loop-invariant (wave-uniform values only: the asm takes a scalar register).
+template <typename T>
+__device__ __forceinline__ T opaque(T x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
+// Rotation constants shared by every token of a launch, copied from the
+// kernel arguments into LDS once per workgroup by wave 0.  Reading them from
+// LDS (not from the argument segment, which the compiler treats as invariant
+// and would keep in registers across the token loop) keeps register use low.
+__shared__ float lds_back_c[kMaxHalfD];      // rotation by -1 position
+__shared__ float lds_back_s[kMaxHalfD];
+__shared__ double lds_freq[kMaxHalfD];       // RoPE pair frequencies (fp64)
+
+template <int D>
+__device__ __forceinline__ void stage_tables(const SharedArgs &sa) {
+  const int tid = threadIdx.x;
+  if (tid < D / 2) {                            // wave 0: the only reader of lds_freq
+    lds_back_c[tid] = sa.back1.c[tid];
+    lds_back_s[tid] = sa.back1.s[tid];
+    lds_freq[tid] = sa.freq[tid];
+  }
+}
+
+// The whole step for cache `hh` of layer `la` (one workgroup).  stage_tables
+// has run in this workgroup.
 template <int D, int NT, int U, bool GUMBEL>
 __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs &sa,
-                                          const RopeTable &rnew, const int hh) {
+                                          const int hh) {
   constexpr int V16 = D / 8;        // 16-byte chunks per row
   constexpr int LPR = D / 8;        // score pass: lanes per row (one chunk each)
   constexpr int RPS = NT / LPR;     // score pass: rows per sweep
@@ -207,6 +260,8 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   __shared__ int red_i[NWAVE];
   __shared__ float bc_v;
   __shared__ int bc_e;
+  __shared__ float rn_c[kMaxHalfD];          // incoming row's rotation (wave 0 only)
+  __shared__ float rn_s[kMaxHalfD];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -218,24 +273,29 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   float *__restrict__ lds_x = lds;
   float *__restrict__ lds_s = lds + np;
   float *__restrict__ lds_g = lds + 2 * np;
-  float *__restrict__ scores = la.scores;
-  float *__restrict__ gumbel = la.gumbel;
+  const gptr<float> __restrict__ scores = global(la.scores);
+  const gptr<float> __restrict__ gumbel = global(la.gumbel);
+  // When this step evicts, the incoming row may have to move from next_pos to
+  // slot n-1; wave 0 evaluates that rotation while its first keys load.
+  const bool rn_lane = over && wave == 0 && lane < D / 2;
+  const double rn_freq = rn_lane ? lds_freq[lane] : 0.0;   // staged by this same lane
 
   // ---- prefetch scores (and, when evicting, gumbel) into LDS ---------------
   // Every lane issues a load (the tail clamps to row n-1 and lands in padding).
   for (int base = wave * 64; base < n; base += NT) {
     const int i = min(base + lane, n - 1);
-    load_dword_to_lds(scores + row0 + i, lds_s + base);
-    if (GUMBEL && over) load_dword_to_lds(gumbel + row0 + i, lds_g + base);
+    load_dword_to_lds(la.scores + row0 + i, lds_s + base);
+    if (GUMBEL && over) load_dword_to_lds(la.gumbel + row0 + i, lds_g + base);
   }
 
   // ---- A: logits of every stored row against the incoming key -------------
   // Two batches of U loads in flight: batch it+1 is issued before batch it
   // is consumed.  Rows past n are clamped to row n-1 (a cache hit) and dropped.
-  const u32x4 *__restrict__ K4 = reinterpret_cast<const u32x4 *>(la.k) + row0 * V16;
+  const gptr<const u32x4> __restrict__ K4 =
+      global(reinterpret_cast<const u32x4 *>(la.k)) + row0 * V16;
   const int lr = tid % LPR;
   const int rr = tid / LPR;
-  const u32x4 q = reinterpret_cast<const u32x4 *>(la.new_k)[(size_t)hh * V16 + lr];
+  const u32x4 q = global(reinterpret_cast<const u32x4 *>(la.new_k))[(size_t)hh * V16 + lr];
   const float scale = sa.scale;
   float mx = -INFINITY;
   const int iters = (n + ROWS_IT - 1) / ROWS_IT;
@@ -264,8 +324,13 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   // for the batch being consumed while the next one is in flight).  The LDS
   // prefetch above must land before the first LDS write: wait for it right
   // after issuing the first batch, so the two latencies overlap.
+  if (iters > 0) load_batch(0, bufa);
+  if (rn_lane) {
+    const f32x2 r = rotation_at(n - 1 - la.next_pos, rn_freq);
+    rn_c[lane] = r.x;
+    rn_s[lane] = r.y;
+  }
   if (iters > 0) {
-    load_batch(0, bufa);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(U));
     int it = 0;
     for (; it + 2 < iters; it += 2) {
@@ -352,10 +417,10 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   }
   __syncthreads();
   const int e = bc_e;
-  if (tid == 0 && la.evicted) la.evicted[hh] = e;
+  if (tid == 0 && la.evicted) global(la.evicted)[hh] = e;
 
   // ---- D: write-back ----------------------------------------------------------
-  int32_t *__restrict__ positions = la.positions;
+  const gptr<int32_t> __restrict__ positions = global(la.positions);
   for (int i = tid; i < n; i += NT) {
     if (e < 0 || i < e) {
       scores[row0 + i] = lds_s[i];
@@ -366,8 +431,8 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
     }
   }
 
-  u32x4 *__restrict__ Kw = reinterpret_cast<u32x4 *>(la.k) + row0 * V16;
-  u32x4 *__restrict__ Vw = reinterpret_cast<u32x4 *>(la.v) + row0 * V16;
+  const gptr<u32x4> __restrict__ Kw = global(reinterpret_cast<u32x4 *>(la.k)) + row0 * V16;
+  const gptr<u32x4> __restrict__ Vw = global(reinterpret_cast<u32x4 *>(la.v)) + row0 * V16;
   const int lm = tid % LPM;                     // chunk lm of the first half, lm of the second
   const int rm = tid / LPM;
 
@@ -385,8 +450,8 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
     float cs[8], sn[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      cs[j] = sa.back1.c[lm * 8 + j];
-      sn[j] = sa.back1.s[lm * 8 + j];
+      cs[j] = lds_back_c[lm * 8 + j];
+      sn[j] = lds_back_s[lm * 8 + j];
     }
     u32x4 ak1[UM], ak2[UM], av1[UM], av2[UM];
     u32x4 bk1[UM], bk2[UM], bv1[UM], bv2[UM];
@@ -446,15 +511,15 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   // or nowhere (it was the one evicted)
   const int f = e < 0 ? n : (e < n ? n - 1 : -1);
   if (f >= 0 && tid < LPM) {
-    const u32x4 *nk = reinterpret_cast<const u32x4 *>(la.new_k) + (size_t)hh * V16;
-    const u32x4 *nv = reinterpret_cast<const u32x4 *>(la.new_v) + (size_t)hh * V16;
+    const gptr<const u32x4> nk = global(reinterpret_cast<const u32x4 *>(la.new_k)) + (size_t)hh * V16;
+    const gptr<const u32x4> nv = global(reinterpret_cast<const u32x4 *>(la.new_v)) + (size_t)hh * V16;
     u32x4 k1 = nk[lm], k2 = nk[lm + V16 / 2];
     if (e >= 0) {                                // moved: rotate to position f
-      float cs[8], sn[8];
+      float cs[8], sn[8];                        // written above by this same wave
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        cs[j] = rnew.c[lm * 8 + j];
-        sn[j] = rnew.s[lm * 8 + j];
+        cs[j] = rn_c[lm * 8 + j];
+        sn[j] = rn_s[lm * 8 + j];
       }
       rotate_chunk(k1, k2, cs, sn);
     }
@@ -473,19 +538,18 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
 
 // One layer per launch: workgroup hh owns cache hh.
 template <int D, int NT, int U, bool GUMBEL>
-__global__ __launch_bounds__(NT) void step_kernel(LayerArgs la, SharedArgs sa, RopeTable rnew) {
-  step_body<D, NT, U, GUMBEL>(la, sa, rnew, blockIdx.x);
+__global__ __launch_bounds__(NT) void step_kernel(LayerArgs la, SharedArgs sa) {
+  stage_tables<D>(sa);
+  step_body<D, NT, U, GUMBEL>(la, sa, blockIdx.x);
 }
 
 // Several layers and/or tokens per launch: the workgroups of layer l are
-// block0(l) .. block0(l+1)-1; layer descriptors and rotation tables live in
-// device memory.  A workgroup steps its cache through the layer's tokens one
+// block0(l) .. block0(l+1)-1; layer descriptors live in device memory.  A workgroup steps its cache through the layer's tokens one
 // after the other (keyformer_update absorbs S tokens as S steps); between
 // tokens every store of the workgroup has landed and every wave has arrived,
 // so the next token reads the state the previous one left.
 template <int D, int NT, int U, bool GUMBEL>
 __global__ __launch_bounds__(NT) void step_layers_kernel(const LayerArgs *__restrict__ layers,
-                                                         const RopeTable *__restrict__ tables,
                                                          int n_layers, SharedArgs sa) {
   // layer of this workgroup: the number of layers starting at or before it,
   // counted with one load per lane and a ballot (at most 128 layers)
@@ -501,15 +565,26 @@ __global__ __launch_bounds__(NT) void step_layers_kernel(const LayerArgs *__rest
   const int hh = b - la.block0;
   const int n_tokens = la.n_tokens;
   const int bh = (count < n_layers ? layers[count].block0 : (int)gridDim.x) - la.block0;
+  stage_tables<D>(sa);
   LayerArgs lt = la;
   for (int t = 0; t < n_tokens; ++t) {
+    // Re-derive every per-cache address on each token (the asm hides these
+    // values from the optimiser): hoisting them out of the loop would hold
+    // them in registers for the whole launch.
+    lt.k = opaque(la.k);
+    lt.v = opaque(la.v);
+    lt.scores = opaque(la.scores);
+    lt.gumbel = opaque(la.gumbel);
+    lt.positions = opaque(la.positions);
+    lt.cap = opaque(la.cap);
+    const int hh_t = opaque(hh);
     lt.n_prev = min(la.n_prev + t, la.budget);
     lt.next_pos = la.next_pos + t;
     lt.pos = la.pos + t;
     lt.new_k = reinterpret_cast<const char *>(la.new_k) + (size_t)t * bh * D * 2;
     lt.new_v = reinterpret_cast<const char *>(la.new_v) + (size_t)t * bh * D * 2;
     lt.evicted = la.evicted ? la.evicted + (size_t)t * bh : nullptr;
-    step_body<D, NT, U, GUMBEL>(lt, sa, tables[la.table + t], hh);
+    step_body<D, NT, U, GUMBEL>(lt, sa, hh_t);
     __builtin_amdgcn_s_waitcnt(0);              // this token's stores have landed
     __syncthreads();
   }
@@ -542,50 +617,44 @@ static hipError_t allow_lds(K kern, size_t bytes) {
 }
 
 template <int D, bool GUMBEL>
-static hipError_t launch_d(const LayerArgs &la, const SharedArgs &sa, const RopeTable &rnew,
-                           int bh, hipStream_t stream) {
+static hipError_t launch_d(const LayerArgs &la, const SharedArgs &sa, int bh,
+                           hipStream_t stream) {
   auto kern = step_kernel<D, kThreads, kUnroll, GUMBEL>;
   const size_t lds = lds_bytes_for(la.n_prev, GUMBEL);
   hipError_t err = allow_lds(kern, lds);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(kern, dim3(bh), dim3(kThreads), lds, stream, la, sa, rnew);
+  hipLaunchKernelGGL(kern, dim3(bh), dim3(kThreads), lds, stream, la, sa);
   return hipGetLastError();
 }
 
 template <int D, bool GUMBEL>
-static hipError_t launch_layers_d(const LayerArgs *layers, const RopeTable *tables, int n_layers,
-                                  int total_blocks, int max_n_prev, const SharedArgs &sa,
-                                  hipStream_t stream) {
+static hipError_t launch_layers_d(const LayerArgs *layers, int n_layers, int total_blocks,
+                                  int max_n_prev, const SharedArgs &sa, hipStream_t stream) {
   auto kern = step_layers_kernel<D, kThreads, kUnroll, GUMBEL>;
   const size_t lds = lds_bytes_for(max_n_prev, GUMBEL);
   hipError_t err = allow_lds(kern, lds);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(kern, dim3(total_blocks), dim3(kThreads), lds, stream, layers, tables,
-                     n_layers, sa);
+  hipLaunchKernelGGL(kern, dim3(total_blocks), dim3(kThreads), lds, stream, layers, n_layers,
+                     sa);
   return hipGetLastError();
 }
 
-hipError_t launch_step(const LayerArgs &la, const SharedArgs &sa, const RopeTable &rnew, int bh,
-                       int d, bool gumbel, hipStream_t stream) {
+hipError_t launch_step(const LayerArgs &la, const SharedArgs &sa, int bh, int d, bool gumbel,
+                       hipStream_t stream) {
   if (d == 128)
-    return gumbel ? launch_d<128, true>(la, sa, rnew, bh, stream)
-                  : launch_d<128, false>(la, sa, rnew, bh, stream);
-  return gumbel ? launch_d<64, true>(la, sa, rnew, bh, stream)
-                : launch_d<64, false>(la, sa, rnew, bh, stream);
+    return gumbel ? launch_d<128, true>(la, sa, bh, stream) : launch_d<128, false>(la, sa, bh, stream);
+  return gumbel ? launch_d<64, true>(la, sa, bh, stream) : launch_d<64, false>(la, sa, bh, stream);
 }
 
-hipError_t launch_step_layers(const LayerArgs *layers, const RopeTable *tables, int n_layers,
-                              int total_blocks, int max_n_prev, const SharedArgs &sa, int d,
-                              bool gumbel, hipStream_t stream) {
+hipError_t launch_step_layers(const LayerArgs *layers, int n_layers, int total_blocks,
+                              int max_n_prev, const SharedArgs &sa, int d, bool gumbel,
+                              hipStream_t stream) {
   if (d == 128)
-    return gumbel ? launch_layers_d<128, true>(layers, tables, n_layers, total_blocks,
-                                               max_n_prev, sa, stream)
-                  : launch_layers_d<128, false>(layers, tables, n_layers, total_blocks,
-                                                max_n_prev, sa, stream);
-  return gumbel ? launch_layers_d<64, true>(layers, tables, n_layers, total_blocks, max_n_prev,
-                                            sa, stream)
-                : launch_layers_d<64, false>(layers, tables, n_layers, total_blocks, max_n_prev,
-                                             sa, stream);
+    return gumbel ? launch_layers_d<128, true>(layers, n_layers, total_blocks, max_n_prev, sa, stream)
+                  : launch_layers_d<128, false>(layers, n_layers, total_blocks, max_n_prev, sa,
+                                                stream);
+  return gumbel ? launch_layers_d<64, true>(layers, n_layers, total_blocks, max_n_prev, sa, stream)
+                : launch_layers_d<64, false>(layers, n_layers, total_blocks, max_n_prev, sa, stream);
 }
 
 }  // namespace kve

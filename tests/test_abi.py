@@ -29,7 +29,8 @@ def _declared() -> list[str]:
 def test_header_declares_the_abi():
     assert set(_declared()) == {"keyformer_step", "pyramid_step", "keyformer_step_layers",
                                 "pyramid_step_layers", "keyformer_step_tokens",
-                                "pyramid_step_tokens", "pyramid_budgets", "kve_strerror"}
+                                "pyramid_step_tokens", "keyformer_step_layers_tokens",
+                                "pyramid_step_layers_tokens", "pyramid_budgets", "kve_strerror"}
 
 
 def test_library_exports_every_declared_symbol():

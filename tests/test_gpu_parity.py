@@ -514,3 +514,97 @@ def test_multi_token_full_trajectory_oracle(dev):
                                   prm.anneal_steps, w.rope_base, w.gumbel_seed, ev[t0:t0 + S])
     torch.cuda.synchronize()
     _assert_parity(L, ev.cpu().numpy(), samples, 0)
+
+
+@pytest.mark.parametrize("kind", ["kf", "pk"])
+@pytest.mark.parametrize("d,S", [(128, 7), (64, 64), (128, 128)])
+def test_layers_tokens_equals_single_calls(dev, kind, d, S):
+    """keyformer_step_layers_tokens / pyramid_step_layers_tokens over layers of
+    different sizes, budgets and Gumbel streams give the same bits as one
+    single-token call per layer and token; the layers cross their budgets at
+    different tokens of one call."""
+    import kv_cache_eviction_step_amd as kve
+    kf = kind == "kf"
+    shapes = [(5, 48, 53, 0), (12, 20, 21, 7), (9, 33, 40, 100)]   # bh, budget, cap, hh_base
+    T = 180
+    _say(f"[layers*tokens==single] kind={kind} d={d} S={S} T={T}")
+    w = synth.Workload("lt", 1, 3, 1, d, T, 0, 48, 4, "keyformer" if kf else "pyramid",
+                       1.0 if kf else 0.0, 2.0 if kf else 0.0, 80 if kf else 0)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(23)
+    nks, nvs, As, Bs, evas, evbs, cas = [], [], [], [], [], [], []
+    for bh, budget, cap, hb in shapes:
+        k, v = synth.bulk_kv_torch(w, 0, T, bh, gen, dev)
+        nks.append(k)
+        nvs.append(v)
+        As.append(kve.Layer.empty(bh, cap, d, dev, gumbel=kf, hh_base=hb))
+        Bs.append(kve.Layer.empty(bh, cap, d, dev, gumbel=kf, hh_base=hb))
+        evas.append(torch.empty((T, bh), dtype=torch.int32, device=dev))
+        evbs.append(torch.full((T, bh), -9, dtype=torch.int32, device=dev))
+        cas.append(kve.Counters(0, 0, 0))
+    budgets = [s[1] for s in shapes]
+    for t in range(T):
+        for l in range(len(shapes)):
+            if kf:
+                kve.keyformer_step(As[l], nks[l][t], nvs[l][t], cas[l], budgets[l], 4, 1.0, 2.0,
+                                   80, 1e4, 5, evas[l][t])
+            else:
+                kve.pyramid_step(As[l], nks[l][t], nvs[l][t], cas[l], budgets[l], 4, 1e4,
+                                 evas[l][t])
+    batch = kve.LayerBatch(Bs, budgets)
+    for t0 in range(0, T, S):
+        t1 = min(T, t0 + S)
+        ks = [x[t0:t1] for x in nks]
+        vs = [x[t0:t1] for x in nvs]
+        es = [x[t0:t1] for x in evbs]
+        if kf:
+            kve.keyformer_step_layers_tokens(batch, ks, vs, 4, 1.0, 2.0, 80, 1e4, 5, es)
+        else:
+            kve.pyramid_step_layers_tokens(batch, ks, vs, 4, 1e4, es)
+    torch.cuda.synchronize()
+    for l in range(len(shapes)):
+        cb = batch.ctrs[l]
+        assert (cas[l].n_kept, cas[l].next_pos, cas[l].pos) == (cb.n_kept, cb.next_pos, cb.pos)
+        assert torch.equal(evas[l], evbs[l]), l
+        n = cas[l].n_kept
+        for name in ("k", "v", "scores", "positions") + (("gumbel",) if kf else ()):
+            assert torch.equal(getattr(As[l], name)[:, :n], getattr(Bs[l], name)[:, :n]), \
+                (l, name)
+
+
+@pytest.mark.parametrize("wi,layers", [(2, [0, 14, 27]), (1, [2, 20])],
+                         ids=["pyramid-beta2", "keyformer"])
+def test_layers_tokens_full_trajectory_oracle(dev, wi, layers):
+    """Llama-3.2-3B-shaped layers (PyramidKV: budgets from the top, middle and
+    bottom of the schedule; Keyformer: two layers) stepped together through
+    the full 3072 tokens in calls of 64 tokens, against the oracle for every
+    cache."""
+    import kv_cache_eviction_step_amd as kve
+    w = synth.WORKLOADS[wi]
+    kf = w.kind == "keyformer"
+    S, T = 64, w.tokens
+    budgets = [w.budgets(oracle.pyramid_budgets)[l] for l in layers]
+    _say(f"[layers*tokens-oracle] {w.name} layers={layers} budgets={budgets} S={S} T={T}")
+    samples = [oracle_samples(w, l, range(w.bh), b, T, b + 1) for l, b in zip(layers, budgets)]
+    Ls = [kve.Layer.empty(w.bh, b + 1, w.d, dev, gumbel=kf) for b in budgets]
+    nk = [torch.stack([torch.from_numpy(s.ks.view(np.float16)) for s in ss], 1).to(dev)
+          for ss in samples]
+    nv = [torch.stack([torch.from_numpy(s.vs.view(np.float16)) for s in ss], 1).to(dev)
+          for ss in samples]
+    ev = torch.full((len(layers), T, w.bh), -7, dtype=torch.int32, device=dev)
+    batch = kve.LayerBatch(Ls, budgets)
+    prm = params_for(w, budgets[0], 0)
+    for t0 in range(0, T, S):
+        ks = [x[t0:t0 + S] for x in nk]
+        vs = [x[t0:t0 + S] for x in nv]
+        es = [ev[i, t0:t0 + S] for i in range(len(layers))]
+        if kf:
+            kve.keyformer_step_layers_tokens(batch, ks, vs, w.n_sink, prm.tau_init, prm.tau_end,
+                                             prm.anneal_steps, w.rope_base, w.gumbel_seed, es)
+        else:
+            kve.pyramid_step_layers_tokens(batch, ks, vs, w.n_sink, w.rope_base, es)
+    torch.cuda.synchronize()
+    evh = ev.cpu().numpy()
+    for i in range(len(layers)):
+        _assert_parity(Ls[i], evh[i], samples[i], 0)
+        assert batch.ctrs[i].n_kept == budgets[i]

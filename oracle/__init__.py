@@ -55,6 +55,7 @@ class _Params(ctypes.Structure):
         ("tau_init", ctypes.c_double), ("tau_end", ctypes.c_double),
         ("rope_base", ctypes.c_double),
         ("seed", ctypes.c_uint64), ("hh", ctypes.c_int64),
+        ("recent", ctypes.c_int32), ("current_score", ctypes.c_int32),
     ]
 
 
@@ -167,11 +168,14 @@ class Params:
     rope_base: float = 10000.0
     seed: int = 0
     hh: int = 0
+    recent: int = 0                  # trailing protected window (0 = off)
+    current_score: bool = False      # TOVA-adapted: score = this step's weight
 
     def c(self) -> _Params:
         return _Params(self.budget, self.n_sink, 1 if self.use_gumbel else 0,
                        self.anneal_steps, self.tau_init, self.tau_end, self.rope_base,
-                       self.seed & (2**64 - 1), self.hh)
+                       self.seed & (2**64 - 1), self.hh, self.recent,
+                       1 if self.current_score else 0)
 
 
 class OracleCache:

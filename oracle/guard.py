@@ -38,7 +38,8 @@ def params_for(w: synth.Workload, budget: int, hh: int) -> Params:
     return Params(budget=budget, n_sink=w.n_sink, use_gumbel=kf,
                   tau_init=w.tau_init if kf else 0.0, tau_end=w.tau_end if kf else 0.0,
                   anneal_steps=w.anneal_steps if kf else 0, rope_base=w.rope_base,
-                  seed=w.gumbel_seed, hh=hh)
+                  seed=w.gumbel_seed, hh=hh, recent=w.recent,
+                  current_score=w.kind == "tova")
 
 
 def guarded_trajectory(w: synth.Workload, layer: int, hh: int, budget: int, T: int,

@@ -209,7 +209,10 @@ int oracle_step(oracle_cache *c, const uint16_t *k, const uint16_t *v,
 {
     const int32_t d = c->d;
     const int32_t n = c->n;            /* rows stored before this token */
-    if (d <= 0 || (d & 1) || n < 0 || prm->n_sink < 0 || prm->budget <= prm->n_sink ||
+    /* [KF] init_keyformer_state: the protected rows (sinks and the recent   */
+    /* window) must leave room to evict within the budget.                    */
+    if (d <= 0 || (d & 1) || n < 0 || prm->n_sink < 0 || prm->recent < 0 ||
+        prm->budget <= prm->n_sink + prm->recent ||
         c->cap < prm->budget + 1 || n > prm->budget || n + 1 > c->cap)
         return -1;
 
@@ -240,9 +243,11 @@ int oracle_step(oracle_cache *c, const uint16_t *k, const uint16_t *v,
             w[i] = exp(x[i] - mx);
             z += w[i];
         }
+        /* TOVA-adapted ([PK] table of eviction axes): the score is the        */
+        /* current step's weight alone.                                        */
         for (int32_t i = 0; i < n; ++i) {
             float inc = (float)(w[i] / z);
-            c->snew[i] = c->s[i] + inc;
+            c->snew[i] = prm->current_score ? inc : c->s[i] + inc;
         }
     }
 
@@ -252,13 +257,16 @@ int oracle_step(oracle_cache *c, const uint16_t *k, const uint16_t *v,
     c->snew[n] = 0.0f;
     float g_new = prm->use_gumbel ? oracle_gumbel(prm->seed, prm->hh, c->pos) : 0.0f;
 
-    /* 3. Over budget: evict the non-sink row with the smallest              */
-    /*    score + tau * gumbel, the new row included; at tau == 0 (and for    */
-    /*    PyramidKV, which carries no noise) the key is the raw score.        */
-    /*    [KF] keyformer_update step 3 and FUSED METAL KERNEL; [PK] How it    */
-    /*    works step 3 (sinks count as +inf).  Readings: exactly one eviction */
-    /*    once the token makes n + 1 > budget; the key is one fused           */
-    /*    multiply-add in float; ties go to the lowest index.                 */
+    /* 3. Over budget: evict the non-protected row with the smallest         */
+    /*    score + tau * gumbel; at tau == 0 (and for PyramidKV, which carries */
+    /*    no noise) the key is the raw score.  Protected: the n_sink leading  */
+    /*    rows and the `recent` trailing rows of the n + 1 rows after the     */
+    /*    append, so the new row is a candidate only when recent == 0.        */
+    /*    [KF] keyformer_update step 3, KeyformerState (recent) and FUSED     */
+    /*    METAL KERNEL; [PK] How it works step 3 (sinks count as +inf).       */
+    /*    Readings: exactly one eviction once the token makes n + 1 > budget; */
+    /*    the key is one fused multiply-add in float; ties go to the lowest   */
+    /*    index.                                                              */
     int32_t e = -1;
     double gap = INFINITY;
     if (n + 1 > prm->budget) {
@@ -266,7 +274,8 @@ int oracle_step(oracle_cache *c, const uint16_t *k, const uint16_t *v,
                                                  prm->anneal_steps, c->pos) : 0.0f;
         float best = INFINITY, second = INFINITY;
         double best_mag = 0.0, second_mag = 0.0;
-        for (int32_t i = prm->n_sink; i <= n; ++i) {
+        const int32_t last = n - prm->recent;     /* last candidate row */
+        for (int32_t i = prm->n_sink; i <= last; ++i) {
             float gi = (i == n) ? g_new : c->g[i];
             float key = prm->use_gumbel ? fmaf(tau, gi, c->snew[i]) : c->snew[i];
             double mag = fabs((double)c->snew[i]) +

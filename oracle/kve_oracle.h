@@ -14,7 +14,8 @@
  *         (RoPE position tracking), THE HONESTY CRUX.
  *   [PK]  "PyramidKV -- Layer-Adaptive Budget Attention-Mass Eviction" --
  *         sections "The budget schedule", "How it works", "Relationship to
- *         H2O", "Evidence".
+ *         H2O", "Evidence", and the table of eviction axes (TOVA-adapted:
+ *         current-step attention weight as the score signal).
  * Where those pages leave a step open, the reading taken is stated next to
  * the function that implements it.
  */
@@ -55,6 +56,9 @@ typedef struct oracle_params {
     double   rope_base;
     uint64_t seed;          /* base seed of the Gumbel stream                 */
     int64_t  hh;            /* row of this cache within its layer's B*H set   */
+    int32_t  recent;        /* trailing rows never evicted (0 = off)          */
+    int32_t  current_score; /* 1 = TOVA-adapted: a row's score is this step's
+                               proxy attention weight alone (not accumulated) */
 } oracle_params;
 
 /* SplitMix64 output function applied to state value z (state advanced by

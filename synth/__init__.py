@@ -49,7 +49,7 @@ class Workload:
     decode: int
     budget: int                      # uniform budget, or the average for a pyramid
     n_sink: int
-    kind: str                        # "keyformer" or "pyramid"
+    kind: str                        # "keyformer", "pyramid" or "tova"
     tau_init: float = 0.0
     tau_end: float = 0.0
     anneal_steps: int = 0
@@ -57,6 +57,7 @@ class Workload:
     late_riser: bool = False
     rope_base: float = 10000.0
     gumbel_seed: int = 0
+    recent: int = 0                  # trailing protected window (0 = off)
     extra: dict = field(default_factory=dict)
 
     @property

@@ -16,7 +16,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 MUTANTS = {
     "no_softmax_scale": ("x[i] = acc / scale;", "x[i] = acc;"),
-    "replace_not_accumulate": ("c->snew[i] = c->s[i] + inc;", "c->snew[i] = inc;"),
+    "replace_not_accumulate": ("c->snew[i] = prm->current_score ? inc : c->s[i] + inc;",
+                               "c->snew[i] = inc;"),
+    "tova_accumulates": ("c->snew[i] = prm->current_score ? inc : c->s[i] + inc;",
+                         "c->snew[i] = c->s[i] + inc;"),
     "rotation_sign": ("float y1 = a - b;", "float y1 = a + b;"),
     "rotation_direction": ("float s = (float)sin(theta);", "float s = (float)sin(-theta);"),
     "frequency_index": ("-(2.0 * (double)j) / (double)d", "-(2.0 * (double)(j + 1)) / (double)d"),
@@ -24,10 +27,15 @@ MUTANTS = {
                    "int64_t delta = (int64_t)c->p[src] - (int64_t)j;"),
     "new_row_not_remapped": ("c->p[n] = c->next_pos;", "c->p[n] = n;"),
     "tie_to_highest": ("if (e < 0 || key < best) {", "if (e < 0 || key <= best) {"),
-    "sinks_evictable": ("for (int32_t i = prm->n_sink; i <= n; ++i) {",
-                        "for (int32_t i = 0; i <= n; ++i) {"),
-    "new_row_protected": ("for (int32_t i = prm->n_sink; i <= n; ++i) {",
-                          "for (int32_t i = prm->n_sink; i < n; ++i) {"),
+    "sinks_evictable": ("for (int32_t i = prm->n_sink; i <= last; ++i) {",
+                        "for (int32_t i = 0; i <= last; ++i) {"),
+    "new_row_protected": ("const int32_t last = n - prm->recent;",
+                          "const int32_t last = n - prm->recent - 1;"),
+    "recent_ignored": ("const int32_t last = n - prm->recent;", "const int32_t last = n;"),
+    "recent_window_one_short": ("const int32_t last = n - prm->recent;",
+                                "const int32_t last = n - prm->recent + (prm->recent > 0);"),
+    "recent_not_validated": ("prm->budget <= prm->n_sink + prm->recent ||",
+                             "prm->budget <= prm->n_sink ||"),
     "evict_one_early": ("if (n + 1 > prm->budget) {", "if (n + 1 >= prm->budget) {"),
     "tau_pos_after_increment": ("prm->anneal_steps, c->pos) : 0.0f;",
                                 "prm->anneal_steps, c->pos + 1) : 0.0f;"),

@@ -372,11 +372,18 @@ def test_block_boundary_independence_and_determinism():
 # brute force on tiny caches: an independent formulation of the same semantics
 # ---------------------------------------------------------------------------
 
-def _brute_force(ks_bits, budget, n_sink, tau_fn, gumbel_fn, base=10000.0):
+def _brute_force(ks_bits, budget, n_sink, tau_fn, gumbel_fn, base=10000.0, recent=0,
+                 current=False):
     """Kept tokens as a list; each kept token's stored key is its incoming key
     rotated (complex form, float64) from its absolute position to its index in
     the list; each step's mass comes from torch.softmax (float64) and is kept as
-    a per-token history whose sum is the score; the eviction is numpy.argmin."""
+    a per-token history whose sum is the score (its last entry, for the
+    current-step score of TOVA); the eviction is numpy.argmin over the tokens
+    after the first n_sink and before the last `recent`."""
+    def score(tok):
+        h = hist[tok]
+        return (h[-1] if h else 0.0) if current else sum(h)
+
     D = ks_bits.shape[1]
     kin = ks_bits.view(np.float16).astype(np.float64)
     kept, hist, evicted = [], {}, []
@@ -390,13 +397,14 @@ def _brute_force(ks_bits, budget, n_sink, tau_fn, gumbel_fn, base=10000.0):
         hist[t] = []
         if len(kept) > budget:
             tau = tau_fn(t)
-            vals = [sum(hist[tok]) + tau * gumbel_fn(tok) for tok in kept[n_sink:]]
+            vals = [score(tok) + tau * gumbel_fn(tok)
+                    for tok in kept[n_sink:len(kept) - recent]]
             e = n_sink + int(np.argmin(vals))
             evicted.append(e)
             kept.pop(e)
         else:
             evicted.append(-1)
-    scores = np.array([sum(hist[tok]) for tok in kept])
+    scores = np.array([score(tok) for tok in kept])
     keys = np.stack([_rope_complex(kin[tok], idx - tok, base) for idx, tok in enumerate(kept)])
     return kept, np.array(evicted), scores, keys
 
@@ -425,3 +433,131 @@ def test_brute_force_tiny_caches(D, tau):
             got = c.k[:c.n]
             want = keys.astype(np.float16).view(np.uint16)
             assert _pair_ulps(got, want).max() <= 8.0
+
+
+# ---------------------------------------------------------------------------
+# the recent window ([KF] KeyformerState, init_keyformer_state: trailing rows
+# protected, an extension off by default) and TOVA-adapted scoring ([PK] table
+# of eviction axes: the current step's attention weight is the score)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("D", [4, 8])
+@pytest.mark.parametrize("tau,current", [((0.0, 0.0, 0), False), ((1.0, 2.0, 16), False),
+                                         ((0.0, 0.0, 0), True), ((0.5, 1.5, 8), True)])
+@pytest.mark.parametrize("recent", [1, 3])
+def test_brute_force_recent_and_tova(D, tau, current, recent):
+    T = 40
+    for n_sink in range(0, 3):
+        for budget in range(n_sink + recent + 1, n_sink + recent + 6):
+            kind = "tova" if current else "keyformer"
+            w = synth.Workload(f"bfr{D}", 1, 1, 1, D, 40, 0, budget, n_sink, kind,
+                               tau[0], tau[1], tau[2], recent=recent)
+            hh = 5 * n_sink + budget
+            prm = Params(budget, n_sink, True, *tau, seed=0, hh=hh, recent=recent,
+                         current_score=current)
+            tr = guarded_trajectory(w, 0, hh, budget, T, min_margin_rel=0.02,
+                                    max_attempts=200, params=prm)
+            c = tr.cache
+            tau_fn = (lambda t: tau[0] + min(t, tau[2]) * (tau[1] - tau[0]) / tau[2]) if tau[2] \
+                else (lambda t: tau[0])
+            kept, ev, sc, keys = _brute_force(tr.ks, budget, n_sink, tau_fn,
+                                              lambda tok: float(oracle.gumbel(0, hh, tok)),
+                                              recent=recent, current=current)
+            assert list(c.tid[:c.n]) == kept
+            assert np.array_equal(tr.evicted, ev)
+            assert np.array_equal(c.v[:c.n], tr.vs[kept])
+            assert np.allclose(c.s[:c.n], sc, rtol=5e-3, atol=1e-6)
+            assert _pair_ulps(c.k[:c.n], keys.astype(np.float16).view(np.uint16)).max() <= 8.0
+
+
+@pytest.mark.parametrize("recent,kind", [(1, "kf"), (7, "kf"), (1, "h2o"), (20, "h2o"),
+                                         (5, "tova")])
+def test_recent_window_always_kept(recent, kind):
+    """The last `recent` tokens and the sinks are present after every step, the
+    newest token is never the one evicted, and positions stay contiguous."""
+    budget, n_sink, T = 32, 4, 200
+    tau = (1.0, 2.0, 64) if kind == "kf" else (0.0, 0.0, 0)
+    w = synth.Workload("rw", 1, 1, 1, 64, T, 0, budget, n_sink, "keyformer", *tau)
+    c = OracleCache(64, budget + 1)
+    prm = Params(budget, n_sink, kind == "kf", *tau, seed=4, hh=1, recent=recent,
+                 current_score=kind == "tova")
+    ks, vs = synth.token_kv(w, 0, 1, np.arange(T))
+    for t in range(T):
+        n_before = c.n
+        rc, e, _ = c.step(ks[t], vs[t], prm)
+        assert rc == 0
+        tid = list(c.tid[:c.n])
+        assert tid[-min(recent, t + 1):] == list(range(max(0, t + 1 - recent), t + 1))
+        assert tid[:min(n_sink, c.n)] == list(range(min(n_sink, c.n)))
+        if e >= 0:
+            assert n_sink <= e <= n_before - recent         # newest never evicted
+            assert np.array_equal(c.p[:c.n], np.arange(c.n))
+
+
+def test_recent_zero_is_the_plain_step():
+    """recent = 0 reproduces the step without the window, bit for bit."""
+    w = synth.TINY_ANNEALED
+    ks, vs = synth.token_kv(w, 0, 3, np.arange(150))
+    a, b = OracleCache(64, 33), OracleCache(64, 33)
+    ea = a.run(ks, vs, Params(32, 4, True, 1.0, 2.0, 64, seed=0, hh=3))
+    eb = b.run(ks, vs, Params(32, 4, True, 1.0, 2.0, 64, seed=0, hh=3, recent=0))
+    assert np.array_equal(ea, eb)
+    for name in ("k", "v", "s", "g", "p", "tid"):
+        assert np.array_equal(getattr(a, name)[:a.n], getattr(b, name)[:b.n])
+
+
+def test_tova_scores_are_the_current_softmax():
+    """One TOVA step from two random states that differ only in their scores:
+    both give the survivors torch.softmax (float64) of this step's logits,
+    rounded to float32, whatever the scores were before; the new row has 0."""
+    rng = np.random.default_rng(9)
+    D, budget, ns, recent = 64, 40, 4, 3
+    K = rng.standard_normal((budget, D)).astype(np.float16)
+    k = rng.standard_normal(D).astype(np.float16)
+    v = rng.standard_normal(D).astype(np.float16)
+    logits = torch.from_numpy(K.astype(np.float64) @ k.astype(np.float64) / math.sqrt(D))
+    p = torch.softmax(logits, dim=0).numpy().astype(np.float32)
+    outs = []
+    for seed in (1, 2):
+        c = OracleCache(D, budget + 1)
+        c.k[:budget] = K.view(np.uint16)
+        c.s[:budget] = np.random.default_rng(seed).uniform(0, 9, budget).astype(np.float32)
+        c.p[:budget] = np.arange(budget)
+        c.tid[:budget] = np.arange(budget)
+        c.set_counters(budget, 500, 500)
+        rc, e, _ = c.step(k.view(np.uint16), v.view(np.uint16),
+                          Params(budget, ns, False, recent=recent, current_score=True))
+        assert rc == 0
+        assert e == ns + int(np.argmin(p[ns:budget + 1 - recent]))
+        want = np.concatenate([p[:e], p[e + 1:], [0.0]]).astype(np.float32)
+        assert np.allclose(c.s[:c.n], want, rtol=2.5e-7, atol=0)
+        assert c.s[c.n - 1] == 0.0
+        outs.append((e, c.s[:c.n].copy()))
+    assert outs[0][0] == outs[1][0] and np.array_equal(outs[0][1], outs[1][1])
+
+
+def test_tova_without_window_evicts_the_newest():
+    """Without a recent window the new row (score 0) is TOVA's minimum on every
+    step, as for H2O: the first `budget` tokens are kept."""
+    w = _tiny(d=64, budget=20, n_sink=4)
+    ks, vs = synth.token_kv(w, 0, 0, np.arange(90))
+    c = OracleCache(64, 21)
+    ev = c.run(ks, vs, Params(20, 4, False, current_score=True))
+    assert list(c.tid[:c.n]) == list(range(20))
+    assert np.all(ev[20:] == 20) and np.all(ev[:20] == -1)
+
+
+@pytest.mark.parametrize("budget,n_sink,recent,ok", [(10, 4, 5, True), (10, 4, 6, False),
+                                                     (10, 0, 9, True), (10, 0, 10, False),
+                                                     (10, 4, -1, False)])
+def test_recent_validation(budget, n_sink, recent, ok):
+    """[KF] init_keyformer_state: sinks plus the recent window must leave room
+    to evict within the budget."""
+    c = OracleCache(8, budget + 1)
+    z = np.zeros(8, dtype=np.uint16)
+    prm = Params(budget, n_sink, False, recent=recent)
+    if ok:
+        assert c.step(z, z, prm)[0] == 0
+    else:
+        with pytest.raises(ValueError):
+            c.step(z, z, prm)

@@ -50,6 +50,10 @@ def parse():
                     help="S > 1: each launch steps S tokens (*_step_tokens per layer, or "
                          "*_step_layers_tokens with --batched); S must divide --steps and "
                          "--warmup")
+    ap.add_argument("--recent", type=int, default=0,
+                    help="protect the last R rows from eviction (kve_step)")
+    ap.add_argument("--tova", action="store_true",
+                    help="TOVA-adapted scoring (current-step weight; kve_step)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the CPU oracle baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -113,7 +117,9 @@ def copy_calibration():
 
 
 def step_bytes(kind: str, n: int, d: int, m):
-    """Algorithmic bytes of one cache-step (m may be an array)."""
+    """Algorithmic bytes of one cache-step (m may be an array).  TOVA-adapted
+    ("tova") moves the PyramidKV bytes minus the 4n-byte read of the old
+    scores; the caller subtracts that."""
     if kind == "keyformer":
         return 2 * n * d + 12 * n + 8 * d + 12 + m * (8 * d + 24)
     return 2 * n * d + 8 * n + 8 * d + 8 + m * (8 * d + 16)
@@ -167,6 +173,7 @@ def main():
               "(the eviction step shards with no exchange; run one process per GPU).",
               file=sys.stderr)
         sys.exit(2)
+    import dataclasses
     import numpy as np
     import torch
     import synth
@@ -175,66 +182,114 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = synth.WORKLOADS[args.config]
+    if args.tova or args.recent:
+        w = dataclasses.replace(w, kind="tova" if args.tova else w.kind, recent=args.recent,
+                                name=w.name + ("-tova" if args.tova else "") +
+                                (f"-recent{args.recent}" if args.recent else ""))
     kf = w.kind == "keyformer"
     budgets = w.budgets(kve.pyramid_budgets)
     L, bh, d = w.layers, w.bh, w.d
     layers = [kve.Layer.empty(bh, b + 1, d, dev, gumbel=kf) for b in budgets]
     cls = [x.c_struct() for x in layers]
-    ctrs = [kve.Counters(0, 0, 0) for _ in range(L)]
     gen = torch.Generator(device=dev)
     gen.manual_seed(2024)
-
-    def step_layer(l, k, v, ev=None):
-        if kf:
-            kve.keyformer_step(layers[l], k, v, ctrs[l], budgets[l], w.n_sink, w.tau_init,
-                               w.tau_end, w.anneal_steps, w.rope_base, w.gumbel_seed, ev,
-                               c_layer=cls[l])
-        else:
-            kve.pyramid_step(layers[l], k, v, ctrs[l], budgets[l], w.n_sink, w.rope_base, ev,
-                             c_layer=cls[l])
-
-    # ---- reach the steady state (untimed) ------------------------------------
-    t_fill = time.time()
     pos0 = w.prompt
-    if args.fill == "synthetic":
-        for l in range(L):
-            x = layers[l]
-            synth.bulk_state_torch(x.k, x.v, x.scores, x.gumbel, x.positions, budgets[l], w, gen)
-            ctrs[l] = kve.Counters(budgets[l], pos0, pos0)
-    else:
-        # the prompt, token by token, through the same entry point as the timed steps
-        chunk = 64
-        fill_batch = kve.LayerBatch(layers, budgets, ctrs) if args.batched else None
-        for t0 in range(0, w.prompt, chunk):
-            cnt = min(chunk, w.prompt - t0)
-            ins_k = torch.empty((cnt, L, bh, d), dtype=torch.float16, device=dev)
-            ins_v = torch.empty_like(ins_k)
-            for l in range(L):
-                k, v = synth.bulk_kv_torch(w, t0, cnt, bh, gen, dev)
-                ins_k[:, l], ins_v[:, l] = k, v
-            for t in range(cnt):
-                if fill_batch is not None:
-                    if kf:
-                        kve.keyformer_step_layers(fill_batch, ins_k[t], ins_v[t], w.n_sink,
-                                                  w.tau_init, w.tau_end, w.anneal_steps,
-                                                  w.rope_base, w.gumbel_seed)
-                    else:
-                        kve.pyramid_step_layers(fill_batch, ins_k[t], ins_v[t], w.n_sink,
-                                                w.rope_base)
-                else:
-                    for l in range(L):
-                        step_layer(l, ins_k[t, l], ins_v[t, l])
-        if fill_batch is not None:
-            ctrs = [fill_batch.ctrs[l] for l in range(L)]
-    torch.cuda.synchronize()
-    t_fill = time.time() - t_fill
-
-    # ---- inputs for warmup + timed steps, resident in HBM ----------------------
     TPC = args.tokens_per_call
     if TPC < 1 or TPC > 128 or args.steps % TPC or args.warmup % TPC:
         print("--tokens-per-call must be 1..128 and divide --steps and --warmup",
               file=sys.stderr)
         sys.exit(2)
+
+    # ---- the calls: named entry points, or kve_step for the extensions --------
+    use_policy = w.kind == "tova" or w.recent > 0
+    pol = (kve.policy(w.kind, w.n_sink, w.recent, w.tau_init, w.tau_end, w.anneal_steps,
+                      w.rope_base, w.gumbel_seed) if use_policy else None)
+    name = "keyformer" if kf else "pyramid"
+    if args.batched:
+        batch = kve.LayerBatch(layers, budgets)
+        singles = None
+        entry = ("kve_step" if use_policy else
+                 f"{name}_step_layers" + ("_tokens" if TPC > 1 else ""))
+    else:
+        batch = None
+        singles = [kve.LayerBatch([layers[l]], [budgets[l]]) for l in range(L)]
+        entry = "kve_step" if use_policy else f"{name}_step" + ("_tokens" if TPC > 1 else "")
+
+    def ctr(l):
+        return batch.ctrs[l] if batch is not None else singles[l].ctrs[0]
+
+    def call(nk, nv, s0, S, ev_out=None):
+        """Tokens s0 .. s0+S-1 of nk/nv ([L, tokens, bh, d]) through every layer;
+        ev_out: None or [L, S, bh]."""
+        if batch is not None:
+            ks, vs = nk[:, s0:s0 + S], nv[:, s0:s0 + S]
+            if use_policy:
+                kve.step(batch, ks, vs, pol, ev_out, n_tokens=S)
+            elif S > 1 and kf:
+                kve.keyformer_step_layers_tokens(batch, ks, vs, w.n_sink, w.tau_init,
+                                                 w.tau_end, w.anneal_steps, w.rope_base,
+                                                 w.gumbel_seed, ev_out, n_tokens=S)
+            elif S > 1:
+                kve.pyramid_step_layers_tokens(batch, ks, vs, w.n_sink, w.rope_base, ev_out,
+                                               n_tokens=S)
+            elif kf:
+                kve.keyformer_step_layers(batch, ks[:, 0], vs[:, 0], w.n_sink, w.tau_init,
+                                          w.tau_end, w.anneal_steps, w.rope_base, w.gumbel_seed,
+                                          ev_out[:, 0] if ev_out is not None else None)
+            else:
+                kve.pyramid_step_layers(batch, ks[:, 0], vs[:, 0], w.n_sink, w.rope_base,
+                                        ev_out[:, 0] if ev_out is not None else None)
+            return
+        for l in range(L):
+            ks, vs = nk[l, s0:s0 + S], nv[l, s0:s0 + S]
+            e_l = ev_out[l] if ev_out is not None else None
+            c = singles[l].ctrs[0]
+            if use_policy:
+                kve.step(singles[l], ks[None], vs[None], pol,
+                         e_l[None] if e_l is not None else None, n_tokens=S)
+            elif S > 1 and kf:
+                kve.keyformer_step_tokens(layers[l], ks, vs, c, budgets[l], w.n_sink,
+                                          w.tau_init, w.tau_end, w.anneal_steps, w.rope_base,
+                                          w.gumbel_seed, e_l, c_layer=cls[l])
+            elif S > 1:
+                kve.pyramid_step_tokens(layers[l], ks, vs, c, budgets[l], w.n_sink, w.rope_base,
+                                        e_l, c_layer=cls[l])
+            elif kf:
+                kve.keyformer_step(layers[l], ks[0], vs[0], c, budgets[l], w.n_sink, w.tau_init,
+                                   w.tau_end, w.anneal_steps, w.rope_base, w.gumbel_seed,
+                                   e_l[0] if e_l is not None else None, c_layer=cls[l])
+            else:
+                kve.pyramid_step(layers[l], ks[0], vs[0], c, budgets[l], w.n_sink, w.rope_base,
+                                 e_l[0] if e_l is not None else None, c_layer=cls[l])
+
+    def set_counters(l, c):
+        if batch is not None:
+            batch.ctrs[l] = c
+        else:
+            singles[l].ctrs[0] = c
+
+    # ---- reach the steady state (untimed) ------------------------------------
+    t_fill = time.time()
+    if args.fill == "synthetic":
+        for l in range(L):
+            x = layers[l]
+            synth.bulk_state_torch(x.k, x.v, x.scores, x.gumbel, x.positions, budgets[l], w, gen)
+            set_counters(l, kve.Counters(budgets[l], pos0, pos0))
+    else:
+        # the prompt through the same calls as the timed steps
+        chunk = 64 * TPC if TPC > 1 else 64
+        for t0 in range(0, w.prompt, chunk):
+            cnt = min(chunk, w.prompt - t0)
+            ins_k = torch.empty((L, cnt, bh, d), dtype=torch.float16, device=dev)
+            ins_v = torch.empty_like(ins_k)
+            for l in range(L):
+                ins_k[l], ins_v[l] = synth.bulk_kv_torch(w, t0, cnt, bh, gen, dev)
+            for s0 in range(0, cnt, TPC):
+                call(ins_k, ins_v, s0, min(TPC, cnt - s0))
+    torch.cuda.synchronize()
+    t_fill = time.time() - t_fill
+
+    # ---- inputs for warmup + timed steps, resident in HBM ----------------------
     S = args.warmup + args.steps
     # [L, S, bh, d]: each layer's tokens contiguous, so that any run of TPC
     # tokens of a layer is one contiguous [TPC, bh, d] block
@@ -246,61 +301,18 @@ def main():
     n_prev = np.zeros((args.steps, L), dtype=np.int64)
     torch.cuda.synchronize()
 
-    batch = kve.LayerBatch(layers, budgets, ctrs) if args.batched else None
-    counters = (lambda l: batch.ctrs[l]) if batch is not None else (lambda l: ctrs[l])
-    name = "keyformer" if kf else "pyramid"
-    if batch is not None:
-        entry = f"{name}_step_layers" + ("_tokens" if TPC > 1 else "")
-    else:
-        entry = f"{name}_step" + ("_tokens" if TPC > 1 else "")
-
-    def call(s0, ev_out=None):
-        """Tokens s0 .. s0+TPC-1 (input index) through every layer."""
-        if batch is not None:
-            if TPC > 1:
-                ks, vs = nk[:, s0:s0 + TPC], nv[:, s0:s0 + TPC]
-                if kf:
-                    kve.keyformer_step_layers_tokens(batch, ks, vs, w.n_sink, w.tau_init,
-                                                     w.tau_end, w.anneal_steps, w.rope_base,
-                                                     w.gumbel_seed, ev_out, n_tokens=TPC)
-                else:
-                    kve.pyramid_step_layers_tokens(batch, ks, vs, w.n_sink, w.rope_base, ev_out,
-                                                   n_tokens=TPC)
-            elif kf:
-                kve.keyformer_step_layers(batch, nk[:, s0], nv[:, s0], w.n_sink, w.tau_init,
-                                          w.tau_end, w.anneal_steps, w.rope_base, w.gumbel_seed,
-                                          ev_out[:, 0] if ev_out is not None else None)
-            else:
-                kve.pyramid_step_layers(batch, nk[:, s0], nv[:, s0], w.n_sink, w.rope_base,
-                                        ev_out[:, 0] if ev_out is not None else None)
-            return
-        for l in range(L):
-            e_l = ev_out[l] if ev_out is not None else None
-            if TPC > 1:
-                if kf:
-                    kve.keyformer_step_tokens(layers[l], nk[l, s0:s0 + TPC], nv[l, s0:s0 + TPC],
-                                              ctrs[l], budgets[l], w.n_sink, w.tau_init,
-                                              w.tau_end, w.anneal_steps, w.rope_base,
-                                              w.gumbel_seed, e_l, c_layer=cls[l])
-                else:
-                    kve.pyramid_step_tokens(layers[l], nk[l, s0:s0 + TPC], nv[l, s0:s0 + TPC],
-                                            ctrs[l], budgets[l], w.n_sink, w.rope_base, e_l,
-                                            c_layer=cls[l])
-            else:
-                step_layer(l, nk[l, s0], nv[l, s0], e_l[0] if e_l is not None else None)
-
     for s0 in range(0, args.warmup, TPC):
-        call(s0)
+        call(nk, nv, s0, TPC)
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
     for s0 in range(0, args.steps, TPC):
         for l in range(L):
-            nk0 = counters(l).n_kept
+            nk0 = ctr(l).n_kept
             for i in range(TPC):
                 n_prev[s0 + i, l] = min(nk0 + i, budgets[l])
-        call(args.warmup + s0, ev[:, s0:s0 + TPC])
+        call(nk, nv, args.warmup + s0, TPC, ev[:, s0:s0 + TPC])
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
@@ -314,6 +326,8 @@ def main():
             e = evn[s, l]
             m = np.where((e >= 0) & (e < n), n - e, 0).astype(np.int64)
             total_bytes += int(step_bytes(w.kind, n, d, m).sum())
+            if w.kind == "tova":                # the old scores are not read
+                total_bytes -= 4 * n * bh
     launches = (args.steps // TPC) * (1 if batch is not None else L)
     sec = ms / 1e3
     updates = bh * L * args.steps
@@ -346,6 +360,8 @@ def main():
                         f"kv_heads={w.kv_heads} D={d} {w.kind} budget="
                         f"{'pyramid avg ' if w.kind == 'pyramid' else ''}{w.budget} "
                         f"n_sink={w.n_sink}",
+            "policy": {"score": "current (TOVA)" if w.kind == "tova" else "cumulative",
+                       "gumbel": kf, "recent": w.recent, "n_sink": w.n_sink},
             "kv_storage": "f16", "bh_per_launch": bh, "layers": L,
             "budgets": [budgets[0], budgets[-1]], "steady_state_fill": args.fill,
             "fill_seconds": round(t_fill, 1), "mean_rows_moved_per_cache_step": mean_m,

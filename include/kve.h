@@ -229,6 +229,58 @@ int pyramid_step_layers_tokens(int32_t n_layers, int32_t n_tokens, const kve_lay
                                double rope_base, int32_t *const *evicted, void *stream);
 
 /*
+ * kve_step -- the general form of every call above, with the two extensions
+ * the pages describe beyond the plain step:
+ *   - a trailing protected window (Keyformer page, KeyformerState `recent`
+ *     and init_keyformer_state: an extension, off by default): the last
+ *     `recent` rows of the budget + 1 rows present after the append are
+ *     never evicted, so the candidates are rows n_sink .. budget - recent and
+ *     the incoming row is one only when recent == 0;
+ *   - TOVA-adapted scoring (PyramidKV page, table of eviction axes: the
+ *     current step's attention weight is the score signal): with
+ *     KVE_SCORE_CURRENT a stored row's score becomes this step's proxy
+ *     weight softmax(K.k/sqrt(d)) instead of accumulating it; the incoming
+ *     row still enters with 0, so without a window TOVA always evicts it.
+ * keyformer_step(...) is kve_step with n_layers = n_tokens = 1 and the policy
+ * {n_sink, 0, KVE_SCORE_CUMULATIVE, 1, tau_init, tau_end, anneal_steps,
+ * rope_base, seed}; pyramid_step the same with gumbel = 0.
+ */
+#define KVE_SCORE_CUMULATIVE 0   /* H2O / Keyformer / PyramidKV: score += weight */
+#define KVE_SCORE_CURRENT    1   /* TOVA-adapted: score = weight                 */
+
+typedef struct kve_policy {
+    int32_t  n_sink;        /* leading rows never evicted, >= 0                       */
+    int32_t  recent;        /* trailing rows never evicted, >= 0 (0 = off); every
+                               layer's budget must exceed n_sink + recent              */
+    int32_t  score;         /* KVE_SCORE_CUMULATIVE or KVE_SCORE_CURRENT              */
+    int32_t  gumbel;        /* 1: Keyformer noise tau * g in the eviction key (every
+                               layer needs its gumbel tensor); 0: no noise, and the
+                               three fields below and `seed` are ignored             */
+    double   tau_init;      /* as keyformer_step                                       */
+    double   tau_end;
+    int32_t  anneal_steps;
+    int32_t  reserved;      /* unused                                                  */
+    double   rope_base;     /* > 0                                                     */
+    uint64_t seed;          /* Gumbel base seed, as keyformer_step                     */
+} kve_policy;
+
+/*
+ *   n_layers   1 .. 128;  n_tokens  1 .. 128
+ *   layers, new_k, new_v, ctrs, budgets, evicted, stream
+ *              as keyformer_step_layers_tokens (with n_tokens == 1 the rows of
+ *              token 0 are simply [bh_l][d])
+ *   policy     HOST pointer, read during the call only
+ * Returns as keyformer_step; KVE_EINVAL also for a NULL policy, an unknown
+ * score rule, gumbel not 0 or 1, recent < 0 or budget <= n_sink + recent.
+ * One layer and one token launch directly; otherwise the call uses the
+ * descriptor ring of the batched calls (not for use under stream capture).
+ */
+int kve_step(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
+             const void *const *new_k, const void *const *new_v, kve_counters *ctrs,
+             const int32_t *budgets, const kve_policy *policy, int32_t *const *evicted,
+             void *stream);
+
+/*
  * pyramid_budgets -- per-layer budgets ("The budget schedule"): a linear taper
  * from the largest budget at layer 0 to the smallest at the last layer, mean
  * avg_budget, every entry at least n_sink + 1.  The smallest is

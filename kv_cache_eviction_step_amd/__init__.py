@@ -99,6 +99,22 @@ _lib.pyramid_step_layers_tokens.argtypes = [
     ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(KveLayer), ctypes.c_void_p, ctypes.c_void_p,
     ctypes.POINTER(Counters), ctypes.c_void_p, ctypes.c_int32, ctypes.c_double, ctypes.c_void_p,
     ctypes.c_void_p]
+class Policy(ctypes.Structure):
+    """kve_policy: the eviction rule of kve_step (see policy())."""
+    _fields_ = [("n_sink", ctypes.c_int32), ("recent", ctypes.c_int32),
+                ("score", ctypes.c_int32), ("gumbel", ctypes.c_int32),
+                ("tau_init", ctypes.c_double), ("tau_end", ctypes.c_double),
+                ("anneal_steps", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("rope_base", ctypes.c_double), ("seed", ctypes.c_uint64)]
+
+
+SCORE_CUMULATIVE, SCORE_CURRENT = 0, 1
+
+_lib.kve_step.restype = ctypes.c_int
+_lib.kve_step.argtypes = [
+    ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(KveLayer), ctypes.c_void_p, ctypes.c_void_p,
+    ctypes.POINTER(Counters), ctypes.c_void_p, ctypes.POINTER(Policy), ctypes.c_void_p,
+    ctypes.c_void_p]
 _lib.pyramid_budgets.restype = ctypes.c_int
 _lib.pyramid_budgets.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                  ctypes.c_double, ctypes.c_void_p]
@@ -107,7 +123,7 @@ _lib.kve_strerror.argtypes = [ctypes.c_int]
 
 EXPORTED = ("keyformer_step", "pyramid_step", "keyformer_step_layers", "pyramid_step_layers",
             "keyformer_step_tokens", "pyramid_step_tokens", "keyformer_step_layers_tokens",
-            "pyramid_step_layers_tokens", "pyramid_budgets", "kve_strerror")
+            "pyramid_step_layers_tokens", "kve_step", "pyramid_budgets", "kve_strerror")
 
 
 def lib() -> ctypes.CDLL:
@@ -419,6 +435,36 @@ def pyramid_step_layers_tokens(batch: LayerBatch, new_k, new_v, n_sink: int, rop
                                          batch.ctrs, batch.budgets, n_sink, rope_base, pe,
                                          _stream_ptr(stream, batch.layers[0]))
     _check(rc, "pyramid_step_layers_tokens")
+
+
+def policy(kind: str, n_sink: int, recent: int = 0, tau_init: float = 0.0, tau_end: float = 0.0,
+           anneal_steps: int = 0, rope_base: float = 10000.0, seed: int = 0) -> Policy:
+    """The kve_step policy of one method.
+
+    kind: "keyformer" (cumulative score + annealed Gumbel noise), "h2o" or
+    "pyramid" (cumulative score, no noise; PyramidKV differs from H2O only in
+    the per-layer budgets), "tova" (current-step score, no noise)."""
+    if kind not in ("keyformer", "h2o", "pyramid", "tova"):
+        raise ValueError(f"unknown method {kind!r}")
+    kf = kind == "keyformer"
+    return Policy(n_sink, recent, SCORE_CURRENT if kind == "tova" else SCORE_CUMULATIVE,
+                  1 if kf else 0, tau_init if kf else 0.0, tau_end if kf else 0.0,
+                  anneal_steps if kf else 0, 0, rope_base,
+                  (seed & 0xFFFFFFFFFFFFFFFF) if kf else 0)
+
+
+def step(batch: LayerBatch, new_k, new_v, pol: Policy, evicted=None, stream=None,
+         n_tokens: int | None = None) -> None:
+    """kve_step over every layer of `batch`.
+
+    n_tokens None: one token, inputs as keyformer_step_layers; n_tokens S:
+    S tokens, inputs as keyformer_step_layers_tokens."""
+    S = 1 if n_tokens is None else n_tokens
+    pe = batch._fill(new_k, new_v, evicted, n_tokens)
+    rc = _lib.kve_step(batch.n, S, batch.c_layers, batch._pk, batch._pv, batch.ctrs,
+                       batch.budgets, ctypes.byref(pol), pe,
+                       _stream_ptr(stream, batch.layers[0]))
+    _check(rc, "kve_step")
 
 
 def pyramid_budgets(n_layers: int, avg_budget: int, n_sink: int, beta: float) -> list[int]:

@@ -63,18 +63,53 @@ int check_device() {
   return s == 1 ? KVE_OK : KVE_ENODEV;
 }
 
+// Everything about a call that is not per layer: the eviction rule and the
+// noise, as the entry points receive them.
+struct Policy {
+  int32_t n_sink = 0;
+  int32_t recent = 0;          // trailing rows protected (0 = off)
+  bool current = false;        // TOVA-adapted: score = this step's weight
+  bool gumbel = false;         // Keyformer-adapted noise in the eviction key
+  double tau_init = 0.0;
+  double tau_end = 0.0;
+  int32_t anneal_steps = 0;
+  double rope_base = 10000.0;
+  uint64_t seed = 0;
+};
+
+Policy keyformer_policy(int32_t n_sink, double tau_init, double tau_end, int32_t anneal_steps,
+                        double rope_base, uint64_t seed) {
+  Policy p;
+  p.n_sink = n_sink;
+  p.gumbel = true;
+  p.tau_init = tau_init;
+  p.tau_end = tau_end;
+  p.anneal_steps = anneal_steps;
+  p.rope_base = rope_base;
+  p.seed = seed;
+  return p;
+}
+
+Policy pyramid_policy(int32_t n_sink, double rope_base) {
+  Policy p;
+  p.n_sink = n_sink;
+  p.rope_base = rope_base;
+  return p;
+}
+
 // Host-side checks shared by every entry point (init_keyformer_state's guards
 // and the layout); returns KVE_OK or KVE_EINVAL.
 int check_layer(const kve_layer *L, const void *new_k, const void *new_v,
-                const kve_counters *ctr, int32_t budget, int32_t n_sink, bool gumbel) {
+                const kve_counters *ctr, int32_t budget, const Policy &p) {
   if (!L || !ctr || !new_k || !new_v) return KVE_EINVAL;
   if (!L->k || !L->v || !L->scores || !L->positions) return KVE_EINVAL;
-  if (gumbel && !L->gumbel) return KVE_EINVAL;
+  if (p.gumbel && !L->gumbel) return KVE_EINVAL;
   if (!aligned16(L->k) || !aligned16(L->v) || !aligned16(new_k) || !aligned16(new_v))
     return KVE_EINVAL;
   if (L->d != 64 && L->d != 128) return KVE_EINVAL;
   if (L->bh < 1 || L->hh_base < 0 || (int64_t)L->hh_base + L->bh > INT32_MAX) return KVE_EINVAL;
-  if (n_sink < 0 || budget <= n_sink || budget > kMaxBudget) return KVE_EINVAL;
+  // the protected rows (sinks and the recent window) must leave room to evict
+  if ((int64_t)budget <= (int64_t)p.n_sink + p.recent || budget > kMaxBudget) return KVE_EINVAL;
   if (L->cap < budget + 1) return KVE_EINVAL;
   const int32_t n = ctr->n_kept;
   if (n < 0 || n > budget) return KVE_EINVAL;
@@ -85,11 +120,12 @@ int check_layer(const kve_layer *L, const void *new_k, const void *new_v,
   return KVE_OK;
 }
 
-int check_shared(double tau_init, double tau_end, int32_t anneal_steps, double rope_base) {
-  if (!(tau_init >= 0.0) || !(tau_end >= 0.0) || !std::isfinite(tau_init) ||
-      !std::isfinite(tau_end) || anneal_steps < 0)
+int check_policy(const Policy &p) {
+  if (p.n_sink < 0 || p.recent < 0) return KVE_EINVAL;
+  if (!(p.tau_init >= 0.0) || !(p.tau_end >= 0.0) || !std::isfinite(p.tau_init) ||
+      !std::isfinite(p.tau_end) || p.anneal_steps < 0)
     return KVE_EINVAL;
-  if (!(rope_base > 0.0) || !std::isfinite(rope_base)) return KVE_EINVAL;
+  if (!(p.rope_base > 0.0) || !std::isfinite(p.rope_base)) return KVE_EINVAL;
   return KVE_OK;
 }
 
@@ -115,18 +151,19 @@ kve::LayerArgs layer_args(const kve_layer *L, const void *new_k, const void *new
   return a;
 }
 
-kve::SharedArgs shared_args(int d, int32_t n_sink, double tau_init, double tau_end,
-                            int32_t anneal_steps, double rope_base, uint64_t seed, bool gumbel) {
+kve::SharedArgs shared_args(int d, const Policy &p) {
   kve::SharedArgs sa;
   std::memset(&sa, 0, sizeof(sa));
-  sa.n_sink = n_sink;
-  sa.anneal_steps = anneal_steps;
-  sa.tau_init = gumbel ? tau_init : 0.0;
-  sa.tau_end = gumbel ? tau_end : 0.0;
-  sa.seed = seed;
+  sa.n_sink = p.n_sink;
+  sa.recent = p.recent;
+  sa.current = p.current ? 1 : 0;
+  sa.anneal_steps = p.anneal_steps;
+  sa.tau_init = p.gumbel ? p.tau_init : 0.0;
+  sa.tau_end = p.gumbel ? p.tau_end : 0.0;
+  sa.seed = p.seed;
   sa.scale = (float)(1.0 / std::sqrt((double)d));
   // keyformer FIXED GAP #2: moved stored rows go back one position
-  const FreqCache &fc = freqs(d, rope_base);
+  const FreqCache &fc = freqs(d, p.rope_base);
   for (int j = 0; j < d / 2; ++j) {
     sa.back1.c[j] = fc.cos_m1[j];
     sa.back1.s[j] = fc.sin_m1[j];
@@ -144,20 +181,18 @@ void advance(kve_counters *ctr, int32_t budget) {
   ctr->pos += 1;
 }
 
+// One layer, one token: the descriptor travels by value with the launch.
 int step_impl(const kve_layer *L, const void *new_k, const void *new_v, kve_counters *ctr,
-              int32_t budget, int32_t n_sink, double tau_init, double tau_end,
-              int32_t anneal_steps, double rope_base, uint64_t seed, int32_t *evicted,
-              void *stream, bool gumbel) {
-  if (check_layer(L, new_k, new_v, ctr, budget, n_sink, gumbel) != KVE_OK) return KVE_EINVAL;
-  if (check_shared(tau_init, tau_end, anneal_steps, rope_base) != KVE_OK) return KVE_EINVAL;
+              int32_t budget, const Policy &p, int32_t *evicted, void *stream) {
+  if (check_policy(p) != KVE_OK) return KVE_EINVAL;
+  if (check_layer(L, new_k, new_v, ctr, budget, p) != KVE_OK) return KVE_EINVAL;
   const int dev = check_device();
   if (dev != KVE_OK) return dev;
 
-  const kve::LayerArgs la = layer_args(L, new_k, new_v, ctr, budget, evicted, gumbel);
-  const kve::SharedArgs sa =
-      shared_args(L->d, n_sink, tau_init, tau_end, anneal_steps, rope_base, seed, gumbel);
+  const kve::LayerArgs la = layer_args(L, new_k, new_v, ctr, budget, evicted, p.gumbel);
+  const kve::SharedArgs sa = shared_args(L->d, p);
   const hipError_t err =
-      kve::launch_step(la, sa, L->bh, L->d, gumbel, reinterpret_cast<hipStream_t>(stream));
+      kve::launch_step(la, sa, L->bh, L->d, p.gumbel, reinterpret_cast<hipStream_t>(stream));
   if (err != hipSuccess) return KVE_ELAUNCH;
   advance(ctr, budget);
   return KVE_OK;
@@ -207,19 +242,16 @@ int ring_init(Ring &r) {
 // Checks every layer first.
 int batch_impl(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
                const void *const *new_k, const void *const *new_v, kve_counters *ctrs,
-               const int32_t *budgets, int32_t n_sink, double tau_init, double tau_end,
-               int32_t anneal_steps, double rope_base, uint64_t seed, int32_t *const *evicted,
-               void *stream, bool gumbel) {
+               const int32_t *budgets, const Policy &p, int32_t *const *evicted, void *stream) {
   if (n_layers < 1 || n_layers > kve::kMaxBatchLayers) return KVE_EINVAL;
   if (n_tokens < 1 || n_tokens > kve::kMaxTokens) return KVE_EINVAL;
   if (!layers || !new_k || !new_v || !ctrs || !budgets) return KVE_EINVAL;
-  if (check_shared(tau_init, tau_end, anneal_steps, rope_base) != KVE_OK) return KVE_EINVAL;
+  if (check_policy(p) != KVE_OK) return KVE_EINVAL;
   const int d = layers[0].d;
   int64_t blocks = 0;
   int max_n = 0;
   for (int32_t l = 0; l < n_layers; ++l) {
-    if (check_layer(&layers[l], new_k[l], new_v[l], &ctrs[l], budgets[l], n_sink, gumbel) !=
-        KVE_OK)
+    if (check_layer(&layers[l], new_k[l], new_v[l], &ctrs[l], budgets[l], p) != KVE_OK)
       return KVE_EINVAL;
     if (layers[l].d != d) return KVE_EINVAL;
     if ((int64_t)ctrs[l].next_pos + n_tokens >= INT32_MAX ||
@@ -249,13 +281,12 @@ int batch_impl(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
   int32_t block0 = 0;
   for (int32_t l = 0; l < n_layers; ++l) {
     hl[l] = layer_args(&layers[l], new_k[l], new_v[l], &ctrs[l], budgets[l],
-                       evicted ? evicted[l] : nullptr, gumbel);
+                       evicted ? evicted[l] : nullptr, p.gumbel);
     hl[l].block0 = block0;
     hl[l].n_tokens = n_tokens;
     block0 += layers[l].bh;
   }
-  const kve::SharedArgs sa =
-      shared_args(d, n_sink, tau_init, tau_end, anneal_steps, rope_base, seed, gumbel);
+  const kve::SharedArgs sa = shared_args(d, p);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const size_t layer_bytes = sizeof(kve::LayerArgs) * n_layers;
   // The copy runs on the library's own stream (it touches only this slot, which
@@ -268,7 +299,7 @@ int batch_impl(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
     return KVE_ELAUNCH;
   const hipError_t err =
       kve::launch_step_layers(reinterpret_cast<const kve::LayerArgs *>(dslot), n_layers,
-                              (int)blocks, max_n, sa, d, gumbel, s);
+                              (int)blocks, max_n, sa, d, p.gumbel, s);
   if (err != hipSuccess) return KVE_ELAUNCH;
   if (hipEventRecord(r.done[slot], s) != hipSuccess) return KVE_ELAUNCH;
   r.pending[slot] = true;
@@ -284,15 +315,16 @@ KVE_EXPORT int keyformer_step(const kve_layer *L, const void *new_k, const void 
                               double tau_init, double tau_end, int32_t anneal_steps,
                               double rope_base, uint64_t seed, int32_t *evicted,
                               void *stream) {
-  return step_impl(L, new_k, new_v, ctr, budget, n_sink, tau_init, tau_end, anneal_steps,
-                   rope_base, seed, evicted, stream, true);
+  return step_impl(L, new_k, new_v, ctr, budget,
+                   keyformer_policy(n_sink, tau_init, tau_end, anneal_steps, rope_base, seed),
+                   evicted, stream);
 }
 
 KVE_EXPORT int pyramid_step(const kve_layer *L, const void *new_k, const void *new_v,
                             kve_counters *ctr, int32_t budget, int32_t n_sink,
                             double rope_base, int32_t *evicted, void *stream) {
-  return step_impl(L, new_k, new_v, ctr, budget, n_sink, 0.0, 0.0, 0, rope_base, 0, evicted,
-                   stream, false);
+  return step_impl(L, new_k, new_v, ctr, budget, pyramid_policy(n_sink, rope_base), evicted,
+                   stream);
 }
 
 KVE_EXPORT int keyformer_step_layers(int32_t n_layers, const kve_layer *layers,
@@ -301,8 +333,17 @@ KVE_EXPORT int keyformer_step_layers(int32_t n_layers, const kve_layer *layers,
                                      double tau_init, double tau_end, int32_t anneal_steps,
                                      double rope_base, uint64_t seed, int32_t *const *evicted,
                                      void *stream) {
-  return batch_impl(n_layers, 1, layers, new_k, new_v, ctrs, budgets, n_sink, tau_init, tau_end,
-                    anneal_steps, rope_base, seed, evicted, stream, true);
+  return batch_impl(n_layers, 1, layers, new_k, new_v, ctrs, budgets,
+                    keyformer_policy(n_sink, tau_init, tau_end, anneal_steps, rope_base, seed),
+                    evicted, stream);
+}
+
+KVE_EXPORT int pyramid_step_layers(int32_t n_layers, const kve_layer *layers,
+                                   const void *const *new_k, const void *const *new_v,
+                                   kve_counters *ctrs, const int32_t *budgets, int32_t n_sink,
+                                   double rope_base, int32_t *const *evicted, void *stream) {
+  return batch_impl(n_layers, 1, layers, new_k, new_v, ctrs, budgets,
+                    pyramid_policy(n_sink, rope_base), evicted, stream);
 }
 
 KVE_EXPORT int keyformer_step_tokens(const kve_layer *L, int32_t n_tokens, const void *new_k,
@@ -312,8 +353,9 @@ KVE_EXPORT int keyformer_step_tokens(const kve_layer *L, int32_t n_tokens, const
                                      int32_t *evicted, void *stream) {
   if (!L) return KVE_EINVAL;
   int32_t *ev[1] = {evicted};
-  return batch_impl(1, n_tokens, L, &new_k, &new_v, ctr, &budget, n_sink, tau_init, tau_end,
-                    anneal_steps, rope_base, seed, ev, stream, true);
+  return batch_impl(1, n_tokens, L, &new_k, &new_v, ctr, &budget,
+                    keyformer_policy(n_sink, tau_init, tau_end, anneal_steps, rope_base, seed),
+                    ev, stream);
 }
 
 KVE_EXPORT int pyramid_step_tokens(const kve_layer *L, int32_t n_tokens, const void *new_k,
@@ -322,16 +364,8 @@ KVE_EXPORT int pyramid_step_tokens(const kve_layer *L, int32_t n_tokens, const v
                                    void *stream) {
   if (!L) return KVE_EINVAL;
   int32_t *ev[1] = {evicted};
-  return batch_impl(1, n_tokens, L, &new_k, &new_v, ctr, &budget, n_sink, 0.0, 0.0, 0,
-                    rope_base, 0, ev, stream, false);
-}
-
-KVE_EXPORT int pyramid_step_layers(int32_t n_layers, const kve_layer *layers,
-                                   const void *const *new_k, const void *const *new_v,
-                                   kve_counters *ctrs, const int32_t *budgets, int32_t n_sink,
-                                   double rope_base, int32_t *const *evicted, void *stream) {
-  return batch_impl(n_layers, 1, layers, new_k, new_v, ctrs, budgets, n_sink, 0.0, 0.0, 0,
-                    rope_base, 0, evicted, stream, false);
+  return batch_impl(1, n_tokens, L, &new_k, &new_v, ctr, &budget,
+                    pyramid_policy(n_sink, rope_base), ev, stream);
 }
 
 KVE_EXPORT int keyformer_step_layers_tokens(int32_t n_layers, int32_t n_tokens,
@@ -342,8 +376,9 @@ KVE_EXPORT int keyformer_step_layers_tokens(int32_t n_layers, int32_t n_tokens,
                                             int32_t anneal_steps, double rope_base,
                                             uint64_t seed, int32_t *const *evicted,
                                             void *stream) {
-  return batch_impl(n_layers, n_tokens, layers, new_k, new_v, ctrs, budgets, n_sink, tau_init,
-                    tau_end, anneal_steps, rope_base, seed, evicted, stream, true);
+  return batch_impl(n_layers, n_tokens, layers, new_k, new_v, ctrs, budgets,
+                    keyformer_policy(n_sink, tau_init, tau_end, anneal_steps, rope_base, seed),
+                    evicted, stream);
 }
 
 KVE_EXPORT int pyramid_step_layers_tokens(int32_t n_layers, int32_t n_tokens,
@@ -352,8 +387,32 @@ KVE_EXPORT int pyramid_step_layers_tokens(int32_t n_layers, int32_t n_tokens,
                                           const int32_t *budgets, int32_t n_sink,
                                           double rope_base, int32_t *const *evicted,
                                           void *stream) {
-  return batch_impl(n_layers, n_tokens, layers, new_k, new_v, ctrs, budgets, n_sink, 0.0, 0.0,
-                    0, rope_base, 0, evicted, stream, false);
+  return batch_impl(n_layers, n_tokens, layers, new_k, new_v, ctrs, budgets,
+                    pyramid_policy(n_sink, rope_base), evicted, stream);
+}
+
+KVE_EXPORT int kve_step(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
+                        const void *const *new_k, const void *const *new_v, kve_counters *ctrs,
+                        const int32_t *budgets, const kve_policy *policy,
+                        int32_t *const *evicted, void *stream) {
+  if (!policy || !layers || !new_k || !new_v || !ctrs || !budgets) return KVE_EINVAL;
+  if (policy->score != KVE_SCORE_CUMULATIVE && policy->score != KVE_SCORE_CURRENT)
+    return KVE_EINVAL;
+  if (policy->gumbel != 0 && policy->gumbel != 1) return KVE_EINVAL;
+  Policy p;
+  p.n_sink = policy->n_sink;
+  p.recent = policy->recent;
+  p.current = policy->score == KVE_SCORE_CURRENT;
+  p.gumbel = policy->gumbel == 1;
+  p.tau_init = p.gumbel ? policy->tau_init : 0.0;
+  p.tau_end = p.gumbel ? policy->tau_end : 0.0;
+  p.anneal_steps = p.gumbel ? policy->anneal_steps : 0;
+  p.rope_base = policy->rope_base;
+  p.seed = p.gumbel ? policy->seed : 0;
+  if (n_layers == 1 && n_tokens == 1)        // no descriptor ring needed
+    return step_impl(&layers[0], new_k[0], new_v[0], &ctrs[0], budgets[0], p,
+                     evicted ? evicted[0] : nullptr, stream);
+  return batch_impl(n_layers, n_tokens, layers, new_k, new_v, ctrs, budgets, p, evicted, stream);
 }
 
 // "The budget schedule": linear taper, mean avg_budget, floor n_sink + 1.

@@ -41,6 +41,8 @@ struct LayerArgs {
 // What every layer of a launch shares.
 struct SharedArgs {
   int32_t n_sink;
+  int32_t recent;          // trailing rows never evicted (0 = off)
+  int32_t current;         // 1: score = this step's weight (TOVA), 0: += (H2O / Keyformer)
   int32_t anneal_steps;
   double tau_init;
   double tau_end;

@@ -282,9 +282,11 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
 
   // ---- prefetch scores (and, when evicting, gumbel) into LDS ---------------
   // Every lane issues a load (the tail clamps to row n-1 and lands in padding).
+  // With the current-step score (TOVA) the old scores are not needed.
+  const bool current = sa.current != 0;
   for (int base = wave * 64; base < n; base += NT) {
     const int i = min(base + lane, n - 1);
-    load_dword_to_lds(la.scores + row0 + i, lds_s + base);
+    if (!current) load_dword_to_lds(la.scores + row0 + i, lds_s + base);
     if (GUMBEL && over) load_dword_to_lds(la.gumbel + row0 + i, lds_g + base);
   }
 
@@ -384,13 +386,18 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   const float g_new = GUMBEL ? gumbel_at(sa.seed, (uint64_t)(int64_t)(la.hh_base + hh),
                                          (uint64_t)(int64_t)la.pos)
                              : 0.f;
+  // Candidates: rows n_sink .. n - recent of the n + 1 rows after the append
+  // (sinks and the trailing window protected); the new row (index n) is one
+  // only without a window.  The host guarantees the range is not empty.
   const int n_sink = sa.n_sink;
+  const int last = n - sa.recent;
   float bv = INFINITY;
   int bi = 0x7fffffff;
   for (int i = tid; i < n; i += NT) {
-    const float s = lds_s[i] + lds_x[i] * rz;
+    const float pi = lds_x[i] * rz;
+    const float s = current ? pi : lds_s[i] + pi;
     lds_s[i] = s;
-    if (over && i >= n_sink) {
+    if (over && i >= n_sink && i <= last) {
       const float key = GUMBEL ? fmaf(tau, lds_g[i], s) : s;
       if (key < bv) {                      // rows visited in increasing order
         bv = key;
@@ -398,7 +405,7 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
       }
     }
   }
-  if (over && tid == 0) {                  // the new row: score 0
+  if (over && tid == 0 && last == n) {     // the new row: score 0
     const float key = GUMBEL ? fmaf(tau, g_new, 0.0f) : 0.0f;
     argmin_merge(bv, bi, key, n);
   }

@@ -164,6 +164,15 @@ def compare_cache(layer, hh: int, s: Sample, gpu_ev: np.ndarray, first_tid: int)
     return errs
 
 
+def policy_for(w: synth.Workload):
+    """The kve_step policy of a workload (same parameters as params_for)."""
+    import kv_cache_eviction_step_amd as kve
+    prm = params_for(w, w.budget, 0)
+    kind = {"keyformer": "keyformer", "pyramid": "pyramid", "tova": "tova"}[w.kind]
+    return kve.policy(kind, w.n_sink, w.recent, prm.tau_init, prm.tau_end, prm.anneal_steps,
+                      w.rope_base, w.gumbel_seed)
+
+
 def run_layer(w: synth.Workload, layer_idx: int, budget: int, T: int, samples: list[Sample],
               init_n: int | None, next_pos: int, device, cap: int | None = None,
               bh: int | None = None, gen_seed: int = 1234, hh_base: int = 0):
@@ -188,6 +197,14 @@ def run_layer(w: synth.Workload, layer_idx: int, budget: int, T: int, samples: l
     ev = torch.full((T, bh), -7, dtype=torch.int32, device=device)
     ctr = kve.Counters(n0, next_pos, next_pos)
     prm = params_for(w, budget, 0)
+    if w.kind == "tova" or w.recent > 0:
+        # the extensions go through the general entry point, one token per call
+        batch = kve.LayerBatch([L], [budget], [ctr])
+        pol = policy_for(w)
+        for t in range(T):
+            kve.step(batch, [nk[t]], [nv[t]], pol, [ev[t]])
+        torch.cuda.synchronize(device)
+        return L, ev.cpu().numpy(), batch.ctrs[0]
     cl = L.c_struct()
     for t in range(T):
         if kf:

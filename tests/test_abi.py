@@ -30,7 +30,8 @@ def test_header_declares_the_abi():
     assert set(_declared()) == {"keyformer_step", "pyramid_step", "keyformer_step_layers",
                                 "pyramid_step_layers", "keyformer_step_tokens",
                                 "pyramid_step_tokens", "keyformer_step_layers_tokens",
-                                "pyramid_step_layers_tokens", "pyramid_budgets", "kve_strerror"}
+                                "pyramid_step_layers_tokens", "kve_step", "pyramid_budgets",
+                                "kve_strerror"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -229,3 +230,74 @@ def test_multi_token_rejects_before_any_launch(n_tokens, ctr):
     assert (c.n_kept, c.next_pos, c.pos) == ctr
     assert kve.lib().pyramid_step_tokens(None, 4, FAKE, FAKE, ctypes.byref(c), 32, 4, 1e4, None,
                                          None) == kve.KVE_EINVAL
+
+
+def _policy_call(layers, ctrs, budgets, pol, n_tokens=1):
+    n = len(layers)
+    arr = (KveLayer * n)(*layers)
+    cs = (Counters * n)(*ctrs)
+    bs = (ctypes.c_int32 * n)(*budgets)
+    ptrs = (ctypes.c_void_p * n)(*([FAKE] * n))
+    rc = kve.lib().kve_step(n, n_tokens, arr, ptrs, ptrs, cs, bs,
+                            ctypes.byref(pol) if pol is not None else None, None, None)
+    return rc, [(c.n_kept, c.next_pos, c.pos) for c in cs]
+
+
+@pytest.mark.parametrize("case", ["null_policy", "bad_score", "bad_gumbel_flag", "negative_recent",
+                                  "window_fills_budget", "window_fills_budget_batched",
+                                  "negative_tau_with_gumbel", "null_gumbel_with_noise",
+                                  "tokens_129"])
+def test_kve_step_rejects_before_any_launch(case):
+    """kve_step checks its policy as init_keyformer_state does: sinks plus the
+    recent window must leave room to evict within every layer's budget."""
+    layers = [_layer(), _layer()]
+    budgets = [32, 32]
+    pol = kve.policy("keyformer", 4, recent=3, tau_init=1.0, tau_end=2.0, anneal_steps=64)
+    n_layers, n_tokens = 1, 1
+    if case == "null_policy":
+        pol = None
+    elif case == "bad_score":
+        pol.score = 2
+    elif case == "bad_gumbel_flag":
+        pol.gumbel = 2
+    elif case == "negative_recent":
+        pol.recent = -1
+    elif case == "window_fills_budget":
+        pol.recent = 28                                   # 4 + 28 == 32: no room
+    elif case == "window_fills_budget_batched":
+        n_layers, budgets, pol.recent = 2, [40, 20], 16   # layer 1: 4 + 16 >= 20
+    elif case == "negative_tau_with_gumbel":
+        pol.tau_init = -1.0
+    elif case == "null_gumbel_with_noise":
+        layers = [_layer(gumbel=None), _layer()]
+    elif case == "tokens_129":
+        n_tokens = 129
+    ctrs = [Counters(32, 100, 100), Counters(32, 100, 100)]
+    if case == "window_fills_budget_batched":
+        ctrs = [Counters(40, 100, 100), Counters(20, 100, 100)]
+        layers = [_layer(cap=41), _layer(cap=41)]
+    before = [(c.n_kept, c.next_pos, c.pos) for c in ctrs[:n_layers]]
+    rc, after = _policy_call(layers[:n_layers], ctrs[:n_layers], budgets[:n_layers], pol, n_tokens)
+    assert rc == kve.KVE_EINVAL
+    assert after == before
+
+
+def test_kve_step_policy_passes_host_checks():
+    """The largest window that leaves one evictable row, with TOVA scoring and
+    no noise (NULL gumbel allowed), reaches the device check."""
+    pol = kve.policy("tova", 4, recent=27)
+    rc, after = _policy_call([_layer(gumbel=None)], [Counters(32, 100, 100)], [32], pol)
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; the no-device path is not reachable")
+    assert rc == kve.KVE_ENODEV
+    assert after == [(32, 100, 100)]
+
+
+def test_policy_helper():
+    p = kve.policy("keyformer", 4, 2, 1.0, 2.0, 64, 5e5, seed=-1)
+    assert (p.n_sink, p.recent, p.score, p.gumbel, p.anneal_steps) == (4, 2, 0, 1, 64)
+    assert p.seed == 2**64 - 1 and p.rope_base == 5e5
+    t = kve.policy("tova", 4, 1, 1.0, 2.0, 64)
+    assert (t.score, t.gumbel, t.tau_init, t.anneal_steps) == (kve.SCORE_CURRENT, 0, 0.0, 0)
+    with pytest.raises(ValueError):
+        kve.policy("snapkv", 4)

@@ -14,7 +14,8 @@ import torch
 
 import oracle
 import synth
-from gpu_harness import (Sample, compare_cache, load_state_into, oracle_samples, random_state,
+from gpu_harness import (Sample, compare_cache, load_state_into, oracle_samples, policy_for,
+                         random_state,
                          run_batched, run_layer)
 from oracle.guard import guarded_trajectory, params_for
 
@@ -608,3 +609,130 @@ def test_layers_tokens_full_trajectory_oracle(dev, wi, layers):
     for i in range(len(layers)):
         _assert_parity(Ls[i], evh[i], samples[i], 0)
         assert batch.ctrs[i].n_kept == budgets[i]
+
+
+
+# ---------------------------------------------------------------------------
+# the general entry point: recent window and TOVA-adapted scoring
+# ---------------------------------------------------------------------------
+
+def _wl(name, kind, d, prompt, decode, budget, recent, batch=1, heads=8, tau=(0.0, 0.0, 0)):
+    return synth.Workload(name, batch, 1, heads, d, prompt, decode, budget, 4, kind, *tau,
+                          recent=recent)
+
+
+POLICY_TRAJECTORIES = [
+    _wl("kf-recent4", "keyformer", 64, 64, 64, 32, 4, tau=(1.0, 2.0, 64)),
+    _wl("h2o-recent1", "pyramid", 64, 64, 64, 32, 1),
+    _wl("tova", "tova", 64, 64, 64, 32, 0),
+    _wl("tova-recent8", "tova", 128, 64, 64, 32, 8),
+    _wl("llama-kf-recent32", "keyformer", 128, 2048, 1024, 512, 32, tau=(1.0, 2.0, 1024)),
+    _wl("llama-tova-recent16", "tova", 128, 600, 400, 512, 16),
+]
+
+
+@pytest.mark.parametrize("w", POLICY_TRAJECTORIES, ids=lambda w: w.name)
+def test_policy_full_trajectory_oracle(dev, w):
+    """kve_step with a recent window and/or TOVA scoring: every cache of one
+    layer through the whole token stream, against the oracle."""
+    T = w.tokens
+    _say(f"[policy-traj] {w.name} kind={w.kind} recent={w.recent} bh={w.bh} T={T}")
+    samples = oracle_samples(w, 1, range(w.bh), w.budget, T, w.budget + 1)
+    L, ev, ctr = run_layer(w, 1, w.budget, T, samples, None, 0, dev)
+    _assert_parity(L, ev, samples, 0)
+    assert (ctr.n_kept, ctr.next_pos) == (w.budget, T)
+    late = ev[w.budget:]
+    if w.recent > 0:                       # the window makes every eviction interior
+        assert bool((late < w.budget - w.recent + 1).all()) and bool((late >= 4).all())
+    elif w.kind == "tova":                 # no window: the newest row always goes
+        assert bool((late == w.budget).all())
+
+
+def test_policy_full_size_sampled_late_riser(dev):
+    """The 8B late-riser launch (256 caches, budget 1024) under Keyformer with a
+    64-row window, from a steady state, four caches checked."""
+    base = synth.WORKLOADS[3]
+    w = synth.Workload("8b-late-riser-recent64", base.batch, base.layers, base.kv_heads, base.d,
+                       base.prompt, base.decode, base.budget, base.n_sink, base.kind,
+                       base.tau_init, base.tau_end, base.anneal_steps,
+                       late_riser=base.late_riser, recent=64)
+    T, next_pos = 40, w.prompt
+    hhs = [0, 77, 200, 255]
+    _say(f"[policy-full] {w.name} bh={w.bh} sampled={hhs} T={T}")
+    samples = oracle_samples(w, 5, hhs, w.budget, T, w.budget + 1, init_n=w.budget,
+                             next_pos=next_pos)
+    L, ev, _ = run_layer(w, 5, w.budget, T, samples, w.budget, next_pos, dev)
+    _assert_parity(L, ev, samples, next_pos)
+    assert bool((ev <= w.budget - 64).all())
+
+
+@pytest.mark.parametrize("kind,recent", [("keyformer", 3), ("tova", 5), ("tova", 0),
+                                         ("pyramid", 2)])
+@pytest.mark.parametrize("S", [1, 9])
+def test_policy_layers_tokens_equals_single(dev, kind, recent, S):
+    """kve_step over three layers and S tokens per call gives the same bits as
+    kve_step one layer and one token at a time."""
+    import kv_cache_eviction_step_amd as kve
+    kf = kind == "keyformer"
+    shapes = [(6, 24, 25, 0), (3, 12, 20, 9), (10, 40, 41, 50)]   # bh, budget, cap, hh_base
+    T, d = 90, 64
+    _say(f"[policy layers*tokens==single] kind={kind} recent={recent} S={S} T={T}")
+    w = _wl("pol", kind, d, T, 0, 24, recent, tau=(1.0, 2.0, 40) if kf else (0.0, 0.0, 0))
+    pol = policy_for(w)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(31)
+    nks, nvs, As, Bs, evas, evbs = [], [], [], [], [], []
+    for bh, budget, cap, hb in shapes:
+        k, v = synth.bulk_kv_torch(w, 0, T, bh, gen, dev)
+        nks.append(k)
+        nvs.append(v)
+        As.append(kve.Layer.empty(bh, cap, d, dev, gumbel=kf, hh_base=hb))
+        Bs.append(kve.Layer.empty(bh, cap, d, dev, gumbel=kf, hh_base=hb))
+        evas.append(torch.empty((T, bh), dtype=torch.int32, device=dev))
+        evbs.append(torch.full((T, bh), -9, dtype=torch.int32, device=dev))
+    budgets = [x[1] for x in shapes]
+    singles = [kve.LayerBatch([As[l]], [budgets[l]]) for l in range(3)]
+    for t in range(T):
+        for l in range(3):
+            kve.step(singles[l], [nks[l][t]], [nvs[l][t]], pol, [evas[l][t]])
+    batch = kve.LayerBatch(Bs, budgets)
+    for t0 in range(0, T, S):
+        t1 = min(T, t0 + S)
+        kve.step(batch, [x[t0:t1] for x in nks], [x[t0:t1] for x in nvs], pol,
+                 [x[t0:t1] for x in evbs], n_tokens=t1 - t0)
+    torch.cuda.synchronize()
+    for l in range(3):
+        a, b = singles[l].ctrs[0], batch.ctrs[l]
+        assert (a.n_kept, a.next_pos, a.pos) == (b.n_kept, b.next_pos, b.pos)
+        assert torch.equal(evas[l], evbs[l]), l
+        n = a.n_kept
+        for name in ("k", "v", "scores", "positions") + (("gumbel",) if kf else ()):
+            assert torch.equal(getattr(As[l], name)[:, :n], getattr(Bs[l], name)[:, :n]), \
+                (l, name)
+
+
+def test_policy_plain_equals_named_entry_points(dev):
+    """kve_step with recent 0 and the cumulative score is keyformer_step /
+    pyramid_step, bit for bit."""
+    import kv_cache_eviction_step_amd as kve
+    T, bh, d, budget = 70, 7, 128, 30
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    for kind in ("keyformer", "pyramid"):
+        kf = kind == "keyformer"
+        w = _wl("eq", kind, d, T, 0, budget, 0, tau=(1.0, 2.0, 32) if kf else (0.0, 0.0, 0))
+        nk, nv = synth.bulk_kv_torch(w, 0, T, bh, gen, dev)
+        A = kve.Layer.empty(bh, budget + 1, d, dev, gumbel=kf)
+        B = kve.Layer.empty(bh, budget + 1, d, dev, gumbel=kf)
+        ca = kve.Counters(0, 0, 0)
+        batch = kve.LayerBatch([B], [budget])
+        pol = policy_for(w)
+        for t in range(T):
+            if kf:
+                kve.keyformer_step(A, nk[t], nv[t], ca, budget, 4, 1.0, 2.0, 32, 1e4, 0)
+            else:
+                kve.pyramid_step(A, nk[t], nv[t], ca, budget, 4, 1e4)
+            kve.step(batch, [nk[t]], [nv[t]], pol)
+        torch.cuda.synchronize()
+        for name in ("k", "v", "scores", "positions") + (("gumbel",) if kf else ()):
+            assert torch.equal(getattr(A, name)[:, :budget], getattr(B, name)[:, :budget]), name

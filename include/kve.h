@@ -296,6 +296,31 @@ int kve_step(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
 int pyramid_budgets(int32_t n_layers, int32_t avg_budget, int32_t n_sink, double beta,
                     int32_t *out);
 
+/*
+ * kve_kept_indices -- return_indices of keyformer_update_batched: after a call
+ * that stepped n_tokens tokens into a cache that held n_prev rows, the rows
+ * now kept, as chronological indices into the prior rows followed by the new
+ * ones (0 .. n_prev-1 the prior rows in their order, n_prev + t the t-th new
+ * token).  Composed from that cache's `evicted` outputs of the call, in
+ * token order (each an index into the rows present after that token's
+ * append, or -1).
+ *   evicted   HOST i32 [n_tokens]; out  HOST i32 [n_prev + n_tokens]
+ * Returns the number of kept rows written to out, or KVE_EINVAL (n_prev < 0,
+ * n_tokens < 0, NULL pointers with n_tokens or n_prev > 0, an evicted index
+ * out of range).  Pure host arithmetic; needs no device.
+ */
+int32_t kve_kept_indices(int32_t n_prev, int32_t n_tokens, const int32_t *evicted, int32_t *out);
+
+/*
+ * kve_fp16_bytes / kve_full_fp16_bytes -- keyformer_fp16_bytes and
+ * full_keyformer_fp16_bytes: the K + V payload in fp16 of n_kept stored rows,
+ * or of all tokens_seen tokens had none been evicted, for one cache of head
+ * dimension d: 2 * 2 * rows * d bytes.  Scores, Gumbel values and positions
+ * are bookkeeping, not payload.  Returns -1 if a count is negative or d < 1.
+ */
+int64_t kve_fp16_bytes(int64_t n_kept, int32_t d);
+int64_t kve_full_fp16_bytes(int64_t tokens_seen, int32_t d);
+
 /* Text for a KVE_* code (static storage). */
 const char *kve_strerror(int code);
 

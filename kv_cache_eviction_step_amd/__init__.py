@@ -115,6 +115,13 @@ _lib.kve_step.argtypes = [
     ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(KveLayer), ctypes.c_void_p, ctypes.c_void_p,
     ctypes.POINTER(Counters), ctypes.c_void_p, ctypes.POINTER(Policy), ctypes.c_void_p,
     ctypes.c_void_p]
+_lib.kve_kept_indices.restype = ctypes.c_int32
+_lib.kve_kept_indices.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+_lib.kve_fp16_bytes.restype = ctypes.c_int64
+_lib.kve_fp16_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32]
+_lib.kve_full_fp16_bytes.restype = ctypes.c_int64
+_lib.kve_full_fp16_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32]
 _lib.pyramid_budgets.restype = ctypes.c_int
 _lib.pyramid_budgets.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                  ctypes.c_double, ctypes.c_void_p]
@@ -123,7 +130,8 @@ _lib.kve_strerror.argtypes = [ctypes.c_int]
 
 EXPORTED = ("keyformer_step", "pyramid_step", "keyformer_step_layers", "pyramid_step_layers",
             "keyformer_step_tokens", "pyramid_step_tokens", "keyformer_step_layers_tokens",
-            "pyramid_step_layers_tokens", "kve_step", "pyramid_budgets", "kve_strerror")
+            "pyramid_step_layers_tokens", "kve_step", "pyramid_budgets", "kve_kept_indices",
+            "kve_fp16_bytes", "kve_full_fp16_bytes", "kve_strerror")
 
 
 def lib() -> ctypes.CDLL:
@@ -187,6 +195,13 @@ class Layer:
                    torch.zeros((bh, cap), dtype=torch.float32, **z),
                    torch.zeros((bh, cap), dtype=torch.float32, **z) if gumbel else None,
                    torch.zeros((bh, cap), dtype=torch.int32, **z), hh_base)
+
+    def get_kv(self, n_kept: int):
+        """keyformer_get_kv: views (no copies) of the live rows, keys and values
+        [bh, n_kept, d]; zero-row views before the first step."""
+        if not 0 <= n_kept <= self.cap:
+            raise ValueError(f"n_kept must be in [0, {self.cap}]")
+        return self.k[:, :n_kept], self.v[:, :n_kept]
 
     def c_struct(self) -> KveLayer:
         return KveLayer(self.k.data_ptr(), self.v.data_ptr(), self.scores.data_ptr(),
@@ -465,6 +480,36 @@ def step(batch: LayerBatch, new_k, new_v, pol: Policy, evicted=None, stream=None
                        batch.budgets, ctypes.byref(pol), pe,
                        _stream_ptr(stream, batch.layers[0]))
     _check(rc, "kve_step")
+
+
+def kept_indices(n_prev: int, evicted) -> list[int]:
+    """return_indices: the kept rows after stepping len(evicted) tokens into a
+    cache of n_prev rows, as chronological indices into prior + new rows.
+    evicted: that cache's evicted outputs (a sequence of ints, or a CPU int32
+    array / tensor), in token order."""
+    import numpy as np
+    ev = np.ascontiguousarray(np.asarray(evicted, dtype=np.int32).reshape(-1))
+    out = np.empty(max(n_prev + len(ev), 1), dtype=np.int32)
+    n = _lib.kve_kept_indices(n_prev, len(ev), ev.ctypes.data, out.ctypes.data)
+    if n < 0:
+        raise ValueError("kve_kept_indices: invalid arguments")
+    return out[:n].tolist()
+
+
+def fp16_bytes(n_kept: int, d: int) -> int:
+    """K + V payload of n_kept rows in fp16 (keyformer_fp16_bytes), one cache."""
+    r = _lib.kve_fp16_bytes(n_kept, d)
+    if r < 0:
+        raise ValueError("fp16_bytes: invalid arguments")
+    return int(r)
+
+
+def full_fp16_bytes(tokens_seen: int, d: int) -> int:
+    """K + V payload had every token been kept (full_keyformer_fp16_bytes)."""
+    r = _lib.kve_full_fp16_bytes(tokens_seen, d)
+    if r < 0:
+        raise ValueError("full_fp16_bytes: invalid arguments")
+    return int(r)
 
 
 def pyramid_budgets(n_layers: int, avg_budget: int, n_sink: int, beta: float) -> list[int]:

@@ -439,6 +439,36 @@ KVE_EXPORT int pyramid_budgets(int32_t n_layers, int32_t avg_budget, int32_t n_s
   return KVE_OK;
 }
 
+// return_indices (keyformer_update_batched): replay the call's evictions on
+// the chronological index list of prior + new rows.
+KVE_EXPORT int32_t kve_kept_indices(int32_t n_prev, int32_t n_tokens, const int32_t *evicted,
+                                    int32_t *out) {
+  if (n_prev < 0 || n_tokens < 0 || (int64_t)n_prev + n_tokens > INT32_MAX) return KVE_EINVAL;
+  if ((n_tokens > 0 && !evicted) || ((int64_t)n_prev + n_tokens > 0 && !out)) return KVE_EINVAL;
+  int32_t n = n_prev;
+  for (int32_t i = 0; i < n_prev; ++i) out[i] = i;
+  for (int32_t t = 0; t < n_tokens; ++t) {
+    out[n++] = n_prev + t;                    // the append
+    const int32_t e = evicted[t];
+    if (e < -1 || e >= n) return KVE_EINVAL;
+    if (e >= 0) {                             // later rows move down one slot
+      for (int32_t j = e; j < n - 1; ++j) out[j] = out[j + 1];
+      --n;
+    }
+  }
+  return n;
+}
+
+// keyformer_fp16_bytes / full_keyformer_fp16_bytes: K + V in fp16.
+KVE_EXPORT int64_t kve_fp16_bytes(int64_t n_kept, int32_t d) {
+  if (n_kept < 0 || d < 1 || n_kept > INT64_MAX / 4 / d) return -1;
+  return 4 * n_kept * d;
+}
+
+KVE_EXPORT int64_t kve_full_fp16_bytes(int64_t tokens_seen, int32_t d) {
+  return kve_fp16_bytes(tokens_seen, d);
+}
+
 KVE_EXPORT const char *kve_strerror(int code) {
   switch (code) {
     case KVE_OK: return "ok";

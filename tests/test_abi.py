@@ -23,7 +23,8 @@ HEADER = os.path.join(ROOT, "include", "kve.h")
 def _declared() -> list[str]:
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^\s*(?:int|const char \*)\s*(\w+)\s*\(", text, flags=re.M)
+    return re.findall(r"^\s*(?:int|int32_t|int64_t|const char \*)\s*(\w+)\s*\(", text,
+                      flags=re.M)
 
 
 def test_header_declares_the_abi():
@@ -31,6 +32,7 @@ def test_header_declares_the_abi():
                                 "pyramid_step_layers", "keyformer_step_tokens",
                                 "pyramid_step_tokens", "keyformer_step_layers_tokens",
                                 "pyramid_step_layers_tokens", "kve_step", "pyramid_budgets",
+                                "kve_kept_indices", "kve_fp16_bytes", "kve_full_fp16_bytes",
                                 "kve_strerror"}
 
 
@@ -301,3 +303,58 @@ def test_policy_helper():
     assert (t.score, t.gumbel, t.tau_init, t.anneal_steps) == (kve.SCORE_CURRENT, 0, 0.0, 0)
     with pytest.raises(ValueError):
         kve.policy("snapkv", 4)
+
+
+# ---------------------------------------------------------------------------
+# inspection helpers: return_indices, get_kv, byte accounting (Keyformer page:
+# keyformer_update_batched return_indices, keyformer_get_kv,
+# keyformer_fp16_bytes, full_keyformer_fp16_bytes)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind,recent", [("keyformer", 0), ("h2o", 3), ("tova", 2)])
+def test_kept_indices_match_oracle_token_ids(kind, recent):
+    """The composed evicted log names the same surviving rows as the oracle's
+    own token-id bookkeeping, from an empty cache and from a mid-run state."""
+    import numpy as np
+    import synth
+    w = synth.TINY_ANNEALED
+    prm = oracle.Params(20, 4, kind == "keyformer", 1.0, 2.0, 64, seed=0, hh=1, recent=recent,
+                        current_score=kind == "tova")
+    ks, vs = synth.token_kv(w, 0, 1, np.arange(160))
+    c = oracle.OracleCache(64, 21)
+    ev0 = c.run(ks[:100], vs[:100], prm)
+    assert kve.kept_indices(0, ev0) == list(c.tid[:c.n])
+    prior = list(c.tid[:c.n])
+    n_prev, t0 = c.n, c.next_pos
+    ev1 = c.run(ks[100:], vs[100:], prm)
+    idx = kve.kept_indices(n_prev, ev1)
+    assert [prior[i] if i < n_prev else t0 + i - n_prev for i in idx] == list(c.tid[:c.n])
+
+
+def test_kept_indices_edges_and_rejects():
+    assert kve.kept_indices(0, []) == []
+    assert kve.kept_indices(3, []) == [0, 1, 2]
+    assert kve.kept_indices(3, [-1, 4, 0]) == [1, 2, 3, 5]
+    assert kve.kept_indices(2, [2]) == [0, 1]                  # the new row itself
+    for n_prev, ev in ((2, [3]), (2, [-2]), (-1, [])):
+        with pytest.raises(ValueError):
+            kve.kept_indices(n_prev, ev)
+    assert kve.lib().kve_kept_indices(0, 1, None, None) == kve.KVE_EINVAL
+
+
+def test_byte_accounting_and_get_kv_views():
+    L = kve.Layer.empty(3, 17, 64, "cpu", gumbel=False)
+    k, v = L.get_kv(9)
+    assert tuple(k.shape) == (3, 9, 64) and k.data_ptr() == L.k.data_ptr()
+    assert v.data_ptr() == L.v.data_ptr()
+    per_cache = (k[0].numel() + v[0].numel()) * k.element_size()
+    assert kve.fp16_bytes(9, 64) == per_cache == 4 * 9 * 64
+    assert kve.full_fp16_bytes(3072, 128) == 4 * 3072 * 128
+    assert kve.full_fp16_bytes(3072, 128) / kve.fp16_bytes(512, 128) == 6.0
+    k0, v0 = L.get_kv(0)
+    assert tuple(k0.shape) == (3, 0, 64) and v0.numel() == 0
+    with pytest.raises(ValueError):
+        L.get_kv(18)
+    with pytest.raises(ValueError):
+        kve.fp16_bytes(-1, 64)
+    assert kve.lib().kve_full_fp16_bytes(10, 0) == -1

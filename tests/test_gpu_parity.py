@@ -514,7 +514,13 @@ def test_multi_token_full_trajectory_oracle(dev):
                                   w.budget, w.n_sink, prm.tau_init, prm.tau_end,
                                   prm.anneal_steps, w.rope_base, w.gumbel_seed, ev[t0:t0 + S])
     torch.cuda.synchronize()
-    _assert_parity(L, ev.cpu().numpy(), samples, 0)
+    evh = ev.cpu().numpy()
+    _assert_parity(L, evh, samples, 0)
+    # return_indices from the GPU's eviction log name the oracle's kept tokens
+    for s in samples:
+        assert kve.kept_indices(0, evh[:, s.hh]) == list(s.final["tid"])
+    k, v = L.get_kv(ctr.n_kept)
+    assert tuple(k.shape) == (w.bh, w.budget, w.d) and k.data_ptr() == L.k.data_ptr()
 
 
 @pytest.mark.parametrize("kind", ["kf", "pk"])

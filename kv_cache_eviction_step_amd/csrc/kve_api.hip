@@ -17,9 +17,9 @@
 
 namespace {
 
-// Largest budget a cache may have: the kernel keeps three fp32 values per
-// stored row in LDS (logit, score, gumbel): at most ~145 KiB of gfx950's 160 KiB.
-constexpr int32_t kMaxBudget = 12288;
+// Largest budget a cache may have: the kernel keeps one fp32 logit per stored
+// row in LDS and each thread's share of the scores in registers.
+constexpr int32_t kMaxBudget = kve::kMaxRows;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

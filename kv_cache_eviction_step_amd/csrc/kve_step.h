@@ -10,6 +10,7 @@ namespace kve {
 constexpr int kMaxHalfD = 64;        // d <= 128
 constexpr int kMaxBatchLayers = 128; // layers in one batched call
 constexpr int kMaxTokens = 128;      // tokens in one multi-token call
+constexpr int kMaxRows = 12288;      // largest budget: rows a cache may hold before a step
 
 // fp32 cosine / sine of one rotation angle per RoPE pair, computed in fp64
 // and rounded once.

@@ -205,19 +205,17 @@ __device__ __forceinline__ void wave_argmin(float &v, int &i) {
 // outstanding (gfx9 encoding; expcnt and lgkmcnt left unconstrained).
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-// One dword per lane from global memory straight into LDS (no registers):
-// lane l of the wave writes lds_wave_base[l].  lds_wave_base must be uniform.
-__device__ __forceinline__ void load_dword_to_lds(const float *src, float *lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                   (__attribute__((address_space(3))) void *)lds_wave_base, 4,
-                                   0, 0);
-}
-
 // x, unchanged, through an empty asm: the optimiser can no longer treat it
 // as loop-invariant (wave-uniform values only: the asm takes a scalar register).
 template <typename T>
 __device__ __forceinline__ T opaque(T x) {
   asm volatile("" : "+s"(x));
+  return x;
+}
+
+// The same for a per-lane value (vector register).
+__device__ __forceinline__ int opaque_lane(int x) {
+  asm volatile("" : "+v"(x));
   return x;
 }
 
@@ -239,11 +237,18 @@ __device__ __forceinline__ void stage_tables(const SharedArgs &sa) {
   }
 }
 
+// Per-token values a launch over several tokens evaluates ahead, kTokChunk
+// tokens at a time, into LDS: per token, the incoming row's rotation
+// (cos[D/2], sin[D/2]), its Gumbel value and tau.
+constexpr int kTokChunk = 16;
+
 // The whole step for cache `hh` of layer `la` (one workgroup).  stage_tables
-// has run in this workgroup.
-template <int D, int NT, int U, bool GUMBEL>
+// has run in this workgroup.  PRE: `pre` holds this token's per-token values
+// (above); otherwise the step evaluates them itself, each where no memory
+// access is in flight (a call there would wait for every outstanding load).
+template <int D, int NT, int U, bool GUMBEL, bool PRE, int R>
 __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs &sa,
-                                          const int hh) {
+                                          const int hh, const float *pre) {
   constexpr int V16 = D / 8;        // 16-byte chunks per row
   constexpr int LPR = D / 8;        // score pass: lanes per row (one chunk each)
   constexpr int RPS = NT / LPR;     // score pass: rows per sweep
@@ -254,7 +259,8 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   constexpr int NWAVE = NT / 64;
   static_assert(NT % 64 == 0 && RPS * LPR == NT && RPM * LPM == NT, "launch shape");
 
-  // LDS: logits -> weights [np] ; scores -> new scores [np] ; gumbel [np]
+  // LDS: logits -> weights [np].  Scores and Gumbel values of the rows
+  // i = tid + k*NT, k < R (R*NT >= n), live in this thread's registers.
   extern __shared__ float lds[];
   __shared__ float red_v[NWAVE];
   __shared__ int red_i[NWAVE];
@@ -263,7 +269,9 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   __shared__ float rn_c[kMaxHalfD];          // incoming row's rotation (wave 0 only)
   __shared__ float rn_s[kMaxHalfD];
 
-  const int tid = threadIdx.x;
+  // In the token loop, per-row offsets derived from the lane index would be
+  // hoisted out of the loop and held for the whole launch; re-derive them.
+  const int tid = PRE ? opaque_lane(threadIdx.x) : (int)threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int n = la.n_prev;
@@ -271,24 +279,11 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   const bool over = n + 1 > la.budget;
   const size_t row0 = (size_t)hh * (size_t)la.cap;     // first row of this cache
   float *__restrict__ lds_x = lds;
-  float *__restrict__ lds_s = lds + np;
-  float *__restrict__ lds_g = lds + 2 * np;
   const gptr<float> __restrict__ scores = global(la.scores);
   const gptr<float> __restrict__ gumbel = global(la.gumbel);
-  // When this step evicts, the incoming row may have to move from next_pos to
-  // slot n-1; wave 0 evaluates that rotation while its first keys load.
-  const bool rn_lane = over && wave == 0 && lane < D / 2;
-  const double rn_freq = rn_lane ? lds_freq[lane] : 0.0;   // staged by this same lane
 
-  // ---- prefetch scores (and, when evicting, gumbel) into LDS ---------------
-  // Every lane issues a load (the tail clamps to row n-1 and lands in padding).
   // With the current-step score (TOVA) the old scores are not needed.
   const bool current = sa.current != 0;
-  for (int base = wave * 64; base < n; base += NT) {
-    const int i = min(base + lane, n - 1);
-    if (!current) load_dword_to_lds(la.scores + row0 + i, lds_s + base);
-    if (GUMBEL && over) load_dword_to_lds(la.gumbel + row0 + i, lds_g + base);
-  }
 
   // ---- A: logits of every stored row against the incoming key -------------
   // Two batches of U loads in flight: batch it+1 is issued before batch it
@@ -323,17 +318,9 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
     }
   };
   // Two register buffers take turns (no copies, so the compiler waits only
-  // for the batch being consumed while the next one is in flight).  The LDS
-  // prefetch above must land before the first LDS write: wait for it right
-  // after issuing the first batch, so the two latencies overlap.
-  if (iters > 0) load_batch(0, bufa);
-  if (rn_lane) {
-    const f32x2 r = rotation_at(n - 1 - la.next_pos, rn_freq);
-    rn_c[lane] = r.x;
-    rn_s[lane] = r.y;
-  }
+  // for the batch being consumed while the next one is in flight).
   if (iters > 0) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(U));
+    load_batch(0, bufa);
     int it = 0;
     for (; it + 2 < iters; it += 2) {
       load_batch(it + 1, bufb);
@@ -350,10 +337,28 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
     }
   }
 
+  // The old scores (and, when evicting, Gumbel values) of this thread's rows:
+  // their loads overlap the normaliser below.  A slot is read only for i < n
+  // (and only under the condition it was loaded under).
+  float sreg[R], greg[R];
+  if (!current) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int i = tid + k * NT;
+      if (i < n) sreg[k] = scores[row0 + i];
+    }
+  }
+  if (GUMBEL && over) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int i = tid + k * NT;
+      if (i < n) greg[k] = gumbel[row0 + i];
+    }
+  }
+
   // ---- B: softmax normaliser ------------------------------------------------
   mx = wave_max(mx);
   if (lane == 0) red_v[wave] = mx;
-  __builtin_amdgcn_s_waitcnt(0);                // prefetched scores / gumbel have landed
   __syncthreads();
   if (wave == 0) {
     float m = lane < NWAVE ? red_v[lane] : -INFINITY;
@@ -381,11 +386,15 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   const float rz = 1.0f / bc_v;
 
   // ---- C: new scores and the eviction choice --------------------------------
-  const float tau = (GUMBEL && over) ? anneal_tau(sa.tau_init, sa.tau_end, sa.anneal_steps, la.pos)
-                                     : 0.f;
-  const float g_new = GUMBEL ? gumbel_at(sa.seed, (uint64_t)(int64_t)(la.hh_base + hh),
-                                         (uint64_t)(int64_t)la.pos)
-                             : 0.f;
+  float tau = 0.f, g_new = 0.f;
+  if constexpr (PRE) {
+    if (GUMBEL) g_new = pre[D];
+    if (GUMBEL && over) tau = pre[D + 1];
+  } else {
+    if (GUMBEL && over) tau = anneal_tau(sa.tau_init, sa.tau_end, sa.anneal_steps, la.pos);
+    if (GUMBEL)
+      g_new = gumbel_at(sa.seed, (uint64_t)(int64_t)(la.hh_base + hh), (uint64_t)(int64_t)la.pos);
+  }
   // Candidates: rows n_sink .. n - recent of the n + 1 rows after the append
   // (sinks and the trailing window protected); the new row (index n) is one
   // only without a window.  The host guarantees the range is not empty.
@@ -393,15 +402,19 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   const int last = n - sa.recent;
   float bv = INFINITY;
   int bi = 0x7fffffff;
-  for (int i = tid; i < n; i += NT) {
-    const float pi = lds_x[i] * rz;
-    const float s = current ? pi : lds_s[i] + pi;
-    lds_s[i] = s;
-    if (over && i >= n_sink && i <= last) {
-      const float key = GUMBEL ? fmaf(tau, lds_g[i], s) : s;
-      if (key < bv) {                      // rows visited in increasing order
-        bv = key;
-        bi = i;
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int i = tid + k * NT;
+    if (i < n) {
+      const float pi = lds_x[i] * rz;
+      const float s = current ? pi : sreg[k] + pi;
+      sreg[k] = s;
+      if (over && i >= n_sink && i <= last) {
+        const float key = GUMBEL ? fmaf(tau, greg[k], s) : s;
+        if (key < bv) {                    // rows visited in increasing order
+          bv = key;
+          bi = i;
+        }
       }
     }
   }
@@ -424,17 +437,32 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   }
   __syncthreads();
   const int e = bc_e;
+  // The incoming row moves (from next_pos to slot n-1) only when an older row
+  // was evicted; only then is its rotation needed.
+  const float *rot_c = rn_c, *rot_s = rn_s;
+  if constexpr (PRE) {
+    rot_c = pre;
+    rot_s = pre + D / 2;
+  } else if (e >= 0 && e < n && wave == 0 && lane < D / 2) {
+    const f32x2 r = rotation_at(n - 1 - la.next_pos, lds_freq[lane]);   // staged by this lane
+    rn_c[lane] = r.x;
+    rn_s[lane] = r.y;
+  }
   if (tid == 0 && la.evicted) global(la.evicted)[hh] = e;
 
   // ---- D: write-back ----------------------------------------------------------
   const gptr<int32_t> __restrict__ positions = global(la.positions);
-  for (int i = tid; i < n; i += NT) {
-    if (e < 0 || i < e) {
-      scores[row0 + i] = lds_s[i];
-    } else if (i > e) {
-      scores[row0 + i - 1] = lds_s[i];
-      if constexpr (GUMBEL) gumbel[row0 + i - 1] = lds_g[i];
-      positions[row0 + i - 1] = i - 1;
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int i = tid + k * NT;
+    if (i < n) {
+      if (e < 0 || i < e) {
+        scores[row0 + i] = sreg[k];
+      } else if (i > e) {
+        scores[row0 + i - 1] = sreg[k];
+        if constexpr (GUMBEL) gumbel[row0 + i - 1] = greg[k];
+        positions[row0 + i - 1] = i - 1;
+      }
     }
   }
 
@@ -522,11 +550,11 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
     const gptr<const u32x4> nv = global(reinterpret_cast<const u32x4 *>(la.new_v)) + (size_t)hh * V16;
     u32x4 k1 = nk[lm], k2 = nk[lm + V16 / 2];
     if (e >= 0) {                                // moved: rotate to position f
-      float cs[8], sn[8];                        // written above by this same wave
+      float cs[8], sn[8];        // written above by this same wave, or before the token
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        cs[j] = rn_c[lm * 8 + j];
-        sn[j] = rn_s[lm * 8 + j];
+        cs[j] = rot_c[lm * 8 + j];
+        sn[j] = rot_s[lm * 8 + j];
       }
       rotate_chunk(k1, k2, cs, sn);
     }
@@ -544,10 +572,10 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
 }
 
 // One layer per launch: workgroup hh owns cache hh.
-template <int D, int NT, int U, bool GUMBEL>
+template <int D, int NT, int U, bool GUMBEL, int R>
 __global__ __launch_bounds__(NT) void step_kernel(LayerArgs la, SharedArgs sa) {
   stage_tables<D>(sa);
-  step_body<D, NT, U, GUMBEL>(la, sa, blockIdx.x);
+  step_body<D, NT, U, GUMBEL, false, R>(la, sa, blockIdx.x, nullptr);
 }
 
 // Several layers and/or tokens per launch: the workgroups of layer l are
@@ -555,7 +583,7 @@ __global__ __launch_bounds__(NT) void step_kernel(LayerArgs la, SharedArgs sa) {
 // after the other (keyformer_update absorbs S tokens as S steps); between
 // tokens every store of the workgroup has landed and every wave has arrived,
 // so the next token reads the state the previous one left.
-template <int D, int NT, int U, bool GUMBEL>
+template <int D, int NT, int U, bool GUMBEL, int R>
 __global__ __launch_bounds__(NT) void step_layers_kernel(const LayerArgs *__restrict__ layers,
                                                          int n_layers, SharedArgs sa) {
   // layer of this workgroup: the number of layers starting at or before it,
@@ -573,8 +601,34 @@ __global__ __launch_bounds__(NT) void step_layers_kernel(const LayerArgs *__rest
   const int n_tokens = la.n_tokens;
   const int bh = (count < n_layers ? layers[count].block0 : (int)gridDim.x) - la.block0;
   stage_tables<D>(sa);
+  __syncthreads();                              // every wave reads lds_freq below
+  // The per-token values, kTokChunk tokens at a time, in dynamic LDS past the
+  // step's own arrays at their largest over this launch's tokens.
+  extern __shared__ float lds_dyn[];
+  constexpr int TAB = D + 2;
+  const int n_last = min(la.n_prev + n_tokens - 1, la.budget);
+  float *const tab = lds_dyn + ((n_last + 63) & ~63) + 64;
   LayerArgs lt = la;
   for (int t = 0; t < n_tokens; ++t) {
+    if (t % kTokChunk == 0) {                   // nothing is in flight here
+      const int cnt = min(kTokChunk, n_tokens - t);
+      for (int k = threadIdx.x; k < cnt * (D / 2); k += NT) {
+        const int i = k / (D / 2), j = k - i * (D / 2);
+        const int tok = t + i;
+        const int n_i = min(la.n_prev + tok, la.budget);
+        const f32x2 r = rotation_at(n_i - 1 - (la.next_pos + tok), lds_freq[j]);
+        tab[i * TAB + j] = r.x;
+        tab[i * TAB + D / 2 + j] = r.y;
+      }
+      if (GUMBEL && (int)threadIdx.x >= NT - cnt) {
+        const int i = threadIdx.x - (NT - cnt);
+        const int32_t pos = la.pos + t + i;
+        tab[i * TAB + D] = gumbel_at(sa.seed, (uint64_t)(int64_t)(la.hh_base + hh),
+                                     (uint64_t)(int64_t)pos);
+        tab[i * TAB + D + 1] = anneal_tau(sa.tau_init, sa.tau_end, sa.anneal_steps, pos);
+      }
+      __syncthreads();
+    }
     // Re-derive every per-cache address on each token (the asm hides these
     // values from the optimiser): hoisting them out of the loop would hold
     // them in registers for the whole launch.
@@ -591,7 +645,7 @@ __global__ __launch_bounds__(NT) void step_layers_kernel(const LayerArgs *__rest
     lt.new_k = reinterpret_cast<const char *>(la.new_k) + (size_t)t * bh * D * 2;
     lt.new_v = reinterpret_cast<const char *>(la.new_v) + (size_t)t * bh * D * 2;
     lt.evicted = la.evicted ? la.evicted + (size_t)t * bh : nullptr;
-    step_body<D, NT, U, GUMBEL>(lt, sa, hh_t);
+    step_body<D, NT, U, GUMBEL, true, R>(lt, sa, hh_t, tab + (t % kTokChunk) * TAB);
     __builtin_amdgcn_s_waitcnt(0);              // this token's stores have landed
     __syncthreads();
   }
@@ -611,9 +665,9 @@ __global__ __launch_bounds__(NT) void step_layers_kernel(const LayerArgs *__rest
 constexpr int kThreads = KVE_THREADS;
 constexpr int kUnroll = KVE_UNROLL;
 
-static size_t lds_bytes_for(int n_prev, bool gumbel) {
+static size_t lds_bytes_for(int n_prev) {
   const size_t np = (size_t)((n_prev + 63) & ~63) + 64;
-  return (gumbel ? 3 : 2) * np * sizeof(float);
+  return np * sizeof(float);
 }
 
 template <typename K>
@@ -623,11 +677,16 @@ static hipError_t allow_lds(K kern, size_t bytes) {
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-template <int D, bool GUMBEL>
-static hipError_t launch_d(const LayerArgs &la, const SharedArgs &sa, int bh,
-                           hipStream_t stream) {
-  auto kern = step_kernel<D, kThreads, kUnroll, GUMBEL>;
-  const size_t lds = lds_bytes_for(la.n_prev, GUMBEL);
+// Register slots per thread for the scores of a cache of n rows: the
+// smallest of three sizes that covers ceil(n / kThreads).
+constexpr int kR0 = 2, kR1 = 8, kR2 = (kMaxRows + kThreads - 1) / kThreads;
+static_assert(kR1 < kR2 || kR1 * kThreads >= kMaxRows, "row slots");
+
+template <int D, bool GUMBEL, int R>
+static hipError_t launch_d_r(const LayerArgs &la, const SharedArgs &sa, int bh,
+                             hipStream_t stream) {
+  auto kern = step_kernel<D, kThreads, kUnroll, GUMBEL, R>;
+  const size_t lds = lds_bytes_for(la.n_prev);
   hipError_t err = allow_lds(kern, lds);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(kern, dim3(bh), dim3(kThreads), lds, stream, la, sa);
@@ -635,15 +694,35 @@ static hipError_t launch_d(const LayerArgs &la, const SharedArgs &sa, int bh,
 }
 
 template <int D, bool GUMBEL>
-static hipError_t launch_layers_d(const LayerArgs *layers, int n_layers, int total_blocks,
-                                  int max_n_prev, const SharedArgs &sa, hipStream_t stream) {
-  auto kern = step_layers_kernel<D, kThreads, kUnroll, GUMBEL>;
-  const size_t lds = lds_bytes_for(max_n_prev, GUMBEL);
+static hipError_t launch_d(const LayerArgs &la, const SharedArgs &sa, int bh,
+                           hipStream_t stream) {
+  const int r = (la.n_prev + kThreads - 1) / kThreads;
+  if (r <= kR0) return launch_d_r<D, GUMBEL, kR0>(la, sa, bh, stream);
+  if (r <= kR1) return launch_d_r<D, GUMBEL, kR1>(la, sa, bh, stream);
+  return launch_d_r<D, GUMBEL, kR2>(la, sa, bh, stream);
+}
+
+template <int D, bool GUMBEL, int R>
+static hipError_t launch_layers_d_r(const LayerArgs *layers, int n_layers, int total_blocks,
+                                    int max_n_prev, const SharedArgs &sa, hipStream_t stream) {
+  auto kern = step_layers_kernel<D, kThreads, kUnroll, GUMBEL, R>;
+  const size_t lds = lds_bytes_for(max_n_prev) + (size_t)kTokChunk * (D + 2) * sizeof(float);
   hipError_t err = allow_lds(kern, lds);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(kern, dim3(total_blocks), dim3(kThreads), lds, stream, layers, n_layers,
                      sa);
   return hipGetLastError();
+}
+
+template <int D, bool GUMBEL>
+static hipError_t launch_layers_d(const LayerArgs *layers, int n_layers, int total_blocks,
+                                  int max_n_prev, const SharedArgs &sa, hipStream_t stream) {
+  const int r = (max_n_prev + kThreads - 1) / kThreads;
+  if (r <= kR0)
+    return launch_layers_d_r<D, GUMBEL, kR0>(layers, n_layers, total_blocks, max_n_prev, sa, stream);
+  if (r <= kR1)
+    return launch_layers_d_r<D, GUMBEL, kR1>(layers, n_layers, total_blocks, max_n_prev, sa, stream);
+  return launch_layers_d_r<D, GUMBEL, kR2>(layers, n_layers, total_blocks, max_n_prev, sa, stream);
 }
 
 hipError_t launch_step(const LayerArgs &la, const SharedArgs &sa, int bh, int d, bool gumbel,

@@ -191,6 +191,36 @@ __device__ __forceinline__ void wave_argmin(float &v, int &i) {
   }
 }
 
+// Reductions of the W per-wave partials held by lanes 0..W-1 (identity
+// elsewhere), done by every wave on its own: the last log2(W) steps of the
+// butterflies above (the earlier ones only meet identities), then lane 0's
+// value, uniform across the wave.
+__device__ __forceinline__ float first_lane(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+template <int W>
+__device__ __forceinline__ float partials_max(float x) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return first_lane(x);
+}
+template <int W>
+__device__ __forceinline__ float partials_sum(float x) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return first_lane(x);
+}
+template <int W>
+__device__ __forceinline__ int partials_argmin(float v, int i) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) {
+    float v2 = __shfl_xor(v, o);
+    int i2 = __shfl_xor(i, o);
+    argmin_merge(v, i, v2, i2);
+  }
+  return __builtin_amdgcn_readfirstlane(i);
+}
+
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
@@ -262,10 +292,11 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   // LDS: logits -> weights [np].  Scores and Gumbel values of the rows
   // i = tid + k*NT, k < R (R*NT >= n), live in this thread's registers.
   extern __shared__ float lds[];
-  __shared__ float red_v[NWAVE];
+  // one slot per wave for each reduction of the step (written once per step)
+  __shared__ float red_m[NWAVE];
+  __shared__ float red_z[NWAVE];
+  __shared__ float red_a[NWAVE];
   __shared__ int red_i[NWAVE];
-  __shared__ float bc_v;
-  __shared__ int bc_e;
   __shared__ float rn_c[kMaxHalfD];          // incoming row's rotation (wave 0 only)
   __shared__ float rn_s[kMaxHalfD];
 
@@ -358,15 +389,9 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
 
   // ---- B: softmax normaliser ------------------------------------------------
   mx = wave_max(mx);
-  if (lane == 0) red_v[wave] = mx;
-  __syncthreads();
-  if (wave == 0) {
-    float m = lane < NWAVE ? red_v[lane] : -INFINITY;
-    m = wave_max(m);
-    if (lane == 0) bc_v = m;
-  }
-  __syncthreads();
-  mx = bc_v;
+  if (lane == 0) red_m[wave] = mx;
+  __syncthreads();                              // also: every logit is in LDS
+  mx = partials_max<NWAVE>(lane < NWAVE ? red_m[lane] : -INFINITY);
   float sum = 0.f;
   for (int i = tid; i < n; i += NT) {
     const float w = expf(lds_x[i] - mx);
@@ -374,16 +399,9 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
     sum += w;
   }
   sum = wave_sum(sum);
-  __syncthreads();                              // every wave has read bc_v / red_v
-  if (lane == 0) red_v[wave] = sum;
+  if (lane == 0) red_z[wave] = sum;
   __syncthreads();
-  if (wave == 0) {
-    float z = lane < NWAVE ? red_v[lane] : 0.f;
-    z = wave_sum(z);
-    if (lane == 0) bc_v = z;
-  }
-  __syncthreads();
-  const float rz = 1.0f / bc_v;
+  const float rz = 1.0f / partials_sum<NWAVE>(lane < NWAVE ? red_z[lane] : 0.f);
 
   // ---- C: new scores and the eviction choice --------------------------------
   float tau = 0.f, g_new = 0.f;
@@ -423,20 +441,14 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
     argmin_merge(bv, bi, key, n);
   }
   wave_argmin(bv, bi);
-  __syncthreads();                              // bc_v consumed by every wave
   if (lane == 0) {
-    red_v[wave] = bv;
+    red_a[wave] = bv;
     red_i[wave] = bi;
   }
   __syncthreads();
-  if (wave == 0) {
-    float v = lane < NWAVE ? red_v[lane] : INFINITY;
-    int i = lane < NWAVE ? red_i[lane] : 0x7fffffff;
-    wave_argmin(v, i);
-    if (lane == 0) bc_e = over ? i : -1;
-  }
-  __syncthreads();
-  const int e = bc_e;
+  const int arg = partials_argmin<NWAVE>(lane < NWAVE ? red_a[lane] : INFINITY,
+                                         lane < NWAVE ? red_i[lane] : 0x7fffffff);
+  const int e = over ? arg : -1;
   // The incoming row moves (from next_pos to slot n-1) only when an older row
   // was evicted; only then is its rotation needed.
   const float *rot_c = rn_c, *rot_s = rn_s;

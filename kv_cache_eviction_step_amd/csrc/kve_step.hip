@@ -168,11 +168,6 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
 
 // (value, index) pairs: smaller value wins, equal values go to the lower index.
 __device__ __forceinline__ void argmin_merge(float &v, int &i, float v2, int i2) {
@@ -205,11 +200,23 @@ __device__ __forceinline__ float partials_max(float x) {
   return first_lane(x);
 }
 template <int W>
-__device__ __forceinline__ float partials_sum(float x) {
+__device__ __forceinline__ uint64_t partials_sum(uint64_t x) {
 #pragma unroll
   for (int o = W / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return first_lane(x);
+  return ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32)) << 32) |
+         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)x);
 }
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// The softmax normaliser is summed exactly: each weight w in [0, 1] as the
+// integer w * 2^40 (exact for w >= 2^-16, rounded to nearest below), so the
+// total does not depend on how rows are grouped over lanes and waves (the
+// workgroup size), and carries no float rounding of its own.
+constexpr float kZScale = 0x1p40f;
 template <int W>
 __device__ __forceinline__ int partials_argmin(float v, int i) {
 #pragma unroll
@@ -294,7 +301,7 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   extern __shared__ float lds[];
   // one slot per wave for each reduction of the step (written once per step)
   __shared__ float red_m[NWAVE];
-  __shared__ float red_z[NWAVE];
+  __shared__ uint64_t red_z[NWAVE];
   __shared__ float red_a[NWAVE];
   __shared__ int red_i[NWAVE];
   __shared__ float rn_c[kMaxHalfD];          // incoming row's rotation (wave 0 only)
@@ -392,16 +399,17 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   if (lane == 0) red_m[wave] = mx;
   __syncthreads();                              // also: every logit is in LDS
   mx = partials_max<NWAVE>(lane < NWAVE ? red_m[lane] : -INFINITY);
-  float sum = 0.f;
+  uint64_t sum = 0;
   for (int i = tid; i < n; i += NT) {
     const float w = expf(lds_x[i] - mx);
     lds_x[i] = w;
-    sum += w;
+    sum += (uint64_t)rintf(w * kZScale);
   }
-  sum = wave_sum(sum);
+  sum = wave_sum_u64(sum);
   if (lane == 0) red_z[wave] = sum;
   __syncthreads();
-  const float rz = 1.0f / partials_sum<NWAVE>(lane < NWAVE ? red_z[lane] : 0.f);
+  const uint64_t z = partials_sum<NWAVE>(lane < NWAVE ? red_z[lane] : (uint64_t)0);
+  const float rz = 1.0f / (float)((double)z * (1.0 / (double)kZScale));
 
   // ---- C: new scores and the eviction choice --------------------------------
   float tau = 0.f, g_new = 0.f;
@@ -690,69 +698,95 @@ static hipError_t allow_lds(K kern, size_t bytes) {
 }
 
 // Register slots per thread for the scores of a cache of n rows: the
-// smallest of three sizes that covers ceil(n / kThreads).
-constexpr int kR0 = 2, kR1 = 8, kR2 = (kMaxRows + kThreads - 1) / kThreads;
-static_assert(kR1 < kR2 || kR1 * kThreads >= kMaxRows, "row slots");
+// smallest of three sizes that covers ceil(n / NT).
+template <int NT>
+struct Slots {
+  static constexpr int r0 = 2, r1 = 8, r2 = (kMaxRows + NT - 1) / NT;
+  static_assert(r1 <= r2, "row slots");
+};
 
-template <int D, bool GUMBEL, int R>
+template <int NT, int D, bool GUMBEL, int R>
 static hipError_t launch_d_r(const LayerArgs &la, const SharedArgs &sa, int bh,
                              hipStream_t stream) {
-  auto kern = step_kernel<D, kThreads, kUnroll, GUMBEL, R>;
+  auto kern = step_kernel<D, NT, kUnroll, GUMBEL, R>;
   const size_t lds = lds_bytes_for(la.n_prev);
   hipError_t err = allow_lds(kern, lds);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(kern, dim3(bh), dim3(kThreads), lds, stream, la, sa);
+  hipLaunchKernelGGL(kern, dim3(bh), dim3(NT), lds, stream, la, sa);
   return hipGetLastError();
 }
 
-template <int D, bool GUMBEL>
+template <int NT, int D, bool GUMBEL>
 static hipError_t launch_d(const LayerArgs &la, const SharedArgs &sa, int bh,
                            hipStream_t stream) {
-  const int r = (la.n_prev + kThreads - 1) / kThreads;
-  if (r <= kR0) return launch_d_r<D, GUMBEL, kR0>(la, sa, bh, stream);
-  if (r <= kR1) return launch_d_r<D, GUMBEL, kR1>(la, sa, bh, stream);
-  return launch_d_r<D, GUMBEL, kR2>(la, sa, bh, stream);
+  using S = Slots<NT>;
+  const int r = (la.n_prev + NT - 1) / NT;
+  if (r <= S::r0) return launch_d_r<NT, D, GUMBEL, S::r0>(la, sa, bh, stream);
+  if (r <= S::r1) return launch_d_r<NT, D, GUMBEL, S::r1>(la, sa, bh, stream);
+  return launch_d_r<NT, D, GUMBEL, S::r2>(la, sa, bh, stream);
 }
 
-template <int D, bool GUMBEL, int R>
+template <int NT, int D, bool GUMBEL, int R>
 static hipError_t launch_layers_d_r(const LayerArgs *layers, int n_layers, int total_blocks,
                                     int max_n_prev, const SharedArgs &sa, hipStream_t stream) {
-  auto kern = step_layers_kernel<D, kThreads, kUnroll, GUMBEL, R>;
+  auto kern = step_layers_kernel<D, NT, kUnroll, GUMBEL, R>;
   const size_t lds = lds_bytes_for(max_n_prev) + (size_t)kTokChunk * (D + 2) * sizeof(float);
   hipError_t err = allow_lds(kern, lds);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(kern, dim3(total_blocks), dim3(kThreads), lds, stream, layers, n_layers,
-                     sa);
+  hipLaunchKernelGGL(kern, dim3(total_blocks), dim3(NT), lds, stream, layers, n_layers, sa);
   return hipGetLastError();
 }
 
-template <int D, bool GUMBEL>
+template <int NT, int D, bool GUMBEL>
 static hipError_t launch_layers_d(const LayerArgs *layers, int n_layers, int total_blocks,
                                   int max_n_prev, const SharedArgs &sa, hipStream_t stream) {
-  const int r = (max_n_prev + kThreads - 1) / kThreads;
-  if (r <= kR0)
-    return launch_layers_d_r<D, GUMBEL, kR0>(layers, n_layers, total_blocks, max_n_prev, sa, stream);
-  if (r <= kR1)
-    return launch_layers_d_r<D, GUMBEL, kR1>(layers, n_layers, total_blocks, max_n_prev, sa, stream);
-  return launch_layers_d_r<D, GUMBEL, kR2>(layers, n_layers, total_blocks, max_n_prev, sa, stream);
+  using S = Slots<NT>;
+  const int r = (max_n_prev + NT - 1) / NT;
+  if (r <= S::r0)
+    return launch_layers_d_r<NT, D, GUMBEL, S::r0>(layers, n_layers, total_blocks, max_n_prev,
+                                                   sa, stream);
+  if (r <= S::r1)
+    return launch_layers_d_r<NT, D, GUMBEL, S::r1>(layers, n_layers, total_blocks, max_n_prev,
+                                                   sa, stream);
+  return launch_layers_d_r<NT, D, GUMBEL, S::r2>(layers, n_layers, total_blocks, max_n_prev, sa,
+                                                 stream);
+}
+
+template <int NT>
+static hipError_t launch_step_nt(const LayerArgs &la, const SharedArgs &sa, int bh, int d,
+                                 bool gumbel, hipStream_t stream) {
+  if (d == 128)
+    return gumbel ? launch_d<NT, 128, true>(la, sa, bh, stream)
+                  : launch_d<NT, 128, false>(la, sa, bh, stream);
+  return gumbel ? launch_d<NT, 64, true>(la, sa, bh, stream)
+                : launch_d<NT, 64, false>(la, sa, bh, stream);
+}
+
+template <int NT>
+static hipError_t launch_layers_nt(const LayerArgs *layers, int n_layers, int total_blocks,
+                                   int max_n_prev, const SharedArgs &sa, int d, bool gumbel,
+                                   hipStream_t stream) {
+  if (d == 128)
+    return gumbel ? launch_layers_d<NT, 128, true>(layers, n_layers, total_blocks, max_n_prev, sa,
+                                                   stream)
+                  : launch_layers_d<NT, 128, false>(layers, n_layers, total_blocks, max_n_prev,
+                                                    sa, stream);
+  return gumbel ? launch_layers_d<NT, 64, true>(layers, n_layers, total_blocks, max_n_prev, sa,
+                                                stream)
+                : launch_layers_d<NT, 64, false>(layers, n_layers, total_blocks, max_n_prev, sa,
+                                                 stream);
 }
 
 hipError_t launch_step(const LayerArgs &la, const SharedArgs &sa, int bh, int d, bool gumbel,
                        hipStream_t stream) {
-  if (d == 128)
-    return gumbel ? launch_d<128, true>(la, sa, bh, stream) : launch_d<128, false>(la, sa, bh, stream);
-  return gumbel ? launch_d<64, true>(la, sa, bh, stream) : launch_d<64, false>(la, sa, bh, stream);
+  return launch_step_nt<kThreads>(la, sa, bh, d, gumbel, stream);
 }
 
 hipError_t launch_step_layers(const LayerArgs *layers, int n_layers, int total_blocks,
                               int max_n_prev, const SharedArgs &sa, int d, bool gumbel,
                               hipStream_t stream) {
-  if (d == 128)
-    return gumbel ? launch_layers_d<128, true>(layers, n_layers, total_blocks, max_n_prev, sa, stream)
-                  : launch_layers_d<128, false>(layers, n_layers, total_blocks, max_n_prev, sa,
-                                                stream);
-  return gumbel ? launch_layers_d<64, true>(layers, n_layers, total_blocks, max_n_prev, sa, stream)
-                : launch_layers_d<64, false>(layers, n_layers, total_blocks, max_n_prev, sa, stream);
+  return launch_layers_nt<kThreads>(layers, n_layers, total_blocks, max_n_prev, sa, d, gumbel,
+                                    stream);
 }
 
 }  // namespace kve

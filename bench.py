@@ -67,11 +67,17 @@ KERNEL_SOURCES = ["kv_cache_eviction_step_amd/csrc/kve_step.hip",
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources with comments and whitespace removed, so that
+    an edit of a comment does not invalidate a measurement."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

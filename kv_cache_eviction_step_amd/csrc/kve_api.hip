@@ -1,6 +1,8 @@
 // kve_api.hip -- host side of the C ABI declared in include/kve.h:
-// argument checks, fp64 rotation tables, the launch on the caller's stream,
-// the counter update, and the pyramid budget schedule.
+// argument checks, the eviction policy, fp64 rotation constants and
+// frequencies, the launch on the caller's stream, the counter update, the
+// descriptor ring of the multi-layer / multi-token calls, and the host-only
+// helpers (pyramid budget schedule, kept indices, byte accounting).
 #include <hip/hip_runtime.h>
 
 #include <atomic>

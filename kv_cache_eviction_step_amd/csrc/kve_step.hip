@@ -6,18 +6,22 @@
 //   A  score pass: coalesced non-temporal 128-bit loads of the stored keys, fp16 dot2
 //      products against the incoming key, 16-lane DPP reduction per row,
 //      logits to LDS (a matrix-vector product: bandwidth bound, no MFMA);
-//   B  softmax: block max, exponentials and block sum over LDS;
-//   C  new scores (fp32 add of the normalised mass) and, when over budget,
-//      the eviction key  fma(tau, gumbel, score)  with a block argmin that
-//      breaks ties towards the lowest index;
+//   B  softmax: block max, exponentials and an exact (fixed-point) block sum;
+//      meanwhile each thread loads the old scores / gumbel of its rows into
+//      registers;
+//   C  new scores (fp32 add of the normalised mass, or the mass itself for
+//      TOVA) and, when over budget, the eviction key  fma(tau, gumbel, score)
+//      over the non-protected rows with a block argmin that breaks ties
+//      towards the lowest index;
 //   D  write-back: scores / gumbel / positions of the rows after the evicted
 //      one move down one slot; keys and values of those rows move in
 //      ascending chunks (load all, barrier, store), keys re-rotated by -1
 //      position in fp32; the new row lands at its final slot.
 //
-// Two entry kernels share the body: one layer per launch (everything passed
-// by value), or several layers per launch (descriptors in device memory, the
-// workgroups of each layer contiguous in the grid).
+// Two entry kernels share the body: one layer and one token per launch
+// (everything passed by value), or several layers and/or tokens per launch
+// (descriptors in device memory, the workgroups of each layer contiguous in
+// the grid, each walking its cache through the tokens).
 //
 // Method (VeloxQuant-MLX pages): "veloxquant_mlx.quantizers.keyformer
 // module" -- keyformer_update steps 1-3, KeyformerState, FIXED GAP #1/#2,
@@ -267,7 +271,7 @@ __shared__ double lds_freq[kMaxHalfD];       // RoPE pair frequencies (fp64)
 template <int D>
 __device__ __forceinline__ void stage_tables(const SharedArgs &sa) {
   const int tid = threadIdx.x;
-  if (tid < D / 2) {                            // wave 0: the only reader of lds_freq
+  if (tid < D / 2) {                            // wave 0 (readers wait for a barrier)
     lds_back_c[tid] = sa.back1.c[tid];
     lds_back_s[tid] = sa.back1.s[tid];
     lds_freq[tid] = sa.freq[tid];

@@ -98,6 +98,13 @@ def _forced(w, hh, n, cap, next_pos, target):
     (300, 300, 4, 4),         # spans two score sweeps; every row after 4 moves
     (1000, 1000, 4, 517),     # several sweeps and move chunks, ragged tails
     (1000, 1000, 4, 998),
+    # score slots per thread change at n = 1024 / 1025 and 4096 / 4097
+    (1024, 1024, 4, 700),     # 2 slots, every slot used
+    (1024, 1100, 4, None),    # 2 slots, under budget
+    (1025, 1025, 4, 1000),    # 8 slots, the 1025th row in the first one
+    (4096, 4096, 4, 3000),    # 8 slots, every slot used
+    (4097, 4097, 4, 4096),    # 24 slots: evict the newest stored row
+    (4097, 4200, 4, None),    # 24 slots, under budget
 ])
 def test_single_step_edges(dev, d, kind, n, budget, n_sink, target):
     import kv_cache_eviction_step_amd as kve
@@ -742,3 +749,59 @@ def test_policy_plain_equals_named_entry_points(dev):
         torch.cuda.synchronize()
         for name in ("k", "v", "scores", "positions") + (("gumbel",) if kf else ()):
             assert torch.equal(getattr(A, name)[:, :budget], getattr(B, name)[:, :budget]), name
+
+
+@pytest.mark.parametrize("kind", ["kf", "pk"])
+def test_layers_tokens_large_budgets_equal_single_calls(dev, kind):
+    """The token-loop kernel with 8 and 24 score slots per thread (budgets 2000
+    and 5000, from full synthetic states): one launch of two layers x 16 tokens
+    gives the same bits as single-token calls per layer."""
+    import kv_cache_eviction_step_amd as kve
+    from gpu_harness import bulk_state
+    kf = kind == "kf"
+    shapes = [(3, 2000, 0), (2, 5000, 11)]                # bh, budget, hh_base
+    T, S, d, pos0 = 40, 16, 128, 9000
+    _say(f"[large layers*tokens==single] kind={kind} budgets={[x[1] for x in shapes]} T={T}")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(57)
+    As, Bs, nks, nvs, evas, evbs = [], [], [], [], [], []
+    for bh, budget, hb in shapes:
+        w = synth.Workload("lg", 1, 1, bh, d, pos0, T, budget, 4, "keyformer" if kf else "pyramid",
+                           1.0 if kf else 0.0, 2.0 if kf else 0.0, 64 if kf else 0)
+        A = kve.Layer.empty(bh, budget + 1, d, dev, gumbel=kf, hh_base=hb)
+        bulk_state(A, budget, w, gen)
+        B = kve.Layer(A.k.clone(), A.v.clone(), A.scores.clone(),
+                      A.gumbel.clone() if kf else None, A.positions.clone(), hh_base=hb)
+        k, v = synth.bulk_kv_torch(w, pos0, T, bh, gen, dev)
+        As.append(A); Bs.append(B); nks.append(k); nvs.append(v)
+        evas.append(torch.empty((T, bh), dtype=torch.int32, device=dev))
+        evbs.append(torch.full((T, bh), -9, dtype=torch.int32, device=dev))
+    budgets = [x[1] for x in shapes]
+    cas = [kve.Counters(b, pos0, pos0) for b in budgets]
+    args = (4, 1.0, 2.0, 64, 1e4, 3) if kf else (4, 1e4)
+    for t in range(T):
+        for l in range(2):
+            if kf:
+                kve.keyformer_step(As[l], nks[l][t], nvs[l][t], cas[l], budgets[l], *args,
+                                   evas[l][t])
+            else:
+                kve.pyramid_step(As[l], nks[l][t], nvs[l][t], cas[l], budgets[l], *args, evas[l][t])
+    batch = kve.LayerBatch(Bs, budgets, [kve.Counters(b, pos0, pos0) for b in budgets])
+    for t0 in range(0, T, S):
+        t1 = min(T, t0 + S)
+        ks = [x[t0:t1] for x in nks]
+        vs = [x[t0:t1] for x in nvs]
+        es = [x[t0:t1] for x in evbs]
+        if kf:
+            kve.keyformer_step_layers_tokens(batch, ks, vs, *args, es)
+        else:
+            kve.pyramid_step_layers_tokens(batch, ks, vs, *args, es)
+    torch.cuda.synchronize()
+    for l in range(2):
+        assert torch.equal(evas[l], evbs[l]), l
+        n = budgets[l]
+        for name in ("k", "v", "scores", "positions") + (("gumbel",) if kf else ()):
+            assert torch.equal(getattr(As[l], name)[:, :n], getattr(Bs[l], name)[:, :n]), \
+                (l, name)
+    if kf:
+        assert any(bool(((e >= 0) & (e < b)).any()) for e, b in zip(evas, budgets))

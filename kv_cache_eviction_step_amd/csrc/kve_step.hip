@@ -64,10 +64,15 @@ __device__ __forceinline__ uint64_t splitmix64_out(uint64_t z) {
 
 // Frozen Gumbel value of the row inserted at running position `pos` of
 // stream `stream`: counter hash -> uniform in (0,1) -> -log(-log u) in fp64.
-__device__ __noinline__ float gumbel_at(uint64_t seed, uint64_t stream, uint64_t pos) {
+// Inlined where it should overlap loads in flight (a call would wait for
+// them); called where inlining would put its constants in a loop's registers.
+__device__ __forceinline__ float gumbel_value(uint64_t seed, uint64_t stream, uint64_t pos) {
   uint64_t h = splitmix64_out(splitmix64_out(splitmix64_out(seed) ^ stream) ^ pos);
   double u = ((double)(h >> 11) + 0.5) * 0x1p-53;
   return (float)(-log(-log(u)));
+}
+__device__ __noinline__ float gumbel_at(uint64_t seed, uint64_t stream, uint64_t pos) {
+  return gumbel_value(seed, stream, pos);
 }
 
 // cos and sin of delta * freq: fp64 sincos, each rounded once to fp32 (the
@@ -84,14 +89,18 @@ __device__ __noinline__ f32x2 rotation_at(int32_t delta, double freq) {
 }
 
 // Annealed temperature (keyformer FIXED GAP #1), fp64, rounded once.
-__device__ __noinline__ float anneal_tau(double tau_init, double tau_end, int32_t steps,
-                                         int32_t pos) {
+__device__ __forceinline__ float tau_value(double tau_init, double tau_end, int32_t steps,
+                                           int32_t pos) {
 #pragma clang fp contract(off)
   if (steps <= 0 || tau_init == tau_end) return (float)tau_init;
   int32_t t = pos < steps ? pos : steps;
   double delta = (tau_end - tau_init) / (double)steps;
   double prod = (double)t * delta;
   return (float)(tau_init + prod);
+}
+__device__ __noinline__ float anneal_tau(double tau_init, double tau_end, int32_t steps,
+                                         int32_t pos) {
+  return tau_value(tau_init, tau_end, steps, pos);
 }
 
 // One RoPE pair rotated in fp32 with every product and sum rounded on its own.
@@ -361,8 +370,22 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   };
   // Two register buffers take turns (no copies, so the compiler waits only
   // for the batch being consumed while the next one is in flight).
+  // tau and the new row's Gumbel value (one token, not precomputed): inlined
+  // here so that they overlap the first key batch's loads.
+  float tau = 0.f, g_new = 0.f;
+  auto noise = [&]() {
+    if constexpr (!PRE) {
+      if (GUMBEL && over) tau = tau_value(sa.tau_init, sa.tau_end, sa.anneal_steps, la.pos);
+      if (GUMBEL)
+        g_new = gumbel_value(sa.seed, (uint64_t)(int64_t)(la.hh_base + hh),
+                             (uint64_t)(int64_t)la.pos);
+    }
+  };
+  if (iters > 0) load_batch(0, bufa);
+  __builtin_amdgcn_sched_barrier(0);            // issue the loads before the fp64 work
+  noise();
+  if constexpr (!PRE) asm volatile("" ::"v"(tau), "v"(g_new));   // evaluate here, not at the use
   if (iters > 0) {
-    load_batch(0, bufa);
     int it = 0;
     for (; it + 2 < iters; it += 2) {
       load_batch(it + 1, bufb);
@@ -416,14 +439,9 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   const float rz = 1.0f / (float)((double)z * (1.0 / (double)kZScale));
 
   // ---- C: new scores and the eviction choice --------------------------------
-  float tau = 0.f, g_new = 0.f;
   if constexpr (PRE) {
     if (GUMBEL) g_new = pre[D];
     if (GUMBEL && over) tau = pre[D + 1];
-  } else {
-    if (GUMBEL && over) tau = anneal_tau(sa.tau_init, sa.tau_end, sa.anneal_steps, la.pos);
-    if (GUMBEL)
-      g_new = gumbel_at(sa.seed, (uint64_t)(int64_t)(la.hh_base + hh), (uint64_t)(int64_t)la.pos);
   }
   // Candidates: rows n_sink .. n - recent of the n + 1 rows after the append
   // (sinks and the trailing window protected); the new row (index n) is one
@@ -625,6 +643,10 @@ __global__ __launch_bounds__(NT) void step_layers_kernel(const LayerArgs *__rest
   const int n_tokens = la.n_tokens;
   const int bh = (count < n_layers ? layers[count].block0 : (int)gridDim.x) - la.block0;
   stage_tables<D>(sa);
+  if (n_tokens == 1) {                          // nothing to share between tokens
+    step_body<D, NT, U, GUMBEL, false, R>(la, sa, hh, nullptr);
+    return;
+  }
   __syncthreads();                              // every wave reads lds_freq below
   // The per-token values, kTokChunk tokens at a time, in dynamic LDS past the
   // step's own arrays at their largest over this launch's tokens.

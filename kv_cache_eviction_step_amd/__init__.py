@@ -227,6 +227,11 @@ def _evicted_ptr(evicted, layer: Layer):
 
 
 def _stream_ptr(stream, layer: Layer):
+    """The stream handle, after checking that the layer lives on the current
+    device (the library launches there, and keeps its descriptor ring there)."""
+    if not layer.k.is_cuda or layer.k.get_device() != torch.cuda.current_device():
+        raise ValueError(f"layer tensors are on {layer.k.device}; calls run on the current "
+                         "GPU (use torch.cuda.device(...) to select it)")
     if stream is None:
         return torch.cuda.current_stream(layer.k.device).cuda_stream
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)

@@ -264,6 +264,20 @@ int batch_impl(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
     if (n_last > max_n) max_n = n_last;
   }
   if (blocks > INT32_MAX) return KVE_EINVAL;
+  // Two layers sharing cache memory (the same layer passed twice, say) would be
+  // stepped by two workgroups at once: reject overlapping key buffers.
+  if (n_layers > 1) {
+    int32_t order[kve::kMaxBatchLayers];
+    for (int32_t l = 0; l < n_layers; ++l) order[l] = l;
+    auto start = [&](int32_t l) { return reinterpret_cast<uintptr_t>(layers[l].k); };
+    std::sort(order, order + n_layers, [&](int32_t a, int32_t b) { return start(a) < start(b); });
+    for (int32_t i = 1; i < n_layers; ++i) {
+      const kve_layer &prev = layers[order[i - 1]];
+      const uintptr_t prev_end =
+          start(order[i - 1]) + (uintptr_t)prev.bh * (uintptr_t)prev.cap * (uintptr_t)prev.d * 2u;
+      if (start(order[i]) < prev_end) return KVE_EINVAL;
+    }
+  }
   const int dev_state = check_device();
   if (dev_state != KVE_OK) return dev_state;
   int dev = 0;

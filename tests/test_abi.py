@@ -188,16 +188,19 @@ def _batch_call(layers, ctrs, budgets, n=None, kf=True):
 
 
 @pytest.mark.parametrize("case", ["zero_layers", "too_many", "mixed_d", "one_bad_budget",
-                                  "one_bad_counter", "one_null_gumbel"])
+                                  "one_bad_counter", "one_null_gumbel", "same_layer_twice",
+                                  "overlapping_keys"])
 def test_batched_rejects_before_any_launch(case):
-    layers = [_layer() for _ in range(3)]
+    layer_bytes = 8 * 33 * 64 * 2
+    layers = [_layer(k=FAKE + i * layer_bytes) for i in range(3)]
     ctrs = [Counters(32, 100, 100) for _ in range(3)]
     budgets = [32, 32, 32]
     n = None
     if case == "zero_layers":
         n = 0
     elif case == "too_many":
-        layers, ctrs, budgets = [_layer()] * 129, [Counters(32, 100, 100)] * 129, [32] * 129
+        layers = [_layer(k=FAKE + i * layer_bytes) for i in range(129)]
+        ctrs, budgets = [Counters(32, 100, 100)] * 129, [32] * 129
     elif case == "mixed_d":
         layers[1] = _layer(d=128)
     elif case == "one_bad_budget":
@@ -206,6 +209,10 @@ def test_batched_rejects_before_any_launch(case):
         ctrs[1] = Counters(10, 50, 50)
     elif case == "one_null_gumbel":
         layers[0] = _layer(gumbel=None)
+    elif case == "same_layer_twice":
+        layers[2] = layers[0]
+    elif case == "overlapping_keys":
+        layers[1] = _layer(k=FAKE + layer_bytes - 256)      # last row of layer 0
     before = [(c.n_kept, c.next_pos, c.pos) for c in ctrs]
     rc, after = _batch_call(layers, ctrs, budgets, n)
     assert rc == kve.KVE_EINVAL
@@ -213,7 +220,7 @@ def test_batched_rejects_before_any_launch(case):
 
 
 def test_batched_pyramid_null_gumbel_passes_host_checks():
-    layers = [_layer(gumbel=None) for _ in range(2)]
+    layers = [_layer(gumbel=None, k=FAKE + i * 8 * 33 * 64 * 2) for i in range(2)]
     rc, after = _batch_call(layers, [Counters(32, 100, 100)] * 2, [32, 32], kf=False)
     if torch.cuda.is_available():
         pytest.skip("a GPU is present; the no-device path is not reachable")
@@ -252,7 +259,7 @@ def _policy_call(layers, ctrs, budgets, pol, n_tokens=1):
 def test_kve_step_rejects_before_any_launch(case):
     """kve_step checks its policy as init_keyformer_state does: sinks plus the
     recent window must leave room to evict within every layer's budget."""
-    layers = [_layer(), _layer()]
+    layers = [_layer(), _layer(k=FAKE + (1 << 20))]
     budgets = [32, 32]
     pol = kve.policy("keyformer", 4, recent=3, tau_init=1.0, tau_end=2.0, anneal_steps=64)
     n_layers, n_tokens = 1, 1
@@ -271,13 +278,13 @@ def test_kve_step_rejects_before_any_launch(case):
     elif case == "negative_tau_with_gumbel":
         pol.tau_init = -1.0
     elif case == "null_gumbel_with_noise":
-        layers = [_layer(gumbel=None), _layer()]
+        layers = [_layer(gumbel=None), _layer(k=FAKE + (1 << 20))]
     elif case == "tokens_129":
         n_tokens = 129
     ctrs = [Counters(32, 100, 100), Counters(32, 100, 100)]
     if case == "window_fills_budget_batched":
         ctrs = [Counters(40, 100, 100), Counters(20, 100, 100)]
-        layers = [_layer(cap=41), _layer(cap=41)]
+        layers = [_layer(cap=41), _layer(cap=41, k=FAKE + (1 << 20))]
     before = [(c.n_kept, c.next_pos, c.pos) for c in ctrs[:n_layers]]
     rc, after = _policy_call(layers[:n_layers], ctrs[:n_layers], budgets[:n_layers], pol, n_tokens)
     assert rc == kve.KVE_EINVAL
@@ -358,3 +365,14 @@ def test_byte_accounting_and_get_kv_views():
     with pytest.raises(ValueError):
         kve.fp16_bytes(-1, 64)
     assert kve.lib().kve_full_fp16_bytes(10, 0) == -1
+
+
+def test_binding_refuses_tensors_off_the_current_gpu():
+    """The library launches on the current device; the binding refuses a layer
+    whose tensors live elsewhere (here: host memory) before calling it."""
+    L = kve.Layer.empty(2, 9, 64, "cpu", gumbel=True)
+    k = torch.zeros(2, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="current"):
+        kve.keyformer_step(L, k, k, Counters(0, 0, 0), 8, 2, 1.0, 2.0, 8, 1e4, 0)
+    with pytest.raises(ValueError, match="current"):
+        kve.pyramid_step_tokens(L, k[None], k[None], Counters(0, 0, 0), 8, 2, 1e4)

@@ -315,7 +315,7 @@ int batch_impl(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
     return KVE_ELAUNCH;
   const hipError_t err =
       kve::launch_step_layers(reinterpret_cast<const kve::LayerArgs *>(dslot), n_layers,
-                              (int)blocks, max_n, sa, d, p.gumbel, s);
+                              (int)blocks, max_n, n_tokens, sa, d, p.gumbel, s);
   if (err != hipSuccess) return KVE_ELAUNCH;
   if (hipEventRecord(r.done[slot], s) != hipSuccess) return KVE_ELAUNCH;
   r.pending[slot] = true;

@@ -59,10 +59,15 @@ hipError_t launch_step(const LayerArgs &la, const SharedArgs &sa, int bh, int d,
                        hipStream_t stream);
 
 // Several layers and/or several tokens per launch: `layers` is device memory;
-// layer l steps layers[l].n_tokens tokens, token t reading its incoming rows at
-// new_k + t*bh*d and writing evicted + t*bh.
+// layer l steps layers[l].n_tokens tokens (n_tokens, the same for every
+// layer), token t reading its incoming rows at new_k + t*bh*d and writing
+// evicted + t*bh.
 hipError_t launch_step_layers(const LayerArgs *layers, int n_layers, int total_blocks,
-                              int max_n_prev, const SharedArgs &sa, int d, bool gumbel,
-                              hipStream_t stream);
+                              int max_n_prev, int n_tokens, const SharedArgs &sa, int d,
+                              bool gumbel, hipStream_t stream);
+
+// Whether such a launch reads the keys with ordinary (cached) loads rather
+// than non-temporal ones.
+bool reuse_keys(int total_blocks, int max_n_prev, int n_tokens, int d);
 
 }  // namespace kve

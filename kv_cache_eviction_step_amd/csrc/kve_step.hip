@@ -296,7 +296,7 @@ constexpr int kTokChunk = 16;
 // has run in this workgroup.  PRE: `pre` holds this token's per-token values
 // (above); otherwise the step evaluates them itself, each where no memory
 // access is in flight (a call there would wait for every outstanding load).
-template <int D, int NT, int U, bool GUMBEL, bool PRE, int R>
+template <int D, int NT, int U, bool GUMBEL, bool PRE, int R, bool REUSE>
 __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs &sa,
                                           const int hh, const float *pre) {
   constexpr int V16 = D / 8;        // 16-byte chunks per row
@@ -348,13 +348,19 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   float mx = -INFINITY;
   const int iters = (n + ROWS_IT - 1) / ROWS_IT;
   u32x4 bufa[U], bufb[U];
-  // Non-temporal loads: the key stream is read once per step and must not
-  // push the scores (written back at the end of the step) out of the caches.
+  // A single step reads the key stream once: non-temporal loads keep it from
+  // pushing the scores (written back at the end of the step) out of the
+  // caches.  When the same caches are stepped through several tokens and
+  // their keys fit in the last-level cache (REUSE), ordinary loads let the
+  // next token's pass hit there instead of HBM.
   auto load_batch = [&](int it, u32x4 *buf) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int r = min(it * ROWS_IT + u * RPS + rr, n - 1);
-      buf[u] = __builtin_nontemporal_load(K4 + (size_t)r * V16 + lr);
+      if constexpr (REUSE)
+        buf[u] = K4[(size_t)r * V16 + lr];
+      else
+        buf[u] = __builtin_nontemporal_load(K4 + (size_t)r * V16 + lr);
     }
   };
   auto consume = [&](int it, const u32x4 *buf) {
@@ -617,7 +623,7 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
 template <int D, int NT, int U, bool GUMBEL, int R>
 __global__ __launch_bounds__(NT) void step_kernel(LayerArgs la, SharedArgs sa) {
   stage_tables<D>(sa);
-  step_body<D, NT, U, GUMBEL, false, R>(la, sa, blockIdx.x, nullptr);
+  step_body<D, NT, U, GUMBEL, false, R, false>(la, sa, blockIdx.x, nullptr);
 }
 
 // Several layers and/or tokens per launch: the workgroups of layer l are
@@ -625,7 +631,7 @@ __global__ __launch_bounds__(NT) void step_kernel(LayerArgs la, SharedArgs sa) {
 // after the other (keyformer_update absorbs S tokens as S steps); between
 // tokens every store of the workgroup has landed and every wave has arrived,
 // so the next token reads the state the previous one left.
-template <int D, int NT, int U, bool GUMBEL, int R>
+template <int D, int NT, int U, bool GUMBEL, int R, bool REUSE>
 __global__ __launch_bounds__(NT) void step_layers_kernel(const LayerArgs *__restrict__ layers,
                                                          int n_layers, SharedArgs sa) {
   // layer of this workgroup: the number of layers starting at or before it,
@@ -643,8 +649,8 @@ __global__ __launch_bounds__(NT) void step_layers_kernel(const LayerArgs *__rest
   const int n_tokens = la.n_tokens;
   const int bh = (count < n_layers ? layers[count].block0 : (int)gridDim.x) - la.block0;
   stage_tables<D>(sa);
-  if (n_tokens == 1) {                          // nothing to share between tokens
-    step_body<D, NT, U, GUMBEL, false, R>(la, sa, hh, nullptr);
+  if (!REUSE && n_tokens == 1) {               // nothing to share between tokens
+    step_body<D, NT, U, GUMBEL, false, R, false>(la, sa, hh, nullptr);
     return;
   }
   __syncthreads();                              // every wave reads lds_freq below
@@ -691,7 +697,7 @@ __global__ __launch_bounds__(NT) void step_layers_kernel(const LayerArgs *__rest
     lt.new_k = reinterpret_cast<const char *>(la.new_k) + (size_t)t * bh * D * 2;
     lt.new_v = reinterpret_cast<const char *>(la.new_v) + (size_t)t * bh * D * 2;
     lt.evicted = la.evicted ? la.evicted + (size_t)t * bh : nullptr;
-    step_body<D, NT, U, GUMBEL, true, R>(lt, sa, hh_t, tab + (t % kTokChunk) * TAB);
+    step_body<D, NT, U, GUMBEL, true, R, REUSE>(lt, sa, hh_t, tab + (t % kTokChunk) * TAB);
     __builtin_amdgcn_s_waitcnt(0);              // this token's stores have landed
     __syncthreads();
   }
@@ -752,10 +758,10 @@ static hipError_t launch_d(const LayerArgs &la, const SharedArgs &sa, int bh,
   return launch_d_r<NT, D, GUMBEL, S::r2>(la, sa, bh, stream);
 }
 
-template <int NT, int D, bool GUMBEL, int R>
+template <int NT, int D, bool GUMBEL, int R, bool REUSE>
 static hipError_t launch_layers_d_r(const LayerArgs *layers, int n_layers, int total_blocks,
                                     int max_n_prev, const SharedArgs &sa, hipStream_t stream) {
-  auto kern = step_layers_kernel<D, NT, kUnroll, GUMBEL, R>;
+  auto kern = step_layers_kernel<D, NT, kUnroll, GUMBEL, R, REUSE>;
   const size_t lds = lds_bytes_for(max_n_prev) + (size_t)kTokChunk * (D + 2) * sizeof(float);
   hipError_t err = allow_lds(kern, lds);
   if (err != hipSuccess) return err;
@@ -763,19 +769,30 @@ static hipError_t launch_layers_d_r(const LayerArgs *layers, int n_layers, int t
   return hipGetLastError();
 }
 
+template <int NT, int D, bool GUMBEL, int R>
+static hipError_t launch_layers_d_r(const LayerArgs *layers, int n_layers, int total_blocks,
+                                    int max_n_prev, const SharedArgs &sa, bool reuse,
+                                    hipStream_t stream) {
+  return reuse ? launch_layers_d_r<NT, D, GUMBEL, R, true>(layers, n_layers, total_blocks,
+                                                          max_n_prev, sa, stream)
+               : launch_layers_d_r<NT, D, GUMBEL, R, false>(layers, n_layers, total_blocks,
+                                                           max_n_prev, sa, stream);
+}
+
 template <int NT, int D, bool GUMBEL>
 static hipError_t launch_layers_d(const LayerArgs *layers, int n_layers, int total_blocks,
-                                  int max_n_prev, const SharedArgs &sa, hipStream_t stream) {
+                                  int max_n_prev, const SharedArgs &sa, bool reuse,
+                                  hipStream_t stream) {
   using S = Slots<NT>;
   const int r = (max_n_prev + NT - 1) / NT;
   if (r <= S::r0)
     return launch_layers_d_r<NT, D, GUMBEL, S::r0>(layers, n_layers, total_blocks, max_n_prev,
-                                                   sa, stream);
+                                                   sa, reuse, stream);
   if (r <= S::r1)
     return launch_layers_d_r<NT, D, GUMBEL, S::r1>(layers, n_layers, total_blocks, max_n_prev,
-                                                   sa, stream);
+                                                   sa, reuse, stream);
   return launch_layers_d_r<NT, D, GUMBEL, S::r2>(layers, n_layers, total_blocks, max_n_prev, sa,
-                                                 stream);
+                                                 reuse, stream);
 }
 
 template <int NT>
@@ -791,16 +808,30 @@ static hipError_t launch_step_nt(const LayerArgs &la, const SharedArgs &sa, int 
 template <int NT>
 static hipError_t launch_layers_nt(const LayerArgs *layers, int n_layers, int total_blocks,
                                    int max_n_prev, const SharedArgs &sa, int d, bool gumbel,
-                                   hipStream_t stream) {
+                                   bool reuse, hipStream_t stream) {
   if (d == 128)
     return gumbel ? launch_layers_d<NT, 128, true>(layers, n_layers, total_blocks, max_n_prev, sa,
-                                                   stream)
+                                                   reuse, stream)
                   : launch_layers_d<NT, 128, false>(layers, n_layers, total_blocks, max_n_prev,
-                                                    sa, stream);
+                                                    sa, reuse, stream);
   return gumbel ? launch_layers_d<NT, 64, true>(layers, n_layers, total_blocks, max_n_prev, sa,
-                                                stream)
+                                                reuse, stream)
                 : launch_layers_d<NT, 64, false>(layers, n_layers, total_blocks, max_n_prev, sa,
-                                                 stream);
+                                                 reuse, stream);
+}
+
+// Whether a launch that steps its caches through several tokens should keep
+// their keys cached between tokens: the keys of the caches resident at once
+// (two workgroups on each of the 256 compute units) must fit in three
+// quarters of the 256 MB last-level (Infinity) cache, so that a cache's next
+// pass finds them there.  Larger footprints stream them non-temporally, as a
+// single token does.
+bool reuse_keys(int total_blocks, int max_n_prev, int n_tokens, int d) {
+  constexpr int64_t kResidentBlocks = 2 * 256;
+  constexpr int64_t kReuseBytes = (int64_t)192 << 20;
+  if (n_tokens < 2) return false;
+  const int64_t resident = total_blocks < kResidentBlocks ? total_blocks : kResidentBlocks;
+  return resident * (int64_t)max_n_prev * d * 2 <= kReuseBytes;
 }
 
 hipError_t launch_step(const LayerArgs &la, const SharedArgs &sa, int bh, int d, bool gumbel,
@@ -809,10 +840,10 @@ hipError_t launch_step(const LayerArgs &la, const SharedArgs &sa, int bh, int d,
 }
 
 hipError_t launch_step_layers(const LayerArgs *layers, int n_layers, int total_blocks,
-                              int max_n_prev, const SharedArgs &sa, int d, bool gumbel,
-                              hipStream_t stream) {
+                              int max_n_prev, int n_tokens, const SharedArgs &sa, int d,
+                              bool gumbel, hipStream_t stream) {
   return launch_layers_nt<kThreads>(layers, n_layers, total_blocks, max_n_prev, sa, d, gumbel,
-                                    stream);
+                                    reuse_keys(total_blocks, max_n_prev, n_tokens, d), stream);
 }
 
 }  // namespace kve

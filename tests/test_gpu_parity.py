@@ -751,19 +751,17 @@ def test_policy_plain_equals_named_entry_points(dev):
             assert torch.equal(getattr(A, name)[:, :budget], getattr(B, name)[:, :budget]), name
 
 
-@pytest.mark.parametrize("kind", ["kf", "pk"])
-def test_layers_tokens_large_budgets_equal_single_calls(dev, kind):
-    """The token-loop kernel with 8 and 24 score slots per thread (budgets 2000
-    and 5000, from full synthetic states): one launch of two layers x 16 tokens
-    gives the same bits as single-token calls per layer."""
+def _layers_tokens_equal_single_calls(dev, kind, shapes, T, S, seed):
+    """Two layers (bh, budget, hh_base) from full synthetic states stepped T
+    tokens, S per launch of the token-loop kernel, give the same bits as
+    single-token calls per layer."""
     import kv_cache_eviction_step_amd as kve
     from gpu_harness import bulk_state
     kf = kind == "kf"
-    shapes = [(3, 2000, 0), (2, 5000, 11)]                # bh, budget, hh_base
-    T, S, d, pos0 = 40, 16, 128, 9000
-    _say(f"[large layers*tokens==single] kind={kind} budgets={[x[1] for x in shapes]} T={T}")
+    d, pos0 = 128, 9000
+    _say(f"[layers*tokens==single] kind={kind} shapes={shapes} T={T} S={S}")
     gen = torch.Generator(device=dev)
-    gen.manual_seed(57)
+    gen.manual_seed(seed)
     As, Bs, nks, nvs, evas, evbs = [], [], [], [], [], []
     for bh, budget, hb in shapes:
         w = synth.Workload("lg", 1, 1, bh, d, pos0, T, budget, 4, "keyformer" if kf else "pyramid",
@@ -805,3 +803,19 @@ def test_layers_tokens_large_budgets_equal_single_calls(dev, kind):
                 (l, name)
     if kf:
         assert any(bool(((e >= 0) & (e < b)).any()) for e, b in zip(evas, budgets))
+
+
+@pytest.mark.parametrize("kind", ["kf", "pk"])
+def test_layers_tokens_large_budgets_equal_single_calls(dev, kind):
+    """The token loop with 8 and 24 score slots per thread (budgets 2000 and
+    5000); the five caches hold 4 MB of keys, which the launch reads cached."""
+    _layers_tokens_equal_single_calls(dev, kind, [(3, 2000, 0), (2, 5000, 11)], 40, 16, 57)
+
+
+@pytest.mark.parametrize("kind", ["kf", "pk"])
+def test_layers_tokens_streamed_keys_equal_single_calls(dev, kind):
+    """512 caches of 1536 and 2048 rows, all resident at once: 235 MB of
+    keys (268 MB by the launch's bound, 512 caches x 2048 rows), more than
+    the 192 MB a launch keeps cached between tokens, so the token loop streams
+    them non-temporally."""
+    _layers_tokens_equal_single_calls(dev, kind, [(256, 2048, 0), (256, 1536, 256)], 24, 12, 58)

@@ -54,6 +54,9 @@ def parse():
                     help="protect the last R rows from eviction (kve_step)")
     ap.add_argument("--tova", action="store_true",
                     help="TOVA-adapted scoring (current-step weight; kve_step)")
+    ap.add_argument("--whole-run", action="store_true",
+                    help="time the whole trajectory instead (prompt + decode from empty "
+                         "caches, token by token; --steps / --warmup / --fill unused)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the CPU oracle baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -122,12 +125,13 @@ def copy_calibration():
                                            "dispatches": 5}}), flush=True)
 
 
-def step_bytes(kind: str, n: int, d: int, m):
+def step_bytes(kind: str, n: int, d: int, m, over: bool = True):
     """Algorithmic bytes of one cache-step (m may be an array).  TOVA-adapted
     ("tova") moves the PyramidKV bytes minus the 4n-byte read of the old
-    scores; the caller subtracts that."""
+    scores; the caller subtracts that.  A Keyformer step under its budget
+    (`over` false: nothing is evicted) reads no Gumbel values."""
     if kind == "keyformer":
-        return 2 * n * d + 12 * n + 8 * d + 12 + m * (8 * d + 24)
+        return 2 * n * d + (12 if over else 8) * n + 8 * d + 12 + m * (8 * d + 24)
     return 2 * n * d + 8 * n + 8 * d + 8 + m * (8 * d + 16)
 
 
@@ -207,7 +211,7 @@ def main():
         # depths (a transient that moves half the cache per step).  Warm up
         # past it; the JSON reports the warmup used.
         args.warmup = -(-w.recent // TPC) * TPC
-    if TPC < 1 or TPC > 128 or args.steps % TPC or args.warmup % TPC:
+    if TPC < 1 or TPC > 128 or (not args.whole_run and (args.steps % TPC or args.warmup % TPC)):
         print("--tokens-per-call must be 1..128 and divide --steps and --warmup",
               file=sys.stderr)
         sys.exit(2)
@@ -280,6 +284,11 @@ def main():
         else:
             singles[l].ctrs[0] = c
 
+    stream = torch.cuda.current_stream(dev)
+    if args.whole_run:
+        whole_run(args, w, budgets, bh, L, d, TPC, call, ctr, batch, entry, stream, gen, dev)
+        return
+
     # ---- reach the steady state (untimed) ------------------------------------
     t_fill = time.time()
     if args.fill == "synthetic":
@@ -315,7 +324,6 @@ def main():
 
     for s0 in range(0, args.warmup, TPC):
         call(nk, nv, s0, TPC)
-    stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
@@ -341,27 +349,36 @@ def main():
             if w.kind == "tova":                # the old scores are not read
                 total_bytes -= 4 * n * bh
     launches = (args.steps // TPC) * (1 if batch is not None else L)
-    sec = ms / 1e3
-    updates = bh * L * args.steps
-    avg_launch_s = sec / launches
-    bytes_per_launch = total_bytes / launches
-    achieved = bytes_per_launch / avg_launch_s / 1e9
     mean_m = float(np.where(evn >= 0, np.maximum(0, n_prev[:, :, None] - evn), 0).mean())
 
     kernel = "step_layers_kernel" if batch is not None or TPC > 1 else "step_kernel"
-    mode = launch_mode(args.batched, TPC)
+    traffic = measured_traffic(w.name, kernel, launch_mode(args.batched, TPC))
+    out = result_line(args, w, budgets, bh, L, d, TPC, batch, entry, args.steps, args.warmup,
+                      ms, launches, total_bytes, mean_m, traffic, kernel)
+    out["config"]["steady_state_fill"] = args.fill
+    out["config"]["fill_seconds"] = round(t_fill, 1)
+    print(json.dumps(out), flush=True)
+
+
+def result_line(args, w, budgets, bh, L, d, TPC, batch, entry, steps, warmup, ms, launches,
+                total_bytes, mean_m, traffic, kernel):
+    """The JSON result (without the fill fields), CPU baseline included."""
+    kf = w.kind == "keyformer"
+    sec = ms / 1e3
+    avg_launch_s = sec / launches
+    bytes_per_launch = total_bytes / launches
+    achieved = bytes_per_launch / avg_launch_s / 1e9
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(w, budgets, args.cpu_seconds)
-
-    out = {
+    return {
         "metric": "cache-row updates/sec (B·L·H·tokens) and achieved HBM GB/s vs peak, 1 GPU",
-        "value": updates / sec,
+        "value": bh * L * steps / sec,
         "unit": "cache-row updates/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms / args.steps,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms / steps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -375,21 +392,79 @@ def main():
             "policy": {"score": "current (TOVA)" if w.kind == "tova" else "cumulative",
                        "gumbel": kf, "recent": w.recent, "n_sink": w.n_sink},
             "kv_storage": "f16", "bh_per_launch": bh, "layers": L,
-            "budgets": [budgets[0], budgets[-1]], "steady_state_fill": args.fill,
-            "fill_seconds": round(t_fill, 1), "mean_rows_moved_per_cache_step": mean_m,
+            "budgets": [budgets[0], budgets[-1]],
+            "mean_rows_moved_per_cache_step": mean_m,
             "launch": (f"one launch per {TPC} token(s) "
                        f"{'over all layers' if batch is not None else 'per layer'} ({entry})"),
             "tokens_per_launch": TPC, "layers_per_launch": L if batch is not None else 1,
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(w.name, kernel, mode),
+            "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
             "kernel": "kve::" + kernel,
             "avg_launch_us": avg_launch_s * 1e6,
             "algorithmic_bytes_per_launch": bytes_per_launch,
         },
         "cpu_baseline": cpu,
     }
+
+
+def whole_run(args, w, budgets, bh, L, d, TPC, call, ctr, batch, entry, stream, gen, dev):
+    """The whole trajectory -- every prompt token appended one by one, then the
+    decode tokens -- from empty caches.  Inputs are generated on the device 64
+    tokens (all layers) at a time, between the timed parts: HIP events bracket
+    each chunk's launches and the chunks' times are summed."""
+    import numpy as np
+    import torch
+    import synth
+    T = w.tokens
+    chunk = -(-64 // TPC) * TPC
+    ins_k = torch.empty((L, chunk, bh, d), dtype=torch.float16, device=dev)
+    ins_v = torch.empty_like(ins_k)
+    ev = torch.empty((L, chunk, bh), dtype=torch.int32, device=dev)
+    bud = np.asarray(budgets, dtype=np.int64)
+    marks, m_sums, n_all = [], [], []
+    launches = 0
+    for t0 in range(0, T, chunk):
+        cnt = min(chunk, T - t0)
+        for l in range(L):
+            synth.bulk_kv_torch(w, t0, cnt, bh, gen, dev, out_k=ins_k[l, :cnt],
+                                out_v=ins_v[l, :cnt])
+        n_prev = np.zeros((cnt, L), dtype=np.int64)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for s0 in range(0, cnt, TPC):
+            S = min(TPC, cnt - s0)
+            nk0 = np.fromiter((ctr(l).n_kept for l in range(L)), dtype=np.int64, count=L)
+            n_prev[s0:s0 + S] = np.minimum(nk0[None, :] + np.arange(S)[:, None], bud[None, :])
+            call(ins_k, ins_v, s0, S, ev[:, s0:s0 + S])
+            launches += 1 if batch is not None else L
+        b.record(stream)
+        marks.append((a, b))
+        # rows moved per (layer, token), summed over the caches (outside the events)
+        npt = torch.from_numpy(np.ascontiguousarray(n_prev.T)).to(dev)[:, :, None]
+        e = ev[:, :cnt].to(torch.int64)
+        m_sums.append(torch.where((e >= 0) & (e < npt), npt - e, 0).sum(dim=2).cpu().numpy())
+        n_all.append(n_prev.T.copy())
+    torch.cuda.synchronize()
+    ms = sum(x.elapsed_time(y) for x, y in marks)
+    n_prev = np.concatenate(n_all, axis=1)                 # [L, T]
+    m_sum = np.concatenate(m_sums, axis=1)                 # [L, T]
+    over = n_prev + 1 > bud[:, None]
+    base = step_bytes(w.kind, n_prev, d, 0, over=True)
+    if w.kind == "keyformer":
+        base = np.where(over, base, step_bytes(w.kind, n_prev, d, 0, over=False))
+    total_bytes = int((base * bh).sum()) + int((m_sum * (8 * d + (24 if w.kind == "keyformer"
+                                                                    else 16))).sum())
+    if w.kind == "tova":
+        total_bytes -= int((4 * n_prev * bh).sum())
+    mean_m = float(m_sum.sum() / (L * T * bh))
+    kernel = "step_layers_kernel" if batch is not None or TPC > 1 else "step_kernel"
+    out = result_line(args, w, budgets, bh, L, d, TPC, batch, entry, T, 0, ms, launches,
+                      total_bytes, mean_m, None, kernel)
+    out["config"]["timing"] = (f"whole run: {w.prompt} prompt + {w.decode} decode tokens from "
+                               f"empty caches, HIP events around the launches of each "
+                               f"{chunk}-token chunk, summed")
     print(json.dumps(out), flush=True)
 
 

@@ -525,10 +525,15 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   // c+1 reads only rows after every row chunk c writes, and chunk c is stored
   // only after every wave's loads of chunk c have landed (wait + barrier).
   // Loads are issued unconditionally (row index clamped to the last source
-  // row) so that the explicit wait counts are exact.
+  // row) so that the explicit wait counts are exact.  The vector-memory
+  // counter retires loads and stores in issue order, so once chunk c-1's
+  // stores sit between chunk c's loads and chunk c+1's, waiting for chunk c
+  // leaves those stores (and chunk c+1's loads) in flight: a chunk never
+  // waits for the previous chunk's stores to be acknowledged.
   if (e >= 0 && e < n - 1) {
     constexpr int CH = RPM * UM;
     constexpr int LOADS = 4 * UM;               // per thread per chunk
+    constexpr int STORES = 4 * UM;              // per thread per full chunk
     const int last = n - 2;                     // last destination row
     float cs[8], sn[8];
 #pragma unroll
@@ -538,52 +543,93 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
     }
     u32x4 ak1[UM], ak2[UM], av1[UM], av2[UM];
     u32x4 bk1[UM], bk2[UM], bv1[UM], bv2[UM];
+    // 32-bit byte offsets from the cache's first row (a cache is at most
+    // kMaxRows + 1 rows of 2D bytes): one address register per access, on
+    // top of the cache's uniform base.
+    gptr<char> const Kc = reinterpret_cast<gptr<char>>(Kw);
+    gptr<char> const Vc = reinterpret_cast<gptr<char>>(Vw);
+    auto at = [](gptr<char> base, uint32_t off) {
+      return reinterpret_cast<gptr<u32x4>>(base + off);
+    };
+    // Moved rows are next read by the next step's key pass.  Unless that
+    // pass can find them in the last-level cache (REUSE), the move streams
+    // them non-temporally, like the key pass itself (measured: 3 % faster
+    // launches where interior evictions are common).
+    auto ld = [](gptr<u32x4> p) {
+      if constexpr (REUSE)
+        return *p;
+      else
+        return __builtin_nontemporal_load(p);
+    };
+    auto st = [](u32x4 x, gptr<u32x4> p) {
+      if constexpr (REUSE)
+        *p = x;
+      else
+        __builtin_nontemporal_store(x, p);
+    };
     auto load_chunk = [&](int d0, u32x4 *k1, u32x4 *k2, u32x4 *v1, u32x4 *v2) {
 #pragma unroll
       for (int u = 0; u < UM; ++u) {
-        const size_t src = (size_t)(min(d0 + rm + u * RPM, last) + 1) * V16;
-        k1[u] = Kw[src + lm];
-        k2[u] = Kw[src + lm + V16 / 2];
-        v1[u] = Vw[src + lm];
-        v2[u] = Vw[src + lm + V16 / 2];
+        const uint32_t src = (uint32_t)(min(d0 + rm + u * RPM, last) + 1) * (2 * D) + lm * 16;
+        k1[u] = ld(at(Kc, src));
+        k2[u] = ld(at(Kc, src + D));
+        v1[u] = ld(at(Vc, src));
+        v2[u] = ld(at(Vc, src + D));
       }
     };
-    auto store_chunk = [&](int d0, u32x4 *k1, u32x4 *k2, const u32x4 *v1, const u32x4 *v2) {
+    // `full`: every row of the chunk is a destination (all chunks but the
+    // last), so the stores need no guard; an unguarded store is never skipped,
+    // which keeps the count of stores in flight exact for the wait above it.
+    auto store_chunk = [&](int d0, u32x4 *k1, u32x4 *k2, const u32x4 *v1, const u32x4 *v2,
+                           bool full) {
 #pragma unroll
       for (int u = 0; u < UM; ++u) rotate_chunk(k1[u], k2[u], cs, sn);
       __syncthreads();                          // every wave's loads of this chunk landed
 #pragma unroll
       for (int u = 0; u < UM; ++u) {
         const int dst = d0 + rm + u * RPM;
-        if (dst <= last) {
-          const size_t o = (size_t)dst * V16;
-          Kw[o + lm] = k1[u];
-          Kw[o + lm + V16 / 2] = k2[u];
-          Vw[o + lm] = v1[u];
-          Vw[o + lm + V16 / 2] = v2[u];
+        if (full || dst <= last) {
+          const uint32_t o = (uint32_t)dst * (2 * D) + lm * 16;
+          st(k1[u], at(Kc, o));
+          st(k2[u], at(Kc, o + D));
+          st(v1[u], at(Vc, o));
+          st(v2[u], at(Vc, o + D));
         }
       }
     };
     int d0 = e;
     load_chunk(d0, ak1, ak2, av1, av2);
-    while (true) {
+    // first chunk: nothing stored yet, only the next chunk's loads stay
+    const bool more = d0 + CH <= last;
+    if (more) {
+      load_chunk(d0 + CH, bk1, bk2, bv1, bv2);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));     // chunk d0 landed, next in flight
+      store_chunk(d0, ak1, ak2, av1, av2, true);
+      d0 += CH;
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+      store_chunk(d0, ak1, ak2, av1, av2, false);
+    }
+    // later chunks (every chunk before the last is full, so every wave issued
+    // STORES stores for it): the previous chunk's stores may stay in flight
+    while (more) {
       if (d0 + CH <= last) {
-        load_chunk(d0 + CH, bk1, bk2, bv1, bv2);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));   // chunk d0 landed, next in flight
-        store_chunk(d0, ak1, ak2, av1, av2);
+        load_chunk(d0 + CH, ak1, ak2, av1, av2);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(STORES + LOADS));
+        store_chunk(d0, bk1, bk2, bv1, bv2, true);
       } else {
         __builtin_amdgcn_s_waitcnt(0);
-        store_chunk(d0, ak1, ak2, av1, av2);
+        store_chunk(d0, bk1, bk2, bv1, bv2, false);
         break;
       }
       d0 += CH;
       if (d0 + CH <= last) {
-        load_chunk(d0 + CH, ak1, ak2, av1, av2);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
-        store_chunk(d0, bk1, bk2, bv1, bv2);
+        load_chunk(d0 + CH, bk1, bk2, bv1, bv2);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(STORES + LOADS));
+        store_chunk(d0, ak1, ak2, av1, av2, true);
       } else {
         __builtin_amdgcn_s_waitcnt(0);
-        store_chunk(d0, bk1, bk2, bv1, bv2);
+        store_chunk(d0, ak1, ak2, av1, av2, false);
         break;
       }
       d0 += CH;

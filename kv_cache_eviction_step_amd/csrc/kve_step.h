@@ -45,6 +45,7 @@ struct SharedArgs {
   int32_t recent;          // trailing rows never evicted (0 = off)
   int32_t current;         // 1: score = this step's weight (TOVA), 0: += (H2O / Keyformer)
   int32_t anneal_steps;
+  int32_t early;           // 1: load the old scores before the key pass (set per launch)
   double tau_init;
   double tau_end;
   uint64_t seed;

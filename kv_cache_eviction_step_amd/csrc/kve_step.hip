@@ -387,6 +387,33 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
                              (uint64_t)(int64_t)la.pos);
     }
   };
+  // The old scores (and, when evicting, Gumbel values) of this thread's rows.
+  // In a launch whose workgroups each have a compute unit to themselves the
+  // step is a latency chain, and loading them before the key pass hides their
+  // latency (with at most 8 slots per thread: larger caches need the registers
+  // for the key pass).  Otherwise they are loaded after it, overlapping the
+  // normaliser: a launch that streams HBM at full rate runs no faster for the
+  // early loads, and measured 1.7 % slower with the key stream cached.  A slot
+  // is read only for i < n (and only under the condition it was loaded under).
+  const bool early = R <= 8 && sa.early != 0;
+  float sreg[R], greg[R];
+  auto load_state = [&]() {
+    if (!current) {
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const int i = tid + k * NT;
+        if (i < n) sreg[k] = scores[row0 + i];
+      }
+    }
+    if (GUMBEL && over) {
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const int i = tid + k * NT;
+        if (i < n) greg[k] = gumbel[row0 + i];
+      }
+    }
+  };
+  if (early) load_state();
   if (iters > 0) load_batch(0, bufa);
   __builtin_amdgcn_sched_barrier(0);            // issue the loads before the fp64 work
   noise();
@@ -408,24 +435,7 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
     }
   }
 
-  // The old scores (and, when evicting, Gumbel values) of this thread's rows:
-  // their loads overlap the normaliser below.  A slot is read only for i < n
-  // (and only under the condition it was loaded under).
-  float sreg[R], greg[R];
-  if (!current) {
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-      const int i = tid + k * NT;
-      if (i < n) sreg[k] = scores[row0 + i];
-    }
-  }
-  if (GUMBEL && over) {
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-      const int i = tid + k * NT;
-      if (i < n) greg[k] = gumbel[row0 + i];
-    }
-  }
+  if (!early) load_state();
 
   // ---- B: softmax normaliser ------------------------------------------------
   mx = wave_max(mx);
@@ -762,6 +772,10 @@ __global__ __launch_bounds__(NT) void step_layers_kernel(const LayerArgs *__rest
 #endif
 constexpr int kThreads = KVE_THREADS;
 constexpr int kUnroll = KVE_UNROLL;
+// MI355X: 256 compute units, each holding two of these workgroups at once.  A
+// launch is a latency chain per cache when no compute unit holds more than
+// one of its workgroups.
+constexpr int kComputeUnits = 256;
 
 static size_t lds_bytes_for(int n_prev) {
   const size_t np = (size_t)((n_prev + 63) & ~63) + 64;
@@ -873,21 +887,25 @@ static hipError_t launch_layers_nt(const LayerArgs *layers, int n_layers, int to
 // pass finds them there.  Larger footprints stream them non-temporally, as a
 // single token does.
 bool reuse_keys(int total_blocks, int max_n_prev, int n_tokens, int d) {
-  constexpr int64_t kResidentBlocks = 2 * 256;
+  constexpr int64_t kResidentBlocks = 2 * kComputeUnits;
   constexpr int64_t kReuseBytes = (int64_t)192 << 20;
   if (n_tokens < 2) return false;
   const int64_t resident = total_blocks < kResidentBlocks ? total_blocks : kResidentBlocks;
   return resident * (int64_t)max_n_prev * d * 2 <= kReuseBytes;
 }
 
-hipError_t launch_step(const LayerArgs &la, const SharedArgs &sa, int bh, int d, bool gumbel,
+hipError_t launch_step(const LayerArgs &la, const SharedArgs &sa_in, int bh, int d, bool gumbel,
                        hipStream_t stream) {
+  SharedArgs sa = sa_in;
+  sa.early = bh <= kComputeUnits;
   return launch_step_nt<kThreads>(la, sa, bh, d, gumbel, stream);
 }
 
 hipError_t launch_step_layers(const LayerArgs *layers, int n_layers, int total_blocks,
-                              int max_n_prev, int n_tokens, const SharedArgs &sa, int d,
+                              int max_n_prev, int n_tokens, const SharedArgs &sa_in, int d,
                               bool gumbel, hipStream_t stream) {
+  SharedArgs sa = sa_in;
+  sa.early = total_blocks <= kComputeUnits;
   return launch_layers_nt<kThreads>(layers, n_layers, total_blocks, max_n_prev, sa, d, gumbel,
                                     reuse_keys(total_blocks, max_n_prev, n_tokens, d), stream);
 }

@@ -3,12 +3,13 @@
 // One workgroup owns one cache (one (batch, kv-head) of the layer) for the
 // whole step, so no cross-workgroup synchronisation or scratch memory is
 // needed.  Phases inside the workgroup:
-//   A  score pass: coalesced non-temporal 128-bit loads of the stored keys, fp16 dot2
-//      products against the incoming key, 16-lane DPP reduction per row,
+//   A  score pass: coalesced 128-bit loads of the stored keys (non-temporal,
+//      or cached in a token loop whose keys fit the last-level cache), fp16
+//      dot2 products against the incoming key, 16-lane DPP reduction per row,
 //      logits to LDS (a matrix-vector product: bandwidth bound, no MFMA);
 //   B  softmax: block max, exponentials and an exact (fixed-point) block sum;
-//      meanwhile each thread loads the old scores / gumbel of its rows into
-//      registers;
+//      each thread holds the old scores / gumbel of its rows in registers,
+//      loaded before the score pass in latency-bound launches, else here;
 //   C  new scores (fp32 add of the normalised mass, or the mass itself for
 //      TOVA) and, when over budget, the eviction key  fma(tau, gumbel, score)
 //      over the non-protected rows with a block argmin that breaks ties
@@ -374,8 +375,6 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
       }
     }
   };
-  // Two register buffers take turns (no copies, so the compiler waits only
-  // for the batch being consumed while the next one is in flight).
   // tau and the new row's Gumbel value (one token, not precomputed): inlined
   // here so that they overlap the first key batch's loads.
   float tau = 0.f, g_new = 0.f;
@@ -418,6 +417,8 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   __builtin_amdgcn_sched_barrier(0);            // issue the loads before the fp64 work
   noise();
   if constexpr (!PRE) asm volatile("" ::"v"(tau), "v"(g_new));   // evaluate here, not at the use
+  // Two register buffers take turns (no copies, so the compiler waits only
+  // for the batch being consumed while the next one is in flight).
   if (iters > 0) {
     int it = 0;
     for (; it + 2 < iters; it += 2) {
@@ -650,8 +651,10 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   // or nowhere (it was the one evicted)
   const int f = e < 0 ? n : (e < n ? n - 1 : -1);
   if (f >= 0 && tid < LPM) {
-    const gptr<const u32x4> nk = global(reinterpret_cast<const u32x4 *>(la.new_k)) + (size_t)hh * V16;
-    const gptr<const u32x4> nv = global(reinterpret_cast<const u32x4 *>(la.new_v)) + (size_t)hh * V16;
+    const gptr<const u32x4> nk =
+        global(reinterpret_cast<const u32x4 *>(la.new_k)) + (size_t)hh * V16;
+    const gptr<const u32x4> nv =
+        global(reinterpret_cast<const u32x4 *>(la.new_v)) + (size_t)hh * V16;
     u32x4 k1 = nk[lm], k2 = nk[lm + V16 / 2];
     if (e >= 0) {                                // moved: rotate to position f
       float cs[8], sn[8];        // written above by this same wave, or before the token
@@ -683,10 +686,11 @@ __global__ __launch_bounds__(NT) void step_kernel(LayerArgs la, SharedArgs sa) {
 }
 
 // Several layers and/or tokens per launch: the workgroups of layer l are
-// block0(l) .. block0(l+1)-1; layer descriptors live in device memory.  A workgroup steps its cache through the layer's tokens one
-// after the other (keyformer_update absorbs S tokens as S steps); between
-// tokens every store of the workgroup has landed and every wave has arrived,
-// so the next token reads the state the previous one left.
+// block0(l) .. block0(l+1)-1; layer descriptors live in device memory.  A
+// workgroup steps its cache through the layer's tokens one after the other
+// (keyformer_update absorbs S tokens as S steps); between tokens every store
+// of the workgroup has landed and every wave has arrived, so the next token
+// reads the state the previous one left.
 template <int D, int NT, int U, bool GUMBEL, int R, bool REUSE>
 __global__ __launch_bounds__(NT) void step_layers_kernel(const LayerArgs *__restrict__ layers,
                                                          int n_layers, SharedArgs sa) {

@@ -819,3 +819,61 @@ def test_layers_tokens_streamed_keys_equal_single_calls(dev, kind):
     the 192 MB a launch keeps cached between tokens, so the token loop streams
     them non-temporally."""
     _layers_tokens_equal_single_calls(dev, kind, [(256, 2048, 0), (256, 1536, 256)], 24, 12, 58)
+
+
+@pytest.mark.parametrize("kind", ["kf", "pk"])
+@pytest.mark.parametrize("budget", [1000, 3000])
+@pytest.mark.parametrize("S", [1, 16])
+def test_launch_size_paths_agree(dev, kind, budget, S):
+    """A launch's grid size picks code paths that must not change any bit:
+    320 caches in one launch (more workgroups than compute units: state loads
+    after the key pass; at budget 3000 with S = 16, keys streamed) against
+    the same caches in two launches of 160 (state loads before the key pass;
+    keys cached between tokens), from a full synthetic state."""
+    import kv_cache_eviction_step_amd as kve
+    from gpu_harness import bulk_state
+    kf = kind == "kf"
+    bh, half, d, T, pos0 = 320, 160, 128, 32, 7000
+    _say(f"[grid paths] kind={kind} budget={budget} S={S} bh={bh} vs 2x{half} T={T}")
+    w = synth.Workload("grid", 1, 1, bh, d, pos0, T, budget, 4, "keyformer" if kf else "pyramid",
+                       1.0 if kf else 0.0, 2.0 if kf else 0.0, 64 if kf else 0)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(61 + budget + S)
+    A = kve.Layer.empty(bh, budget + 1, d, dev, gumbel=kf)
+    bulk_state(A, budget, w, gen)
+    parts = []
+    for i in range(2):
+        sl = slice(i * half, (i + 1) * half)
+        parts.append(kve.Layer(A.k[sl].clone(), A.v[sl].clone(), A.scores[sl].clone(),
+                               A.gumbel[sl].clone() if kf else None, A.positions[sl].clone(),
+                               hh_base=i * half))
+    nk, nv = synth.bulk_kv_torch(w, pos0, T, bh, gen, dev)
+    ev_a = torch.full((T, bh), -9, dtype=torch.int32, device=dev)
+    ev_p = [torch.full((T, half), -9, dtype=torch.int32, device=dev) for _ in range(2)]
+    args = (4, 1.0, 2.0, 64, 1e4, 5) if kf else (4, 1e4)
+
+    def run(L, ks, vs, ev, c):
+        for t0 in range(0, T, S):
+            if S == 1 and kf:
+                kve.keyformer_step(L, ks[t0], vs[t0], c, budget, *args, ev[t0])
+            elif S == 1:
+                kve.pyramid_step(L, ks[t0], vs[t0], c, budget, *args, ev[t0])
+            elif kf:
+                kve.keyformer_step_tokens(L, ks[t0:t0 + S], vs[t0:t0 + S], c, budget, *args,
+                                          ev[t0:t0 + S])
+            else:
+                kve.pyramid_step_tokens(L, ks[t0:t0 + S], vs[t0:t0 + S], c, budget, *args,
+                                        ev[t0:t0 + S])
+
+    run(A, nk, nv, ev_a, kve.Counters(budget, pos0, pos0))
+    for i in range(2):
+        sl = slice(i * half, (i + 1) * half)
+        run(parts[i], nk[:, sl].contiguous(), nv[:, sl].contiguous(), ev_p[i],
+            kve.Counters(budget, pos0, pos0))
+    torch.cuda.synchronize()
+    assert torch.equal(ev_a, torch.cat(ev_p, dim=1))
+    for name in ("k", "v", "scores", "positions") + (("gumbel",) if kf else ()):
+        joined = torch.cat([getattr(p, name) for p in parts])
+        assert torch.equal(getattr(A, name)[:, :budget], joined[:, :budget]), name
+    if kf:
+        assert bool(((ev_a >= 0) & (ev_a < budget)).any())     # interior evictions happened

@@ -345,6 +345,10 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   const int lr = tid % LPR;
   const int rr = tid / LPR;
   const u32x4 q = global(reinterpret_cast<const u32x4 *>(la.new_k))[(size_t)hh * V16 + lr];
+  // The incoming row's value chunk `lr` (lanes 0..LPR-1 store the row at the
+  // end of the step): loaded now, so that no load is left for the step's end.
+  u32x4 v_new = {};
+  if (tid < LPR) v_new = global(reinterpret_cast<const u32x4 *>(la.new_v))[(size_t)hh * V16 + lr];
   const float scale = sa.scale;
   float mx = -INFINITY;
   const int iters = (n + ROWS_IT - 1) / ROWS_IT;
@@ -648,28 +652,32 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   }
 
   // the new row at its final slot: n (no eviction), n-1 (an older row left),
-  // or nowhere (it was the one evicted)
+  // or nowhere (it was the one evicted).  Lane c < LPR stores chunk c: the key
+  // chunk it already holds in q (with lr == c), rotated when the row moved
+  // together with its RoPE partner chunk c ^ (LPR/2), which lane c ^ (LPR/2)
+  // holds; and the value chunk loaded at the start.
   const int f = e < 0 ? n : (e < n ? n - 1 : -1);
-  if (f >= 0 && tid < LPM) {
-    const gptr<const u32x4> nk =
-        global(reinterpret_cast<const u32x4 *>(la.new_k)) + (size_t)hh * V16;
-    const gptr<const u32x4> nv =
-        global(reinterpret_cast<const u32x4 *>(la.new_v)) + (size_t)hh * V16;
-    u32x4 k1 = nk[lm], k2 = nk[lm + V16 / 2];
-    if (e >= 0) {                                // moved: rotate to position f
-      float cs[8], sn[8];        // written above by this same wave, or before the token
+  u32x4 k_new = q;
+  if (f >= 0 && e >= 0 && wave == 0) {          // partner chunks (whole wave: shuffles)
+    u32x4 other;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        cs[j] = rot_c[lm * 8 + j];
-        sn[j] = rot_s[lm * 8 + j];
-      }
-      rotate_chunk(k1, k2, cs, sn);
+    for (int w = 0; w < 4; ++w) other[w] = __shfl_xor(q[w], LPR / 2);
+    const int c = lane & (LPR / 2 - 1);         // pair block of the first half
+    float cs[8], sn[8];          // written above by this same wave, or before the token
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      cs[j] = rot_c[c * 8 + j];
+      sn[j] = rot_s[c * 8 + j];
     }
+    const bool first = (lane & (LPR / 2)) == 0;
+    u32x4 x1 = first ? q : other, x2 = first ? other : q;
+    rotate_chunk(x1, x2, cs, sn);
+    k_new = first ? x1 : x2;
+  }
+  if (f >= 0 && tid < LPR) {
     const size_t o = (size_t)f * V16;
-    Kw[o + lm] = k1;
-    Kw[o + lm + V16 / 2] = k2;
-    Vw[o + lm] = nv[lm];
-    Vw[o + lm + V16 / 2] = nv[lm + V16 / 2];
+    Kw[o + tid] = k_new;
+    Vw[o + tid] = v_new;
     if (tid == 0) {
       scores[row0 + f] = 0.0f;
       if constexpr (GUMBEL) gumbel[row0 + f] = g_new;

@@ -160,13 +160,28 @@ __device__ __forceinline__ float dot8(const u32x4 a, const u32x4 b) {
 }
 
 template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, x)));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+  const uint32_t lo = (uint32_t)dpp_i<CTRL>((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)dpp_i<CTRL>((int)(uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
 }
 
+// In-row butterfly of the reductions below, one DPP move per step (a VALU
+// operation, no LDS traffic): quad_perm [1,0,3,2] and [2,3,0,1] (0xB1, 0x4E:
+// partners 1 and 2 lanes away), then half-row mirror (0x141: lane i <-> 7-i of
+// each 8) and row mirror (0x140: lane i <-> 15-i of each 16).  After the
+// first k steps every lane holds the combination over its aligned group of
+// 2^k lanes (k <= 4), for any associative and commutative combination.
+
 // Sum over aligned groups of LANES lanes (8 or 16); every lane gets the sum.
-// quad_perm [1,0,3,2] and [2,3,0,1], then half-row mirror, then row mirror.
 template <int LANES>
 __device__ __forceinline__ float group_sum(float x) {
   x += dpp<0xB1>(x);
@@ -176,12 +191,32 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+__device__ __forceinline__ float lane_f(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+__device__ __forceinline__ uint64_t lane_u64(uint64_t x, int l) {
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
 }
 
+// Whole-wave reductions, result uniform across the wave: the in-row butterfly
+// (every lane of a row of 16 then holds its row's result), then the four row
+// results read from lanes 0, 16, 32, 48 and combined.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x141>(x));
+  x = fmaxf(x, dpp<0x140>(x));
+  return fmaxf(fmaxf(lane_f(x, 0), lane_f(x, 16)), fmaxf(lane_f(x, 32), lane_f(x, 48)));
+}
+
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t x) {
+  x += dpp_u64<0xB1>(x);
+  x += dpp_u64<0x4E>(x);
+  x += dpp_u64<0x141>(x);
+  x += dpp_u64<0x140>(x);
+  return lane_u64(x, 0) + lane_u64(x, 16) + lane_u64(x, 32) + lane_u64(x, 48);
+}
 
 // (value, index) pairs: smaller value wins, equal values go to the lower index.
 __device__ __forceinline__ void argmin_merge(float &v, int &i, float v2, int i2) {
@@ -190,40 +225,53 @@ __device__ __forceinline__ void argmin_merge(float &v, int &i, float v2, int i2)
     i = i2;
   }
 }
-
+template <int CTRL>
+__device__ __forceinline__ void argmin_dpp(float &v, int &i) {
+  argmin_merge(v, i, dpp<CTRL>(v), dpp_i<CTRL>(i));
+}
 __device__ __forceinline__ void wave_argmin(float &v, int &i) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    float v2 = __shfl_xor(v, o);
-    int i2 = __shfl_xor(i, o);
-    argmin_merge(v, i, v2, i2);
-  }
+  argmin_dpp<0xB1>(v, i);
+  argmin_dpp<0x4E>(v, i);
+  argmin_dpp<0x141>(v, i);
+  argmin_dpp<0x140>(v, i);
+  float bv = lane_f(v, 0);
+  int bi = __builtin_amdgcn_readlane(i, 0);
+  argmin_merge(bv, bi, lane_f(v, 16), __builtin_amdgcn_readlane(i, 16));
+  argmin_merge(bv, bi, lane_f(v, 32), __builtin_amdgcn_readlane(i, 32));
+  argmin_merge(bv, bi, lane_f(v, 48), __builtin_amdgcn_readlane(i, 48));
+  v = bv;
+  i = bi;
 }
 
 // Reductions of the W per-wave partials held by lanes 0..W-1 (identity
-// elsewhere), done by every wave on its own: the last log2(W) steps of the
-// butterflies above (the earlier ones only meet identities), then lane 0's
-// value, uniform across the wave.
-__device__ __forceinline__ float first_lane(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
-}
+// elsewhere), done by every wave on its own: the first log2(W) steps of the
+// in-row butterfly, then lane 0's value, uniform across the wave.
 template <int W>
 __device__ __forceinline__ float partials_max(float x) {
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return first_lane(x);
+  static_assert(W >= 1 && W <= 16 && (W & (W - 1)) == 0, "partials");
+  if constexpr (W > 1) x = fmaxf(x, dpp<0xB1>(x));
+  if constexpr (W > 2) x = fmaxf(x, dpp<0x4E>(x));
+  if constexpr (W > 4) x = fmaxf(x, dpp<0x141>(x));
+  if constexpr (W > 8) x = fmaxf(x, dpp<0x140>(x));
+  return lane_f(x, 0);
 }
 template <int W>
 __device__ __forceinline__ uint64_t partials_sum(uint64_t x) {
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32)) << 32) |
-         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)x);
+  static_assert(W >= 1 && W <= 16 && (W & (W - 1)) == 0, "partials");
+  if constexpr (W > 1) x += dpp_u64<0xB1>(x);
+  if constexpr (W > 2) x += dpp_u64<0x4E>(x);
+  if constexpr (W > 4) x += dpp_u64<0x141>(x);
+  if constexpr (W > 8) x += dpp_u64<0x140>(x);
+  return lane_u64(x, 0);
 }
-__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+template <int W>
+__device__ __forceinline__ int partials_argmin(float v, int i) {
+  static_assert(W >= 1 && W <= 16 && (W & (W - 1)) == 0, "partials");
+  if constexpr (W > 1) argmin_dpp<0xB1>(v, i);
+  if constexpr (W > 2) argmin_dpp<0x4E>(v, i);
+  if constexpr (W > 4) argmin_dpp<0x141>(v, i);
+  if constexpr (W > 8) argmin_dpp<0x140>(v, i);
+  return __builtin_amdgcn_readlane(i, 0);
 }
 
 // The softmax normaliser is summed exactly: each weight w in [0, 1] as the
@@ -231,16 +279,6 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t x) {
 // total does not depend on how rows are grouped over lanes and waves (the
 // workgroup size), and carries no float rounding of its own.
 constexpr float kZScale = 0x1p40f;
-template <int W>
-__device__ __forceinline__ int partials_argmin(float v, int i) {
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) {
-    float v2 = __shfl_xor(v, o);
-    int i2 = __shfl_xor(i, o);
-    argmin_merge(v, i, v2, i2);
-  }
-  return __builtin_amdgcn_readfirstlane(i);
-}
 
 // ---------------------------------------------------------------------------
 // the kernel

@@ -821,6 +821,7 @@ __global__ __launch_bounds__(NT) void step_layers_kernel(const LayerArgs *__rest
 #define KVE_UNROLL 8
 #endif
 constexpr int kThreads = KVE_THREADS;
+constexpr int kWideThreads = 2 * KVE_THREADS;
 constexpr int kUnroll = KVE_UNROLL;
 // MI355X: 256 compute units, each holding two of these workgroups at once.  A
 // launch is a latency chain per cache when no compute unit holds more than
@@ -879,30 +880,19 @@ static hipError_t launch_layers_d_r(const LayerArgs *layers, int n_layers, int t
   return hipGetLastError();
 }
 
-template <int NT, int D, bool GUMBEL, int R>
-static hipError_t launch_layers_d_r(const LayerArgs *layers, int n_layers, int total_blocks,
-                                    int max_n_prev, const SharedArgs &sa, bool reuse,
-                                    hipStream_t stream) {
-  return reuse ? launch_layers_d_r<NT, D, GUMBEL, R, true>(layers, n_layers, total_blocks,
-                                                          max_n_prev, sa, stream)
-               : launch_layers_d_r<NT, D, GUMBEL, R, false>(layers, n_layers, total_blocks,
-                                                           max_n_prev, sa, stream);
-}
-
-template <int NT, int D, bool GUMBEL>
+template <int NT, int D, bool GUMBEL, bool REUSE>
 static hipError_t launch_layers_d(const LayerArgs *layers, int n_layers, int total_blocks,
-                                  int max_n_prev, const SharedArgs &sa, bool reuse,
-                                  hipStream_t stream) {
+                                  int max_n_prev, const SharedArgs &sa, hipStream_t stream) {
   using S = Slots<NT>;
   const int r = (max_n_prev + NT - 1) / NT;
   if (r <= S::r0)
-    return launch_layers_d_r<NT, D, GUMBEL, S::r0>(layers, n_layers, total_blocks, max_n_prev,
-                                                   sa, reuse, stream);
+    return launch_layers_d_r<NT, D, GUMBEL, S::r0, REUSE>(layers, n_layers, total_blocks,
+                                                          max_n_prev, sa, stream);
   if (r <= S::r1)
-    return launch_layers_d_r<NT, D, GUMBEL, S::r1>(layers, n_layers, total_blocks, max_n_prev,
-                                                   sa, reuse, stream);
-  return launch_layers_d_r<NT, D, GUMBEL, S::r2>(layers, n_layers, total_blocks, max_n_prev, sa,
-                                                 reuse, stream);
+    return launch_layers_d_r<NT, D, GUMBEL, S::r1, REUSE>(layers, n_layers, total_blocks,
+                                                          max_n_prev, sa, stream);
+  return launch_layers_d_r<NT, D, GUMBEL, S::r2, REUSE>(layers, n_layers, total_blocks,
+                                                        max_n_prev, sa, stream);
 }
 
 template <int NT>
@@ -915,19 +905,19 @@ static hipError_t launch_step_nt(const LayerArgs &la, const SharedArgs &sa, int 
                 : launch_d<NT, 64, false>(la, sa, bh, stream);
 }
 
-template <int NT>
+template <int NT, bool REUSE>
 static hipError_t launch_layers_nt(const LayerArgs *layers, int n_layers, int total_blocks,
                                    int max_n_prev, const SharedArgs &sa, int d, bool gumbel,
-                                   bool reuse, hipStream_t stream) {
+                                   hipStream_t stream) {
   if (d == 128)
-    return gumbel ? launch_layers_d<NT, 128, true>(layers, n_layers, total_blocks, max_n_prev, sa,
-                                                   reuse, stream)
-                  : launch_layers_d<NT, 128, false>(layers, n_layers, total_blocks, max_n_prev,
-                                                    sa, reuse, stream);
-  return gumbel ? launch_layers_d<NT, 64, true>(layers, n_layers, total_blocks, max_n_prev, sa,
-                                                reuse, stream)
-                : launch_layers_d<NT, 64, false>(layers, n_layers, total_blocks, max_n_prev, sa,
-                                                 reuse, stream);
+    return gumbel ? launch_layers_d<NT, 128, true, REUSE>(layers, n_layers, total_blocks,
+                                                          max_n_prev, sa, stream)
+                  : launch_layers_d<NT, 128, false, REUSE>(layers, n_layers, total_blocks,
+                                                           max_n_prev, sa, stream);
+  return gumbel ? launch_layers_d<NT, 64, true, REUSE>(layers, n_layers, total_blocks, max_n_prev,
+                                                       sa, stream)
+                : launch_layers_d<NT, 64, false, REUSE>(layers, n_layers, total_blocks,
+                                                        max_n_prev, sa, stream);
 }
 
 // Whether a launch that steps its caches through several tokens should keep
@@ -956,8 +946,18 @@ hipError_t launch_step_layers(const LayerArgs *layers, int n_layers, int total_b
                               bool gumbel, hipStream_t stream) {
   SharedArgs sa = sa_in;
   sa.early = total_blocks <= kComputeUnits;
-  return launch_layers_nt<kThreads>(layers, n_layers, total_blocks, max_n_prev, sa, d, gumbel,
-                                    reuse_keys(total_blocks, max_n_prev, n_tokens, d), stream);
+  if (!reuse_keys(total_blocks, max_n_prev, n_tokens, d))
+    return launch_layers_nt<kThreads, false>(layers, n_layers, total_blocks, max_n_prev, sa, d,
+                                             gumbel, stream);
+  // A cached token loop with more workgroups than the GPU holds at once:
+  // 1024-thread workgroups (one per compute unit, twice the key bytes in
+  // flight per cache) walk their caches' tokens faster.  Fewer, latency-bound
+  // workgroups keep 512 threads, whose reductions are shorter.
+  if (total_blocks > 2 * kComputeUnits)
+    return launch_layers_nt<kWideThreads, true>(layers, n_layers, total_blocks, max_n_prev, sa, d,
+                                                gumbel, stream);
+  return launch_layers_nt<kThreads, true>(layers, n_layers, total_blocks, max_n_prev, sa, d,
+                                          gumbel, stream);
 }
 
 }  // namespace kve

@@ -813,6 +813,14 @@ def test_layers_tokens_large_budgets_equal_single_calls(dev, kind):
 
 
 @pytest.mark.parametrize("kind", ["kf", "pk"])
+def test_layers_tokens_wide_workgroups_equal_single_calls(dev, kind):
+    """600 caches of 600 and 400 rows: 79 MB of keys resident at once, so the
+    launch keeps them cached between tokens, and with more workgroups than the
+    GPU holds at once it runs 1024-thread workgroups."""
+    _layers_tokens_equal_single_calls(dev, kind, [(300, 600, 0), (300, 400, 300)], 24, 12, 59)
+
+
+@pytest.mark.parametrize("kind", ["kf", "pk"])
 def test_layers_tokens_streamed_keys_equal_single_calls(dev, kind):
     """512 caches of 1536 and 2048 rows, all resident at once: 235 MB of
     keys (268 MB by the launch's bound, 512 caches x 2048 rows), more than

@@ -82,6 +82,28 @@ def oracle_samples(w: synth.Workload, layer: int, hhs, budget: int, T: int, cap:
         return list(ex.map(_sample_job, jobs))
 
 
+def oracle_samples_layers(w: synth.Workload, picks: dict, budgets, T: int, init_n: bool,
+                          next_pos: int = 0) -> dict:
+    """oracle_samples for several layers at once (one pool): picks[l] lists the
+    sampled caches of layer l, budgets[l] its budget; init_n: start full."""
+    jobs, keys = [], []
+    for l, hhs in picks.items():
+        for hh in hhs:
+            jobs.append((w, l, hh, budgets[l], T, budgets[l] + 1,
+                         budgets[l] if init_n else None, next_pos))
+            keys.append(l)
+    workers = min(len(jobs), max(1, min(16, (os.cpu_count() or 2) - 1)))
+    if workers <= 1:
+        res = [_sample_job(j) for j in jobs]
+    else:
+        with ProcessPoolExecutor(workers) as ex:
+            res = list(ex.map(_sample_job, jobs))
+    out: dict = {}
+    for l, smp in zip(keys, res):
+        out.setdefault(l, []).append(smp)
+    return out
+
+
 def load_state_into(layer, hh: int, st: dict) -> None:
     """Copy an oracle snapshot into row hh of a GPU layer."""
     n = st["n"]
@@ -218,10 +240,11 @@ def run_layer(w: synth.Workload, layer_idx: int, budget: int, T: int, samples: l
 
 
 def run_batched(w: synth.Workload, layer_ids, budgets, T: int, samples: dict, init_n, next_pos,
-                device, gen_seed: int = 99):
-    """Step several layers together (one batched launch per token) on the GPU.
-    samples[l] lists the oracle samples of layer position l.  Returns
-    (layers, evicted log [T, L, bh] numpy)."""
+                device, gen_seed: int = 99, tokens_per_call: int = 1):
+    """Step several layers together on the GPU: one batched launch per token,
+    or per `tokens_per_call` tokens (*_step_layers_tokens).  samples[l] lists
+    the oracle samples of layer position l.  Returns (layers, evicted log
+    [T, L, bh] numpy, batch)."""
     import kv_cache_eviction_step_amd as kve
     kf = w.kind == "keyformer"
     gen = torch.Generator(device=device)
@@ -247,12 +270,30 @@ def run_batched(w: synth.Workload, layer_ids, budgets, T: int, samples: dict, in
             nv[:, li, s.hh] = torch.from_numpy(s.vs.view(np.float16)).to(device)
     ev = torch.full((T, len(budgets), w.bh), -7, dtype=torch.int32, device=device)
     prm = params_for(w, budgets[0], 0)
-    for t in range(T):
-        if kf:
-            kve.keyformer_step_layers(batch, nk[t], nv[t], w.n_sink, prm.tau_init, prm.tau_end,
-                                      prm.anneal_steps, w.rope_base, w.gumbel_seed, ev[t])
-        else:
-            kve.pyramid_step_layers(batch, nk[t], nv[t], w.n_sink, w.rope_base, ev[t])
+    S = tokens_per_call
+    if S > 1:
+        # [L, T, bh, d]: each layer's run of tokens is one contiguous block
+        nkl, nvl = nk.transpose(0, 1).contiguous(), nv.transpose(0, 1).contiguous()
+        evl = torch.full((len(budgets), T, w.bh), -7, dtype=torch.int32, device=device)
+        for t0 in range(0, T, S):
+            n = min(S, T - t0)
+            ks, vs, es = nkl[:, t0:t0 + n], nvl[:, t0:t0 + n], evl[:, t0:t0 + n]
+            if kf:
+                kve.keyformer_step_layers_tokens(batch, ks, vs, w.n_sink, prm.tau_init,
+                                                 prm.tau_end, prm.anneal_steps, w.rope_base,
+                                                 w.gumbel_seed, es, n_tokens=n)
+            else:
+                kve.pyramid_step_layers_tokens(batch, ks, vs, w.n_sink, w.rope_base, es,
+                                               n_tokens=n)
+        ev = evl.transpose(0, 1)
+    else:
+        for t in range(T):
+            if kf:
+                kve.keyformer_step_layers(batch, nk[t], nv[t], w.n_sink, prm.tau_init,
+                                          prm.tau_end, prm.anneal_steps, w.rope_base,
+                                          w.gumbel_seed, ev[t])
+            else:
+                kve.pyramid_step_layers(batch, nk[t], nv[t], w.n_sink, w.rope_base, ev[t])
     torch.cuda.synchronize(device)
     _ = layer_ids
     return layers, ev.cpu().numpy(), batch

@@ -14,7 +14,8 @@ import torch
 
 import oracle
 import synth
-from gpu_harness import (Sample, compare_cache, load_state_into, oracle_samples, policy_for,
+from gpu_harness import (Sample, compare_cache, load_state_into, oracle_samples,
+                         oracle_samples_layers, policy_for,
                          random_state,
                          run_batched, run_layer)
 from oracle.guard import guarded_trajectory, params_for
@@ -343,6 +344,43 @@ def test_full_size_batched_all_layers_late_riser(dev):
                                  next_pos=next_pos) for l, hhs in picks.items()}
     layers, ev, _ = run_batched(w, list(range(w.layers)), [w.budget] * w.layers, T, samples,
                                 w.budget, next_pos, dev)
+    errs = []
+    for l, ss in samples.items():
+        for s in ss:
+            errs += compare_cache(layers[l], s.hh, s, ev[:, l, s.hh], next_pos)
+    assert not errs, "\n".join(errs[:20])
+
+
+def test_full_size_tokens_late_riser_every_layer(dev):
+    """The 8B-shaped workload as the bench times it best: all 32 layers x 32
+    tokens in one launch (keys cached between tokens, 1024-thread
+    workgroups), one sampled cache per layer spread over batch and head."""
+    w = synth.WORKLOADS[3]
+    T, next_pos = 32, w.prompt
+    picks = {l: [(7 + 37 * l) % w.bh] for l in range(w.layers)}
+    _say(f"[full-tokens] {w.name} layers={w.layers} bh={w.bh} one cache per layer T={T} S={T}")
+    samples = oracle_samples_layers(w, picks, [w.budget] * w.layers, T, True, next_pos)
+    layers, ev, _ = run_batched(w, list(range(w.layers)), [w.budget] * w.layers, T, samples,
+                                w.budget, next_pos, dev, tokens_per_call=T)
+    errs = []
+    for l, ss in samples.items():
+        for s in ss:
+            errs += compare_cache(layers[l], s.hh, s, ev[:, l, s.hh], next_pos)
+    assert not errs, "\n".join(errs[:20])
+    assert any(((ev[:, l] >= 0) & (ev[:, l] < w.budget)).any() for l in range(w.layers))
+
+
+def test_full_size_tokens_long_context_every_layer(dev):
+    """The long-context workload, all 32 layers (budgets 6144 .. 2048) x 16
+    tokens in one launch (keys streamed), one sampled cache per layer."""
+    w = synth.WORKLOADS[4]
+    budgets = oracle.pyramid_budgets(w.layers, w.budget, w.n_sink, w.beta)
+    T, next_pos = 16, w.prompt
+    picks = {l: [(11 + 53 * l) % w.bh] for l in range(w.layers)}
+    _say(f"[full-tokens] {w.name} layers={w.layers} bh={w.bh} one cache per layer T={T} S={T}")
+    samples = oracle_samples_layers(w, picks, budgets, T, True, next_pos)
+    layers, ev, _ = run_batched(w, list(range(w.layers)), budgets, T, samples, 1, next_pos, dev,
+                                tokens_per_call=T)
     errs = []
     for l, ss in samples.items():
         for s in ss:

@@ -27,8 +27,9 @@ def hipcc() -> str:
     return "hipcc"
 
 
-# Every kernel must keep two 512-thread workgroups per compute unit (4 waves
-# per SIMD, i.e. at most 128 VGPRs) and must not spill VGPRs to scratch memory.
+# Every kernel must keep two 512-thread workgroups (or one 1024-thread
+# workgroup) per compute unit (4 waves per SIMD, i.e. at most 128 VGPRs) and
+# must not spill VGPRs to scratch memory.
 MIN_WAVES_PER_SIMD = 4
 
 

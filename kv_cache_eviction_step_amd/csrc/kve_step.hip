@@ -946,18 +946,21 @@ hipError_t launch_step_layers(const LayerArgs *layers, int n_layers, int total_b
                               bool gumbel, hipStream_t stream) {
   SharedArgs sa = sa_in;
   sa.early = total_blocks <= kComputeUnits;
-  if (!reuse_keys(total_blocks, max_n_prev, n_tokens, d))
-    return launch_layers_nt<kThreads, false>(layers, n_layers, total_blocks, max_n_prev, sa, d,
-                                             gumbel, stream);
-  // A cached token loop with more workgroups than the GPU holds at once:
-  // 1024-thread workgroups (one per compute unit, twice the key bytes in
-  // flight per cache) walk their caches' tokens faster.  Fewer, latency-bound
-  // workgroups keep 512 threads, whose reductions are shorter.
-  if (total_blocks > 2 * kComputeUnits)
-    return launch_layers_nt<kWideThreads, true>(layers, n_layers, total_blocks, max_n_prev, sa, d,
-                                                gumbel, stream);
-  return launch_layers_nt<kThreads, true>(layers, n_layers, total_blocks, max_n_prev, sa, d,
-                                          gumbel, stream);
+  const bool reuse = reuse_keys(total_blocks, max_n_prev, n_tokens, d);
+  // A token loop that fills the GPU (at least as many workgroups as it holds
+  // of 512 threads) walks its caches' tokens faster with 1024-thread
+  // workgroups: one per compute unit, twice the key bytes in flight per
+  // cache.  Fewer, latency-bound workgroups, and single tokens, keep 512
+  // threads, whose reductions are shorter.
+  if (n_tokens > 1 && total_blocks >= 2 * kComputeUnits)
+    return reuse ? launch_layers_nt<kWideThreads, true>(layers, n_layers, total_blocks,
+                                                        max_n_prev, sa, d, gumbel, stream)
+                 : launch_layers_nt<kWideThreads, false>(layers, n_layers, total_blocks,
+                                                         max_n_prev, sa, d, gumbel, stream);
+  return reuse ? launch_layers_nt<kThreads, true>(layers, n_layers, total_blocks, max_n_prev, sa,
+                                                  d, gumbel, stream)
+               : launch_layers_nt<kThreads, false>(layers, n_layers, total_blocks, max_n_prev, sa,
+                                                   d, gumbel, stream);
 }
 
 }  // namespace kve

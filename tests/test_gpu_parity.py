@@ -372,7 +372,8 @@ def test_full_size_tokens_late_riser_every_layer(dev):
 
 def test_full_size_tokens_long_context_every_layer(dev):
     """The long-context workload, all 32 layers (budgets 6144 .. 2048) x 16
-    tokens in one launch (keys streamed), one sampled cache per layer."""
+    tokens in one launch (keys streamed, 1024-thread workgroups), one sampled
+    cache per layer."""
     w = synth.WORKLOADS[4]
     budgets = oracle.pyramid_budgets(w.layers, w.budget, w.n_sink, w.beta)
     T, next_pos = 16, w.prompt
@@ -863,7 +864,7 @@ def test_layers_tokens_streamed_keys_equal_single_calls(dev, kind):
     """512 caches of 1536 and 2048 rows, all resident at once: 235 MB of
     keys (268 MB by the launch's bound, 512 caches x 2048 rows), more than
     the 192 MB a launch keeps cached between tokens, so the token loop streams
-    them non-temporally."""
+    them non-temporally (and, filling the GPU, runs 1024-thread workgroups)."""
     _layers_tokens_equal_single_calls(dev, kind, [(256, 2048, 0), (256, 1536, 256)], 24, 12, 58)
 
 

@@ -790,15 +790,15 @@ def test_policy_plain_equals_named_entry_points(dev):
             assert torch.equal(getattr(A, name)[:, :budget], getattr(B, name)[:, :budget]), name
 
 
-def _layers_tokens_equal_single_calls(dev, kind, shapes, T, S, seed):
+def _layers_tokens_equal_single_calls(dev, kind, shapes, T, S, seed, d=128):
     """Two layers (bh, budget, hh_base) from full synthetic states stepped T
     tokens, S per launch of the token-loop kernel, give the same bits as
     single-token calls per layer."""
     import kv_cache_eviction_step_amd as kve
     from gpu_harness import bulk_state
     kf = kind == "kf"
-    d, pos0 = 128, 9000
-    _say(f"[layers*tokens==single] kind={kind} shapes={shapes} T={T} S={S}")
+    pos0 = 9000
+    _say(f"[layers*tokens==single] kind={kind} d={d} shapes={shapes} T={T} S={S}")
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
     As, Bs, nks, nvs, evas, evbs = [], [], [], [], [], []
@@ -852,11 +852,13 @@ def test_layers_tokens_large_budgets_equal_single_calls(dev, kind):
 
 
 @pytest.mark.parametrize("kind", ["kf", "pk"])
-def test_layers_tokens_wide_workgroups_equal_single_calls(dev, kind):
-    """600 caches of 600 and 400 rows: 79 MB of keys resident at once, so the
-    launch keeps them cached between tokens, and with more workgroups than the
-    GPU holds at once it runs 1024-thread workgroups."""
-    _layers_tokens_equal_single_calls(dev, kind, [(300, 600, 0), (300, 400, 300)], 24, 12, 59)
+@pytest.mark.parametrize("d", [128, 64])
+def test_layers_tokens_wide_workgroups_equal_single_calls(dev, kind, d):
+    """600 caches of 600 and 400 rows: at most 79 MB of keys resident at once,
+    so the launch keeps them cached between tokens, and with more workgroups
+    than the GPU holds at once it runs 1024-thread workgroups."""
+    _layers_tokens_equal_single_calls(dev, kind, [(300, 600, 0), (300, 400, 300)], 24, 12, 59,
+                                      d=d)
 
 
 @pytest.mark.parametrize("kind", ["kf", "pk"])

@@ -151,7 +151,7 @@ __device__ __forceinline__ void rotate_chunk(u32x4 &x1, u32x4 &x2, const float *
   x2 = y2;
 }
 
-// 8 fp16 products accumulated in fp32 (v_dot2_f32_f16).
+// 8 fp16 products of one 16-byte chunk accumulated in fp32 (v_dot2_f32_f16).
 __device__ __forceinline__ float dot8(const u32x4 a, const u32x4 b) {
   float acc = 0.f;
 #pragma unroll
@@ -181,12 +181,13 @@ __device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
 // first k steps every lane holds the combination over its aligned group of
 // 2^k lanes (k <= 4), for any associative and commutative combination.
 
-// Sum over aligned groups of LANES lanes (8 or 16); every lane gets the sum.
+// Sum over aligned groups of LANES lanes (4, 8 or 16); every lane gets the sum.
 template <int LANES>
 __device__ __forceinline__ float group_sum(float x) {
+  static_assert(LANES == 4 || LANES == 8 || LANES == 16, "group");
   x += dpp<0xB1>(x);
   x += dpp<0x4E>(x);
-  x += dpp<0x141>(x);
+  if constexpr (LANES >= 8) x += dpp<0x141>(x);
   if constexpr (LANES == 16) x += dpp<0x140>(x);
   return x;
 }
@@ -339,14 +340,25 @@ template <int D, int NT, int U, bool GUMBEL, bool PRE, int R, bool REUSE>
 __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs &sa,
                                           const int hh, const float *pre) {
   constexpr int V16 = D / 8;        // 16-byte chunks per row
-  constexpr int LPR = D / 8;        // score pass: lanes per row (one chunk each)
+  // Score pass: CPL chunks of a row per lane -- two, one RoPE pair, at 512
+  // threads (less reduction work per byte, which a latency-bound workgroup
+  // feels); one at 1024 threads (measured faster there) -- LPR lanes per row.
+  // Either way a logit is the same sum, so results do not depend on it: the
+  // 8-product partial of every chunk, each pair's two partials added (chunks
+  // c and c + D/16), then the pairs combined by the in-row butterfly.  With
+  // one chunk per lane (lane c reads chunk c), a first step adds the partner
+  // lane c ^ (D/16), and the butterfly over the pairs follows.
+  constexpr int CPL = NT >= 1024 ? 1 : 2;
+  constexpr int LPR = V16 / CPL;
   constexpr int RPS = NT / LPR;     // score pass: rows per sweep
-  constexpr int ROWS_IT = RPS * U;  // score pass: rows per batch of loads
+  constexpr int UR = U / CPL;       // score pass: rows per lane per batch
+  constexpr int ROWS_IT = RPS * UR; // score pass: rows per batch of loads
   constexpr int LPM = D / 16;       // move pass: lanes per row (one chunk of each half)
   constexpr int RPM = NT / LPM;     // move pass: rows per sweep
   constexpr int UM = KVE_MOVE_UNROLL; // move pass: sweeps per chunk
   constexpr int NWAVE = NT / 64;
-  static_assert(NT % 64 == 0 && RPS * LPR == NT && RPM * LPM == NT, "launch shape");
+  static_assert(NT % 64 == 0 && RPS * LPR == NT && RPM * LPM == NT && U % CPL == 0,
+                "launch shape");
 
   // LDS: logits -> weights [np].  Scores and Gumbel values of the rows
   // i = tid + k*NT, k < R (R*NT >= n), live in this thread's registers.
@@ -376,17 +388,24 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   const bool current = sa.current != 0;
 
   // ---- A: logits of every stored row against the incoming key -------------
-  // Two batches of U loads in flight: batch it+1 is issued before batch it
-  // is consumed.  Rows past n are clamped to row n-1 (a cache hit) and dropped.
+  // Lane lr of a row's LPR lanes holds the 16-byte chunks chunk_of(c), c <
+  // CPL (each load instruction reads whole 128-byte lines).  Two batches of U
+  // loads in flight: batch it+1 is issued before batch it is consumed.  Rows
+  // past n are clamped to row n-1 (a cache hit) and dropped.
   const gptr<const u32x4> __restrict__ K4 =
       global(reinterpret_cast<const u32x4 *>(la.k)) + row0 * V16;
   const int lr = tid % LPR;
   const int rr = tid / LPR;
-  const u32x4 q = global(reinterpret_cast<const u32x4 *>(la.new_k))[(size_t)hh * V16 + lr];
-  // The incoming row's value chunk `lr` (lanes 0..LPR-1 store the row at the
+  auto chunk_of = [&](int c) { return lr + c * LPR; };
+  const gptr<const u32x4> nk4 =
+      global(reinterpret_cast<const u32x4 *>(la.new_k)) + (size_t)hh * V16;
+  u32x4 q[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) q[c] = nk4[chunk_of(c)];
+  // The incoming row's value chunk `tid` (lanes 0..V16-1 store the row at the
   // end of the step): loaded now, so that no load is left for the step's end.
   u32x4 v_new = {};
-  if (tid < LPR) v_new = global(reinterpret_cast<const u32x4 *>(la.new_v))[(size_t)hh * V16 + lr];
+  if (tid < V16) v_new = global(reinterpret_cast<const u32x4 *>(la.new_v))[(size_t)hh * V16 + tid];
   const float scale = sa.scale;
   float mx = -INFINITY;
   const int iters = (n + ROWS_IT - 1) / ROWS_IT;
@@ -398,19 +417,31 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   // next token's pass hit there instead of HBM.
   auto load_batch = [&](int it, u32x4 *buf) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < UR; ++u) {
       const int r = min(it * ROWS_IT + u * RPS + rr, n - 1);
-      if constexpr (REUSE)
-        buf[u] = K4[(size_t)r * V16 + lr];
-      else
-        buf[u] = __builtin_nontemporal_load(K4 + (size_t)r * V16 + lr);
+      const gptr<const u32x4> p = K4 + (size_t)r * V16;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        if constexpr (REUSE)
+          buf[u * CPL + c] = p[chunk_of(c)];
+        else
+          buf[u * CPL + c] = __builtin_nontemporal_load(p + chunk_of(c));
+      }
     }
   };
   auto consume = [&](int it, const u32x4 *buf) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < UR; ++u) {
       const int r = it * ROWS_IT + u * RPS + rr;
-      const float x = group_sum<LPR>(dot8(buf[u], q)) * scale;
+      float part = dot8(buf[u * CPL], q[0]);
+      if constexpr (CPL == 2) {
+        part += dot8(buf[u * CPL + 1], q[1]);
+      } else if constexpr (V16 == 16) {
+        part += dpp<0x128>(part);                  // row_ror:8 -- lane c ^ 8 of the row
+      } else {
+        part += __shfl_xor(part, V16 / 2);
+      }
+      const float x = group_sum<V16 / 2>(part) * scale;
       if (r < n) {
         if (lr == 0) lds_x[r] = x;
         mx = fmaxf(mx, x);
@@ -690,31 +721,34 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   }
 
   // the new row at its final slot: n (no eviction), n-1 (an older row left),
-  // or nowhere (it was the one evicted).  Lane c < LPR stores chunk c: the key
-  // chunk it already holds in q (with lr == c), rotated when the row moved
-  // together with its RoPE partner chunk c ^ (LPR/2), which lane c ^ (LPR/2)
-  // holds; and the value chunk loaded at the start.
+  // or nowhere (it was the one evicted).  Lane c < LPM stores key chunks c
+  // and c + LPM, a RoPE pair (with two chunks per lane the pair it holds in
+  // q, lr == c), rotated when the row moved; lane c < V16 stores value chunk
+  // c, loaded at the start.
   const int f = e < 0 ? n : (e < n ? n - 1 : -1);
-  u32x4 k_new = q;
-  if (f >= 0 && e >= 0 && wave == 0) {          // partner chunks (whole wave: shuffles)
-    u32x4 other;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) other[w] = __shfl_xor(q[w], LPR / 2);
-    const int c = lane & (LPR / 2 - 1);         // pair block of the first half
-    float cs[8], sn[8];          // written above by this same wave, or before the token
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      cs[j] = rot_c[c * 8 + j];
-      sn[j] = rot_s[c * 8 + j];
-    }
-    const bool first = (lane & (LPR / 2)) == 0;
-    u32x4 x1 = first ? q : other, x2 = first ? other : q;
-    rotate_chunk(x1, x2, cs, sn);
-    k_new = first ? x1 : x2;
-  }
-  if (f >= 0 && tid < LPR) {
+  if (f >= 0 && tid < V16) {
     const size_t o = (size_t)f * V16;
-    Kw[o + tid] = k_new;
+    if (tid < LPM) {
+      u32x4 k1, k2;
+      if constexpr (CPL == 2) {
+        k1 = q[0];
+        k2 = q[CPL - 1];
+      } else {
+        k1 = nk4[tid];
+        k2 = nk4[tid + LPM];
+      }
+      if (e >= 0) {                              // moved: rotate to position f
+        float cs[8], sn[8];      // written above by this same wave, or before the token
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          cs[j] = rot_c[tid * 8 + j];
+          sn[j] = rot_s[tid * 8 + j];
+        }
+        rotate_chunk(k1, k2, cs, sn);
+      }
+      Kw[o + tid] = k1;
+      Kw[o + tid + LPM] = k2;
+    }
     Vw[o + tid] = v_new;
     if (tid == 0) {
       scores[row0 + f] = 0.0f;

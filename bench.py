@@ -325,13 +325,15 @@ def main():
     for s0 in range(0, args.warmup, TPC):
         call(nk, nv, s0, TPC)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # rows stored before each timed step (byte model), from the counters now:
+    # every step adds one row up to the layer's budget
+    bud = np.asarray(budgets, dtype=np.int64)
+    nk0 = np.fromiter((ctr(l).n_kept for l in range(L)), dtype=np.int64, count=L)
+    n_prev[:] = np.minimum(nk0[None, :] + np.arange(args.steps, dtype=np.int64)[:, None],
+                           bud[None, :])
     torch.cuda.synchronize()
     e0.record(stream)
-    bud = np.asarray(budgets, dtype=np.int64)
-    ramp = np.arange(TPC, dtype=np.int64)[:, None]
     for s0 in range(0, args.steps, TPC):
-        nk0 = np.fromiter((ctr(l).n_kept for l in range(L)), dtype=np.int64, count=L)
-        n_prev[s0:s0 + TPC] = np.minimum(nk0[None, :] + ramp, bud[None, :])
         call(nk, nv, args.warmup + s0, TPC, ev[:, s0:s0 + TPC])
     e1.record(stream)
     torch.cuda.synchronize()
@@ -430,16 +432,16 @@ def whole_run(args, w, budgets, bh, L, d, TPC, call, ctr, batch, entry, stream, 
         for l in range(L):
             synth.bulk_kv_torch(w, t0, cnt, bh, gen, dev, out_k=ins_k[l, :cnt],
                                 out_v=ins_v[l, :cnt])
-        n_prev = np.zeros((cnt, L), dtype=np.int64)
+        # rows stored before each step of the chunk (byte model), outside the
+        # timed part: every step adds one row up to the layer's budget
+        nk0 = np.fromiter((ctr(l).n_kept for l in range(L)), dtype=np.int64, count=L)
+        n_prev = np.minimum(nk0[None, :] + np.arange(cnt, dtype=np.int64)[:, None], bud[None, :])
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         for s0 in range(0, cnt, TPC):
-            S = min(TPC, cnt - s0)
-            nk0 = np.fromiter((ctr(l).n_kept for l in range(L)), dtype=np.int64, count=L)
-            n_prev[s0:s0 + S] = np.minimum(nk0[None, :] + np.arange(S)[:, None], bud[None, :])
-            call(ins_k, ins_v, s0, S, ev[:, s0:s0 + S])
-            launches += 1 if batch is not None else L
+            call(ins_k, ins_v, s0, min(TPC, cnt - s0), ev[:, s0:s0 + min(TPC, cnt - s0)])
         b.record(stream)
+        launches += -(-cnt // TPC) * (1 if batch is not None else L)
         marks.append((a, b))
         # rows moved per (layer, token), summed over the caches (outside the events)
         npt = torch.from_numpy(np.ascontiguousarray(n_prev.T)).to(dev)[:, :, None]

@@ -25,6 +25,8 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
+
 import torch  # noqa: F401  (loads torch's HIP runtime first; libkve binds to it)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -293,10 +295,27 @@ class LayerBatch:
         self._pk = (ctypes.c_void_p * n)()
         self._pv = (ctypes.c_void_p * n)()
         self._pe = (ctypes.c_void_p * n)()
+        # numpy views of the pointer arrays: a whole-batch tensor fills them
+        # with one vectorised write instead of a Python loop over the layers
+        self._pk_np = np.frombuffer(self._pk, dtype=np.uint64)
+        self._pv_np = np.frombuffer(self._pv, dtype=np.uint64)
+        self._pe_np = np.frombuffer(self._pe, dtype=np.uint64)
+        self._idx = np.arange(n, dtype=np.uint64)
         dev = layers[0].k.device
         if any(x.k.device != dev for x in layers):
             raise ValueError("all layers must be on one device")
         self.device = dev
+        # (bh, d) of every layer, and the common one when all layers agree
+        self._rows = [(x.bh, x.d) for x in layers]
+        self._common = self._rows[0] if len(set(self._rows)) == 1 else None
+
+    def _same_rows(self, shape: tuple, tok: tuple, with_d: bool = True) -> bool:
+        """shape == tok + (bh_l, d_l) for every layer l (tok + (bh_l,) without d)."""
+        def want(rows):
+            return tok + (rows if with_d else rows[:1])
+        if self._common is not None:
+            return shape == want(self._common)
+        return all(shape == want(r) for r in self._rows)
 
     def _fill(self, new_k, new_v, evicted, n_tokens: int | None = None):
         """Pointer arrays for this call.
@@ -311,18 +330,17 @@ class LayerBatch:
         layer's block is contiguous."""
         n = self.n
         tok = () if n_tokens is None else (n_tokens,)
-        for arr, src, name in ((self._pk, new_k, "new_k"), (self._pv, new_v, "new_v")):
+        for arr, arr_np, src, name in ((self._pk, self._pk_np, new_k, "new_k"),
+                                       (self._pv, self._pv_np, new_v, "new_v")):
             if isinstance(src, torch.Tensor):
                 L0 = self.layers[0]
                 if (src.dtype != torch.float16 or src.dim() != 3 + len(tok) or
                         src.shape[0] != n or not _blocks_contiguous(src) or
                         src.device != self.device or
-                        any(tuple(src.shape[1:]) != tok + (x.bh, x.d) for x in self.layers)):
+                        not self._same_rows(tuple(src.shape[1:]), tok)):
                     raise ValueError(f"{name} must be float16 {[n, *tok, L0.bh, L0.d]} "
                                      "with contiguous per-layer blocks")
-                base, step = src.data_ptr(), src.stride(0) * 2
-                for i in range(n):
-                    arr[i] = base + i * step
+                arr_np[:] = np.uint64(src.data_ptr()) + self._idx * np.uint64(src.stride(0) * 2)
             else:
                 if len(src) != n:
                     raise ValueError(f"{name}: one tensor per layer")
@@ -339,12 +357,11 @@ class LayerBatch:
             if (evicted.dtype != torch.int32 or evicted.dim() != 2 + len(tok) or
                     evicted.shape[0] != n or not _blocks_contiguous(evicted) or
                     evicted.device != self.device or
-                    any(tuple(evicted.shape[1:]) != tok + (x.bh,) for x in self.layers)):
+                    not self._same_rows(tuple(evicted.shape[1:]), tok, with_d=False)):
                 raise ValueError(f"evicted must be int32 {[n, *tok, 'bh']} with contiguous "
                                  "per-layer blocks")
-            base, step = evicted.data_ptr(), evicted.stride(0) * 4
-            for i in range(n):
-                self._pe[i] = base + i * step
+            self._pe_np[:] = (np.uint64(evicted.data_ptr()) +
+                              self._idx * np.uint64(evicted.stride(0) * 4))
         else:
             if len(evicted) != n:
                 raise ValueError("evicted: one tensor (or None) per layer")

@@ -862,6 +862,14 @@ def test_layers_tokens_wide_workgroups_equal_single_calls(dev, kind, d):
 
 
 @pytest.mark.parametrize("kind", ["kf", "pk"])
+def test_layers_tokens_wide_largest_slots_equal_single_calls(dev, kind):
+    """512 caches of 9000 rows in a 4-token call: 1024-thread workgroups with
+    their largest score-slot count (12 per thread) against single-token calls
+    (512 threads, 24 slots per thread)."""
+    _layers_tokens_equal_single_calls(dev, kind, [(256, 9000, 0), (256, 8500, 256)], 8, 4, 60)
+
+
+@pytest.mark.parametrize("kind", ["kf", "pk"])
 def test_layers_tokens_streamed_keys_equal_single_calls(dev, kind):
     """512 caches of 1536 and 2048 rows, all resident at once: 235 MB of
     keys (268 MB by the launch's bound, 512 caches x 2048 rows), more than

@@ -125,6 +125,29 @@ def copy_calibration():
                                            "dispatches": 5}}), flush=True)
 
 
+def bandwidth_context(dev) -> dict:
+    """What a plain torch kernel reaches on this GPU in the same run: a 1 GiB
+    elementwise copy (reads and writes 1 GiB each), HIP events around 5
+    repetitions after one untimed."""
+    import torch
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.mul(src, 1.0, out=dst)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)
+    b.record()
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * n * 4 / (a.elapsed_time(b) / 1e3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"copy_kernel_GBs": copy_gbs,
+            "copy_kernel": "torch elementwise copy, 1 GiB read + 1 GiB written"}
+
+
 def step_bytes(kind: str, n: int, d: int, m, over: bool = True):
     """Algorithmic bytes of one cache-step (m may be an array).  TOVA-adapted
     ("tova") moves the PyramidKV bytes minus the 4n-byte read of the old
@@ -359,6 +382,7 @@ def main():
                       ms, launches, total_bytes, mean_m, traffic, kernel)
     out["config"]["steady_state_fill"] = args.fill
     out["config"]["fill_seconds"] = round(t_fill, 1)
+    out["context"] = bandwidth_context(dev)
     print(json.dumps(out), flush=True)
 
 

@@ -30,9 +30,15 @@
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and the call returns without synchronising.  Results are visible to
  *     later work on the same stream; synchronise before reading elsewhere.
- *   - The per-layer calls allocate nothing and keep no state besides small
- *     per-thread caches of rotation frequencies; they are reentrant.  The
- *     batched calls also use a per-device descriptor ring (see below).
+ *   - The per-layer calls keep no state besides small per-thread caches of
+ *     rotation frequencies and, in single-token calls that hand long
+ *     compactions to a second kernel (Keyformer noise, TOVA scoring or a
+ *     window longer than 128 rows, on at least 256 caches), a per-device
+ *     scratch buffer: allocated on the first such call on a device, grown
+ *     (after a device synchronisation) when a later call needs more, shared
+ *     by every stream with an event ordering its users.  Other per-layer
+ *     calls allocate nothing.  All calls are reentrant.  The batched calls
+ *     also use a per-device descriptor ring (see below).
  *   - Arguments are checked on the host before anything is enqueued.  A
  *     failing check returns KVE_EINVAL and leaves the counters and every
  *     tensor untouched.  A device fault is asynchronous and surfaces at the

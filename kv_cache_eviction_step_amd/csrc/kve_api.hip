@@ -183,19 +183,149 @@ void advance(kve_counters *ctr, int32_t budget) {
   ctr->pos += 1;
 }
 
+// ---------------------------------------------------------------------------
+// deferred compactions: single-token launches that hand their long moves to
+// the move kernel (kve_step.h) park rows in a per-device scratch
+// ---------------------------------------------------------------------------
+
+// Handed over in single-token launches whose policy makes long interior
+// moves routine (Gumbel noise, current-step scores, a window longer than a
+// step moves by itself) and that hold at least this many caches: there the
+// longest move, done by one compute unit, sets the launch's length.  Smaller
+// launches are bound by their latency chain, where a second launch would cost
+// more than it saves.  (With cumulative scores and a window, the row evicted
+// is nearly always the one just outside the window: a move of `recent` rows.)
+constexpr int64_t kDeferMinCaches = 256;
+
+bool defers(const Policy &p, int64_t caches) {
+  return (p.gumbel || p.current || p.recent > kve::kDeferRows) && caches >= kDeferMinCaches;
+}
+
+// Parked rows per workgroup for budgets up to `budget`: the chunks of the
+// longest move (at most budget - 1 rows).
+int defer_slots(int32_t budget) {
+  return std::max(1, (budget - 1 + kve::kMoveChunk - 1) / kve::kMoveChunk);
+}
+
+struct MoveScratch {
+  std::mutex mu;
+  kve::MoveDesc *desc = nullptr;
+  void *rows = nullptr;
+  int32_t *items = nullptr;      // (workgroup, chunk) pairs
+  int32_t *count = nullptr;      // [2], zero when allocated
+  int64_t desc_cap = 0;          // descriptors
+  int64_t rows_cap = 0;          // bytes
+  int64_t items_cap = 0;         // items
+  int parity = 0;                // the counter the next launch appends to
+  hipEvent_t done = nullptr;     // the last move kernel that used the scratch has finished
+  hipStream_t last = nullptr;    // ... on this stream
+  bool used = false;
+};
+
+void free_moves(MoveScratch &s) {
+  (void)hipFree(s.desc);
+  (void)hipFree(s.rows);
+  (void)hipFree(s.items);
+  (void)hipFree(s.count);
+  s.desc = nullptr;
+  s.rows = nullptr;
+  s.items = nullptr;
+  s.count = nullptr;
+  s.desc_cap = s.rows_cap = s.items_cap = 0;
+  s.parity = 0;
+  s.used = false;
+}
+
+MoveScratch g_moves[128];
+
+// The scratch for `blocks` workgroups with `slots` parked rows of dimension d,
+// ordered after its previous user; false if none can be had (the launch then
+// compacts every cache itself).  s.mu must be held until finish_moves.
+bool move_scratch(MoveScratch &s, int64_t blocks, int slots, int d, hipStream_t stream,
+                  kve::DeferArgs &out) {
+  const int64_t rows_bytes = blocks * slots * 4 * (int64_t)d;
+  const int64_t items = blocks * slots;
+  if (!s.done && hipEventCreateWithFlags(&s.done, hipEventDisableTiming) != hipSuccess) {
+    s.done = nullptr;
+    return false;
+  }
+  if (blocks > s.desc_cap || rows_bytes > s.rows_cap || items > s.items_cap) {
+    const int64_t nd = std::max(blocks, 2 * s.desc_cap);
+    const int64_t nr = std::max(rows_bytes, 2 * s.rows_cap);
+    const int64_t ni = std::max(items, 2 * s.items_cap);
+    if (s.desc) {                               // launches in flight may still read them
+      if (hipDeviceSynchronize() != hipSuccess) return false;
+      free_moves(s);
+    }
+    if (hipMalloc(reinterpret_cast<void **>(&s.desc), nd * sizeof(kve::MoveDesc)) !=
+            hipSuccess ||
+        hipMalloc(&s.rows, nr) != hipSuccess ||
+        hipMalloc(reinterpret_cast<void **>(&s.items), ni * 2 * sizeof(int32_t)) !=
+            hipSuccess ||
+        hipMalloc(reinterpret_cast<void **>(&s.count), 2 * sizeof(int32_t)) != hipSuccess ||
+        hipMemset(s.count, 0, 2 * sizeof(int32_t)) != hipSuccess) {
+      free_moves(s);
+      return false;
+    }
+    s.desc_cap = nd;
+    s.rows_cap = nr;
+    s.items_cap = ni;
+  }
+  if (s.used && s.last != stream && hipStreamWaitEvent(stream, s.done, 0) != hipSuccess)
+    return false;
+  out.desc = s.desc;
+  out.rows = s.rows;
+  out.items = s.items;
+  out.count = s.count;
+  out.slots = slots;
+  out.parity = s.parity;
+  return true;
+}
+
+// The move kernel after a launch that handed moves over, and the record that
+// later users of the scratch wait for.
+int finish_moves(MoveScratch &s, const kve::SharedArgs &sa, int64_t blocks, int d,
+                 hipStream_t stream) {
+  if (kve::launch_moves(sa.defer, (int)blocks, sa.back1, d, stream) != hipSuccess)
+    return KVE_ELAUNCH;
+  if (hipEventRecord(s.done, stream) != hipSuccess) return KVE_ELAUNCH;
+  s.last = stream;
+  s.used = true;
+  s.parity ^= 1;
+  return KVE_OK;
+}
+
+// The scratch of the current device for a launch of `blocks` workgroups at
+// budgets up to `budget`, taken (lock held) when the launch hands moves over.
+MoveScratch *take_moves(const Policy &p, int64_t blocks, int32_t budget, int d,
+                        hipStream_t stream, std::unique_lock<std::mutex> &lock,
+                        kve::SharedArgs &sa) {
+  int dev = 0;
+  if (!defers(p, blocks) || hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 128)
+    return nullptr;
+  lock = std::unique_lock<std::mutex>(g_moves[dev].mu);
+  if (move_scratch(g_moves[dev], blocks, defer_slots(budget), d, stream, sa.defer))
+    return &g_moves[dev];
+  sa.defer = kve::DeferArgs{};
+  lock.unlock();
+  return nullptr;
+}
+
 // One layer, one token: the descriptor travels by value with the launch.
 int step_impl(const kve_layer *L, const void *new_k, const void *new_v, kve_counters *ctr,
               int32_t budget, const Policy &p, int32_t *evicted, void *stream) {
   if (check_policy(p) != KVE_OK) return KVE_EINVAL;
   if (check_layer(L, new_k, new_v, ctr, budget, p) != KVE_OK) return KVE_EINVAL;
-  const int dev = check_device();
-  if (dev != KVE_OK) return dev;
+  const int dev_state = check_device();
+  if (dev_state != KVE_OK) return dev_state;
 
   const kve::LayerArgs la = layer_args(L, new_k, new_v, ctr, budget, evicted, p.gumbel);
-  const kve::SharedArgs sa = shared_args(L->d, p);
-  const hipError_t err =
-      kve::launch_step(la, sa, L->bh, L->d, p.gumbel, reinterpret_cast<hipStream_t>(stream));
-  if (err != hipSuccess) return KVE_ELAUNCH;
+  kve::SharedArgs sa = shared_args(L->d, p);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  std::unique_lock<std::mutex> lock;
+  MoveScratch *ms = take_moves(p, L->bh, budget, L->d, s, lock, sa);
+  if (kve::launch_step(la, sa, L->bh, L->d, p.gumbel, s) != hipSuccess) return KVE_ELAUNCH;
+  if (ms && finish_moves(*ms, sa, L->bh, L->d, s) != KVE_OK) return KVE_ELAUNCH;
   advance(ctr, budget);
   return KVE_OK;
 }
@@ -302,9 +432,16 @@ int batch_impl(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
     hl[l].n_tokens = n_tokens;
     block0 += layers[l].bh;
   }
-  const kve::SharedArgs sa = shared_args(d, p);
+  kve::SharedArgs sa = shared_args(d, p);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const size_t layer_bytes = sizeof(kve::LayerArgs) * n_layers;
+  std::unique_lock<std::mutex> move_lock;
+  MoveScratch *ms = nullptr;
+  if (n_tokens == 1) {
+    int32_t max_budget = 1;
+    for (int32_t l = 0; l < n_layers; ++l) max_budget = std::max(max_budget, budgets[l]);
+    ms = take_moves(p, blocks, max_budget, d, s, move_lock, sa);
+  }
   // The copy runs on the library's own stream (it touches only this slot, which
   // no queued launch reads any more), so it overlaps the caller's earlier work;
   // the launch on the caller's stream waits for it.
@@ -319,6 +456,7 @@ int batch_impl(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
   if (err != hipSuccess) return KVE_ELAUNCH;
   if (hipEventRecord(r.done[slot], s) != hipSuccess) return KVE_ELAUNCH;
   r.pending[slot] = true;
+  if (ms && finish_moves(*ms, sa, blocks, d, s) != KVE_OK) return KVE_ELAUNCH;
   for (int32_t l = 0; l < n_layers; ++l)
     for (int32_t t = 0; t < n_tokens; ++t) advance(&ctrs[l], budgets[l]);
   return KVE_OK;

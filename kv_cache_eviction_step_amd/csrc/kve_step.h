@@ -19,6 +19,37 @@ struct RopeTable {
   float s[kMaxHalfD];
 };
 
+// Rows per chunk of a deferred compaction (one workgroup of the move kernel
+// each), and the longest move a step still does itself.
+constexpr int kMoveChunk = 64;
+constexpr int kDeferRows = 2 * kMoveChunk;
+
+// One cache's compaction handed from a step to the move kernel that follows
+// it: rows e+1 .. n-1 move down one slot.  e < 0: nothing handed over.
+struct MoveDesc {
+  void *k;                 // the cache's row 0 (keys)
+  void *v;                 // the cache's row 0 (values)
+  int32_t e;               // evicted row
+  int32_t n;               // rows stored before the step
+};
+
+// Deferred compactions of one launch, indexed by workgroup: the descriptors,
+// and per workgroup `slots` rows of key + value (2d fp16 each): slot 0 the
+// incoming row (its key already rotated to its final position), slot j >= 1
+// row e + j*kMoveChunk as it was before the move (the first destination of
+// move chunk j, read by chunk j-1).  Each handed-over chunk is one work item
+// (workgroup, chunk) appended at count[parity]; the move kernel works through
+// them and zeroes count[1 - parity], which the launch before it used, so the
+// next launch (the other parity) starts from zero.
+struct DeferArgs {
+  MoveDesc *desc;          // [workgroups]; null: every step compacts its own cache
+  void *rows;              // fp16 [workgroups][slots][2][d]
+  int32_t *items;          // [workgroups * slots][2]: (workgroup, chunk)
+  int32_t *count;          // [2]: items queued, by parity
+  int32_t slots;           // >= the chunks of the longest possible move
+  int32_t parity;          // 0 or 1, alternating between launches
+};
+
 // One layer of a step: its B*H caches and where the incoming rows are.
 struct LayerArgs {
   void *k;                 // fp16 [bh][cap][d]
@@ -46,6 +77,7 @@ struct SharedArgs {
   int32_t current;         // 1: score = this step's weight (TOVA), 0: += (H2O / Keyformer)
   int32_t anneal_steps;
   int32_t early;           // 1: load the old scores before the key pass (set per launch)
+  DeferArgs defer;         // long compactions handed to the move kernel (single tokens)
   double tau_init;
   double tau_end;
   uint64_t seed;
@@ -70,5 +102,11 @@ hipError_t launch_step_layers(const LayerArgs *layers, int n_layers, int total_b
 // Whether such a launch reads the keys with ordinary (cached) loads rather
 // than non-temporal ones.
 bool reuse_keys(int total_blocks, int max_n_prev, int n_tokens, int d);
+
+// The move kernel: finishes the compactions that a single-token launch with
+// sa.defer.desc set handed over (`blocks` = that launch's workgroups).  Must
+// run after it on the same stream.
+hipError_t launch_moves(const DeferArgs &defer, int blocks, const RopeTable &back1, int d,
+                        hipStream_t stream);
 
 }  // namespace kve

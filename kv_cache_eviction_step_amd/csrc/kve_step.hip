@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "kve_step.h"
 
 namespace kve {
@@ -377,7 +379,6 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int n = la.n_prev;
-  const int np = (n + 63) & ~63;
   const bool over = n + 1 > la.budget;
   const size_t row0 = (size_t)hh * (size_t)la.cap;     // first row of this cache
   float *__restrict__ lds_x = lds;
@@ -603,6 +604,44 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   const int lm = tid % LPM;                     // chunk lm of the first half, lm of the second
   const int rm = tid / LPM;
 
+  // A single-token launch followed by the move kernel hands it every move
+  // longer than kDeferRows: the step parks the rows that move chunks would
+  // otherwise race on (each chunk's first destination) and the incoming row
+  // in the launch's scratch, and the move kernel shifts the chunks in
+  // parallel over the GPU instead of one compute unit doing them in turn.
+  // Every workgroup writes its descriptor (e < 0: nothing handed over).
+  const bool handoff = !PRE && sa.defer.desc != nullptr;
+  const bool defer = handoff && e >= 0 && e < n - 1 && n - 1 - e > kDeferRows;
+  gptr<u32x4> slot = nullptr;                   // this workgroup's scratch rows
+  if (handoff) {
+    if (tid == 0) {
+      MoveDesc md;
+      md.k = static_cast<char *>(la.k) + row0 * (size_t)(2 * D);
+      md.v = static_cast<char *>(la.v) + row0 * (size_t)(2 * D);
+      md.e = defer ? e : -1;
+      md.n = n;
+      sa.defer.desc[blockIdx.x] = md;
+    }
+    slot = global(reinterpret_cast<u32x4 *>(sa.defer.rows)) +
+           (size_t)blockIdx.x * sa.defer.slots * (2 * V16);
+  }
+  if (defer) {
+    __shared__ int item_base;
+    const int chunks = (n - 1 - e + kMoveChunk - 1) / kMoveChunk;
+    if (tid == 0) item_base = atomicAdd(sa.defer.count + sa.defer.parity, chunks);
+    for (int i = tid; i < (chunks - 1) * 2 * V16; i += NT) {
+      const int j = 1 + i / (2 * V16), w = i % (2 * V16);
+      const size_t row = (size_t)(e + j * kMoveChunk) * V16;
+      slot[(size_t)j * 2 * V16 + w] = w < V16 ? Kw[row + w] : Vw[row + w - V16];
+    }
+    __syncthreads();                            // item_base
+    if (tid < chunks) {
+      int32_t *it = sa.defer.items + 2 * (size_t)(item_base + tid);
+      it[0] = (int32_t)blockIdx.x;
+      it[1] = tid;
+    }
+  }
+
   // old rows e+1 .. n-1 move to e .. n-2, keys rotated by one position back.
   // Chunks of CH destination rows, software-pipelined: chunk c+1's loads are
   // in flight while chunk c is rotated and stored.  In place and safe: chunk
@@ -614,7 +653,7 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   // stores sit between chunk c's loads and chunk c+1's, waiting for chunk c
   // leaves those stores (and chunk c+1's loads) in flight: a chunk never
   // waits for the previous chunk's stores to be acknowledged.
-  if (e >= 0 && e < n - 1) {
+  if (!defer && e >= 0 && e < n - 1) {
     constexpr int CH = RPM * UM;
     constexpr int LOADS = 4 * UM;               // per thread per chunk
     constexpr int STORES = 4 * UM;              // per thread per full chunk
@@ -728,6 +767,10 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   const int f = e < 0 ? n : (e < n ? n - 1 : -1);
   if (f >= 0 && tid < V16) {
     const size_t o = (size_t)f * V16;
+    // handed over: the row goes to scratch slot 0 (keys, then values), and
+    // the move kernel writes it once it has read row n-1
+    const gptr<u32x4> dk = defer ? slot : Kw + o;
+    const gptr<u32x4> dv = defer ? slot + V16 : Vw + o;
     if (tid < LPM) {
       u32x4 k1, k2;
       if constexpr (CPL == 2) {
@@ -746,10 +789,10 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
         }
         rotate_chunk(k1, k2, cs, sn);
       }
-      Kw[o + tid] = k1;
-      Kw[o + tid + LPM] = k2;
+      dk[tid] = k1;
+      dk[tid + LPM] = k2;
     }
-    Vw[o + tid] = v_new;
+    dv[tid] = v_new;
     if (tid == 0) {
       scores[row0 + f] = 0.0f;
       if constexpr (GUMBEL) gumbel[row0 + f] = g_new;
@@ -840,6 +883,90 @@ __global__ __launch_bounds__(NT) void step_layers_kernel(const LayerArgs *__rest
     step_body<D, NT, U, GUMBEL, true, R, REUSE>(lt, sa, hh_t, tab + (t % kTokChunk) * TAB);
     __builtin_amdgcn_s_waitcnt(0);              // this token's stores have landed
     __syncthreads();
+  }
+}
+
+// Finishes the compactions a single-token launch handed over, one work item
+// (b, j) at a time: chunk j of workgroup b's cache -- destination rows
+// e + j*C .. e + (j+1)*C - 1 (C = kMoveChunk, the last chunk ending at row
+// n-2) from the rows one below, keys rotated by -1 position.  A chunk reads
+// from the cache only rows inside its own destination range, plus row n-1
+// for the last chunk; the one row it needs beyond that, the next chunk's
+// first destination, comes from the scratch slot the step filled before
+// anything moved.  So no two chunks touch the same row, and each chunk reads
+// everything before it writes.  The last chunk then writes the incoming row
+// at n-1.  The grid strides over the queued items; workgroup 0 first zeroes
+// the other parity's counter (its launch has finished).
+template <int D>
+__global__ __launch_bounds__(256) void move_kernel(DeferArgs defer, RopeTable back1) {
+  constexpr int NT = 256;
+  constexpr int V16 = D / 8;
+  constexpr int LPM = D / 16;                   // lanes per row: chunks lm and lm + LPM
+  constexpr int RPM = NT / LPM;                 // rows per sweep
+  constexpr int SW = kMoveChunk / RPM;          // sweeps per chunk
+  static_assert(SW * RPM == kMoveChunk, "move chunk");
+  if (blockIdx.x == 0 && threadIdx.x == 0) defer.count[1 - defer.parity] = 0;
+  const int queued = defer.count[defer.parity];
+  const int tid = threadIdx.x, lm = tid % LPM, rm = tid / LPM;
+  float cs[8], sn[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    cs[i] = back1.c[lm * 8 + i];
+    sn[i] = back1.s[lm * 8 + i];
+  }
+  for (int item = blockIdx.x; item < queued; item += gridDim.x) {
+    const int b = defer.items[2 * (size_t)item], j = defer.items[2 * (size_t)item + 1];
+    const MoveDesc md = defer.desc[b];
+    const int e = md.e, n = md.n, last = n - 2;
+    const int chunks = (n - 1 - e + kMoveChunk - 1) / kMoveChunk;
+    const int d0 = e + j * kMoveChunk;
+    const gptr<u32x4> K = global(reinterpret_cast<u32x4 *>(md.k));
+    const gptr<u32x4> V = global(reinterpret_cast<u32x4 *>(md.v));
+    const gptr<const u32x4> S = global(reinterpret_cast<const u32x4 *>(defer.rows)) +
+                                (size_t)b * defer.slots * (2 * V16);
+    u32x4 k1[SW], k2[SW], v1[SW], v2[SW];
+#pragma unroll
+    for (int w = 0; w < SW; ++w) {
+      const int dst = d0 + rm + w * RPM;
+      if (dst <= last) {
+        const int src = dst + 1;
+        if (j + 1 < chunks && src == d0 + kMoveChunk) {    // next chunk's first row
+          const gptr<const u32x4> r = S + (size_t)(j + 1) * 2 * V16;
+          k1[w] = r[lm];
+          k2[w] = r[lm + LPM];
+          v1[w] = r[V16 + lm];
+          v2[w] = r[V16 + lm + LPM];
+        } else {
+          const size_t o = (size_t)src * V16;
+          k1[w] = __builtin_nontemporal_load(K + o + lm);
+          k2[w] = __builtin_nontemporal_load(K + o + lm + LPM);
+          v1[w] = __builtin_nontemporal_load(V + o + lm);
+          v2[w] = __builtin_nontemporal_load(V + o + lm + LPM);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();                            // every row of the chunk has been read
+#pragma unroll
+    for (int w = 0; w < SW; ++w) {
+      const int dst = d0 + rm + w * RPM;
+      if (dst <= last) {
+        rotate_chunk(k1[w], k2[w], cs, sn);
+        const size_t o = (size_t)dst * V16;
+        __builtin_nontemporal_store(k1[w], K + o + lm);
+        __builtin_nontemporal_store(k2[w], K + o + lm + LPM);
+        __builtin_nontemporal_store(v1[w], V + o + lm);
+        __builtin_nontemporal_store(v2[w], V + o + lm + LPM);
+      }
+    }
+    if (j == chunks - 1 && tid < 2 * V16) {     // the incoming row (slot 0) at n-1
+      const u32x4 x = S[tid];
+      const size_t o = (size_t)(n - 1) * V16;
+      if (tid < V16)
+        K[o + tid] = x;
+      else
+        V[o + tid - V16] = x;
+    }
   }
 }
 
@@ -995,6 +1122,19 @@ hipError_t launch_step_layers(const LayerArgs *layers, int n_layers, int total_b
                                                   d, gumbel, stream)
                : launch_layers_nt<kThreads, false>(layers, n_layers, total_blocks, max_n_prev, sa,
                                                    d, gumbel, stream);
+}
+
+hipError_t launch_moves(const DeferArgs &defer, int blocks, const RopeTable &back1, int d,
+                        hipStream_t stream) {
+  // enough workgroups to spread the longest moves of a launch over the GPU;
+  // each strides over the queued chunks
+  const int64_t most = (int64_t)blocks * defer.slots;
+  const dim3 grid((unsigned)std::min<int64_t>(most, 4 * kComputeUnits));
+  if (d == 128)
+    hipLaunchKernelGGL(move_kernel<128>, grid, dim3(256), 0, stream, defer, back1);
+  else
+    hipLaunchKernelGGL(move_kernel<64>, grid, dim3(256), 0, stream, defer, back1);
+  return hipGetLastError();
 }
 
 }  // namespace kve

@@ -881,17 +881,20 @@ def test_layers_tokens_streamed_keys_equal_single_calls(dev, kind):
 @pytest.mark.parametrize("kind", ["kf", "pk"])
 @pytest.mark.parametrize("budget", [1000, 3000])
 @pytest.mark.parametrize("S", [1, 16])
-def test_launch_size_paths_agree(dev, kind, budget, S):
+@pytest.mark.parametrize("d", [128, 64])
+def test_launch_size_paths_agree(dev, kind, budget, S, d):
     """A launch's grid size picks code paths that must not change any bit:
     320 caches in one launch (more workgroups than compute units: state loads
-    after the key pass; at budget 3000 with S = 16, keys streamed) against
-    the same caches in two launches of 160 (state loads before the key pass;
-    keys cached between tokens), from a full synthetic state."""
+    after the key pass; Keyformer single tokens hand moves over 128 rows to
+    the move kernel; at budget 3000 with S = 16, keys streamed) against the
+    same caches in two launches of 160 (state loads before the key pass;
+    every cache compacted by its own workgroup; keys cached between tokens),
+    from a full synthetic state."""
     import kv_cache_eviction_step_amd as kve
     from gpu_harness import bulk_state
     kf = kind == "kf"
-    bh, half, d, T, pos0 = 320, 160, 128, 32, 7000
-    _say(f"[grid paths] kind={kind} budget={budget} S={S} bh={bh} vs 2x{half} T={T}")
+    bh, half, T, pos0 = 320, 160, 32, 7000
+    _say(f"[grid paths] kind={kind} d={d} budget={budget} S={S} bh={bh} vs 2x{half} T={T}")
     w = synth.Workload("grid", 1, 1, bh, d, pos0, T, budget, 4, "keyformer" if kf else "pyramid",
                        1.0 if kf else 0.0, 2.0 if kf else 0.0, 64 if kf else 0)
     gen = torch.Generator(device=dev)
@@ -934,3 +937,44 @@ def test_launch_size_paths_agree(dev, kind, budget, S):
         assert torch.equal(getattr(A, name)[:, :budget], joined[:, :budget]), name
     if kf:
         assert bool(((ev_a >= 0) & (ev_a < budget)).any())     # interior evictions happened
+
+
+@pytest.mark.parametrize("recent", [8, 200])
+def test_tova_handoff_equals_own_moves(dev, recent):
+    """TOVA scoring with a window (without one the incoming row, at score 0,
+    is always the one evicted) on 320 caches, one token per call: long moves
+    go to the move kernel; two calls of 160 caches compact every cache in its
+    own workgroup.  Same bits."""
+    import kv_cache_eviction_step_amd as kve
+    from gpu_harness import bulk_state
+    bh, half, d, budget, T, pos0 = 320, 160, 128, 1500, 24, 5000
+    _say(f"[tova handoff] recent={recent} bh={bh} vs 2x{half} budget={budget} T={T}")
+    w = synth.Workload("tv", 1, 1, bh, d, pos0, T, budget, 4, "tova", recent=recent)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(71 + recent)
+    A = kve.Layer.empty(bh, budget + 1, d, dev, gumbel=False)
+    bulk_state(A, budget, w, gen)
+    parts = []
+    for i in range(2):
+        sl = slice(i * half, (i + 1) * half)
+        parts.append(kve.Layer(A.k[sl].clone(), A.v[sl].clone(), A.scores[sl].clone(), None,
+                               A.positions[sl].clone(), hh_base=i * half))
+    nk, nv = synth.bulk_kv_torch(w, pos0, T, bh, gen, dev)
+    pol = kve.policy("tova", n_sink=4, recent=recent, rope_base=1e4)
+    ev_a = torch.full((T, bh), -9, dtype=torch.int32, device=dev)
+    ev_p = [torch.full((T, half), -9, dtype=torch.int32, device=dev) for _ in range(2)]
+    ba = kve.LayerBatch([A], [budget], [kve.Counters(budget, pos0, pos0)])
+    bp = [kve.LayerBatch([parts[i]], [budget], [kve.Counters(budget, pos0, pos0)])
+          for i in range(2)]
+    for t in range(T):
+        kve.step(ba, [nk[t]], [nv[t]], pol, [ev_a[t]])
+        for i in range(2):
+            sl = slice(i * half, (i + 1) * half)
+            kve.step(bp[i], [nk[t, sl].contiguous()], [nv[t, sl].contiguous()], pol, [ev_p[i][t]])
+    torch.cuda.synchronize()
+    assert torch.equal(ev_a, torch.cat(ev_p, dim=1))
+    for name in ("k", "v", "scores", "positions"):
+        joined = torch.cat([getattr(p, name) for p in parts])
+        assert torch.equal(getattr(A, name)[:, :budget], joined[:, :budget]), name
+    moved = torch.where((ev_a >= 0) & (ev_a < budget), budget - 1 - ev_a, 0)
+    assert int(moved.max()) > 128                      # some move was handed over

@@ -209,11 +209,9 @@ int defer_slots(int32_t budget) {
 
 struct MoveScratch {
   std::mutex mu;
-  kve::MoveDesc *desc = nullptr;
   void *rows = nullptr;
-  int32_t *items = nullptr;      // (workgroup, chunk) pairs
+  kve::MoveItem *items = nullptr;
   int32_t *count = nullptr;      // [2], zero when allocated
-  int64_t desc_cap = 0;          // descriptors
   int64_t rows_cap = 0;          // bytes
   int64_t items_cap = 0;         // items
   int parity = 0;                // the counter the next launch appends to
@@ -223,15 +221,13 @@ struct MoveScratch {
 };
 
 void free_moves(MoveScratch &s) {
-  (void)hipFree(s.desc);
   (void)hipFree(s.rows);
   (void)hipFree(s.items);
   (void)hipFree(s.count);
-  s.desc = nullptr;
   s.rows = nullptr;
   s.items = nullptr;
   s.count = nullptr;
-  s.desc_cap = s.rows_cap = s.items_cap = 0;
+  s.rows_cap = s.items_cap = 0;
   s.parity = 0;
   s.used = false;
 }
@@ -249,31 +245,26 @@ bool move_scratch(MoveScratch &s, int64_t blocks, int slots, int d, hipStream_t 
     s.done = nullptr;
     return false;
   }
-  if (blocks > s.desc_cap || rows_bytes > s.rows_cap || items > s.items_cap) {
-    const int64_t nd = std::max(blocks, 2 * s.desc_cap);
+  if (rows_bytes > s.rows_cap || items > s.items_cap) {
     const int64_t nr = std::max(rows_bytes, 2 * s.rows_cap);
     const int64_t ni = std::max(items, 2 * s.items_cap);
-    if (s.desc) {                               // launches in flight may still read them
+    if (s.rows) {                               // launches in flight may still read them
       if (hipDeviceSynchronize() != hipSuccess) return false;
       free_moves(s);
     }
-    if (hipMalloc(reinterpret_cast<void **>(&s.desc), nd * sizeof(kve::MoveDesc)) !=
-            hipSuccess ||
-        hipMalloc(&s.rows, nr) != hipSuccess ||
-        hipMalloc(reinterpret_cast<void **>(&s.items), ni * 2 * sizeof(int32_t)) !=
+    if (hipMalloc(&s.rows, nr) != hipSuccess ||
+        hipMalloc(reinterpret_cast<void **>(&s.items), ni * sizeof(kve::MoveItem)) !=
             hipSuccess ||
         hipMalloc(reinterpret_cast<void **>(&s.count), 2 * sizeof(int32_t)) != hipSuccess ||
         hipMemset(s.count, 0, 2 * sizeof(int32_t)) != hipSuccess) {
       free_moves(s);
       return false;
     }
-    s.desc_cap = nd;
     s.rows_cap = nr;
     s.items_cap = ni;
   }
   if (s.used && s.last != stream && hipStreamWaitEvent(stream, s.done, 0) != hipSuccess)
     return false;
-  out.desc = s.desc;
   out.rows = s.rows;
   out.items = s.items;
   out.count = s.count;

@@ -24,27 +24,28 @@ struct RopeTable {
 constexpr int kMoveChunk = 64;
 constexpr int kDeferRows = 2 * kMoveChunk;
 
-// One cache's compaction handed from a step to the move kernel that follows
-// it: rows e+1 .. n-1 move down one slot.  e < 0: nothing handed over.
-struct MoveDesc {
+// One chunk of a compaction handed from a step to the move kernel that
+// follows it: of the cache whose rows e+1 .. n-1 move down one slot, chunk j
+// (destination rows e + j*kMoveChunk .. up to n-2).
+struct MoveItem {
   void *k;                 // the cache's row 0 (keys)
   void *v;                 // the cache's row 0 (values)
   int32_t e;               // evicted row
   int32_t n;               // rows stored before the step
+  int32_t b;               // workgroup of the step (its scratch rows)
+  int32_t j;               // chunk
 };
 
-// Deferred compactions of one launch, indexed by workgroup: the descriptors,
-// and per workgroup `slots` rows of key + value (2d fp16 each): slot 0 the
-// incoming row (its key already rotated to its final position), slot j >= 1
-// row e + j*kMoveChunk as it was before the move (the first destination of
-// move chunk j, read by chunk j-1).  Each handed-over chunk is one work item
-// (workgroup, chunk) appended at count[parity]; the move kernel works through
+// Deferred compactions of one launch: per workgroup `slots` rows of key +
+// value (2d fp16 each) -- slot 0 the incoming row (its key already rotated to
+// its final position), slot j >= 1 row e + j*kMoveChunk as it was before the
+// move (the first destination of move chunk j, read by chunk j-1) -- and the
+// queue of chunks, appended at count[parity].  The move kernel works through
 // them and zeroes count[1 - parity], which the launch before it used, so the
 // next launch (the other parity) starts from zero.
 struct DeferArgs {
-  MoveDesc *desc;          // [workgroups]; null: every step compacts its own cache
+  MoveItem *items;         // [workgroups * slots]; null: every step compacts its own cache
   void *rows;              // fp16 [workgroups][slots][2][d]
-  int32_t *items;          // [workgroups * slots][2]: (workgroup, chunk)
   int32_t *count;          // [2]: items queued, by parity
   int32_t slots;           // >= the chunks of the longest possible move
   int32_t parity;          // 0 or 1, alternating between launches
@@ -104,7 +105,7 @@ hipError_t launch_step_layers(const LayerArgs *layers, int n_layers, int total_b
 bool reuse_keys(int total_blocks, int max_n_prev, int n_tokens, int d);
 
 // The move kernel: finishes the compactions that a single-token launch with
-// sa.defer.desc set handed over (`blocks` = that launch's workgroups).  Must
+// sa.defer.items set handed over (`blocks` = that launch's workgroups).  Must
 // run after it on the same stream.
 hipError_t launch_moves(const DeferArgs &defer, int blocks, const RopeTable &back1, int d,
                         hipStream_t stream);

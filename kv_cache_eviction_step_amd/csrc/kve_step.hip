@@ -607,26 +607,16 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   // A single-token launch followed by the move kernel hands it every move
   // longer than kDeferRows: the step parks the rows that move chunks would
   // otherwise race on (each chunk's first destination) and the incoming row
-  // in the launch's scratch, and the move kernel shifts the chunks in
-  // parallel over the GPU instead of one compute unit doing them in turn.
-  // Every workgroup writes its descriptor (e < 0: nothing handed over).
-  const bool handoff = !PRE && sa.defer.desc != nullptr;
-  const bool defer = handoff && e >= 0 && e < n - 1 && n - 1 - e > kDeferRows;
+  // in the launch's scratch, queues the chunks, and the move kernel shifts
+  // them in parallel over the GPU instead of one compute unit doing them in
+  // turn.
+  const bool defer = !PRE && sa.defer.items != nullptr && e >= 0 && e < n - 1 &&
+                     n - 1 - e > kDeferRows;
   gptr<u32x4> slot = nullptr;                   // this workgroup's scratch rows
-  if (handoff) {
-    if (tid == 0) {
-      MoveDesc md;
-      md.k = static_cast<char *>(la.k) + row0 * (size_t)(2 * D);
-      md.v = static_cast<char *>(la.v) + row0 * (size_t)(2 * D);
-      md.e = defer ? e : -1;
-      md.n = n;
-      sa.defer.desc[blockIdx.x] = md;
-    }
-    slot = global(reinterpret_cast<u32x4 *>(sa.defer.rows)) +
-           (size_t)blockIdx.x * sa.defer.slots * (2 * V16);
-  }
   if (defer) {
     __shared__ int item_base;
+    slot = global(reinterpret_cast<u32x4 *>(sa.defer.rows)) +
+           (size_t)blockIdx.x * sa.defer.slots * (2 * V16);
     const int chunks = (n - 1 - e + kMoveChunk - 1) / kMoveChunk;
     if (tid == 0) item_base = atomicAdd(sa.defer.count + sa.defer.parity, chunks);
     for (int i = tid; i < (chunks - 1) * 2 * V16; i += NT) {
@@ -636,9 +626,14 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
     }
     __syncthreads();                            // item_base
     if (tid < chunks) {
-      int32_t *it = sa.defer.items + 2 * (size_t)(item_base + tid);
-      it[0] = (int32_t)blockIdx.x;
-      it[1] = tid;
+      MoveItem it;
+      it.k = static_cast<char *>(la.k) + row0 * (size_t)(2 * D);
+      it.v = static_cast<char *>(la.v) + row0 * (size_t)(2 * D);
+      it.e = e;
+      it.n = n;
+      it.b = (int32_t)blockIdx.x;
+      it.j = tid;
+      sa.defer.items[item_base + tid] = it;
     }
   }
 
@@ -886,10 +881,10 @@ __global__ __launch_bounds__(NT) void step_layers_kernel(const LayerArgs *__rest
   }
 }
 
-// Finishes the compactions a single-token launch handed over, one work item
-// (b, j) at a time: chunk j of workgroup b's cache -- destination rows
-// e + j*C .. e + (j+1)*C - 1 (C = kMoveChunk, the last chunk ending at row
-// n-2) from the rows one below, keys rotated by -1 position.  A chunk reads
+// Finishes the compactions a single-token launch handed over, one queued
+// chunk at a time.  Chunk j of a cache fills destination rows e + j*C ..
+// e + (j+1)*C - 1 (C = kMoveChunk, the last chunk ending at row n-2) from the
+// rows one below, keys rotated by -1 position.  A chunk reads
 // from the cache only rows inside its own destination range, plus row n-1
 // for the last chunk; the one row it needs beyond that, the next chunk's
 // first destination, comes from the scratch slot the step filled before
@@ -915,9 +910,8 @@ __global__ __launch_bounds__(256) void move_kernel(DeferArgs defer, RopeTable ba
     sn[i] = back1.s[lm * 8 + i];
   }
   for (int item = blockIdx.x; item < queued; item += gridDim.x) {
-    const int b = defer.items[2 * (size_t)item], j = defer.items[2 * (size_t)item + 1];
-    const MoveDesc md = defer.desc[b];
-    const int e = md.e, n = md.n, last = n - 2;
+    const MoveItem md = defer.items[item];
+    const int b = md.b, j = md.j, e = md.e, n = md.n, last = n - 2;
     const int chunks = (n - 1 - e + kMoveChunk - 1) / kMoveChunk;
     const int d0 = e + j * kMoveChunk;
     const gptr<u32x4> K = global(reinterpret_cast<u32x4 *>(md.k));

@@ -21,8 +21,12 @@ struct RopeTable {
 
 // Rows per chunk of a deferred compaction (one workgroup of the move kernel
 // each), and the longest move a step still does itself.
+// (Tuning builds may override the second with -D.)
 constexpr int kMoveChunk = 64;
-constexpr int kDeferRows = 2 * kMoveChunk;
+#ifndef KVE_DEFER_ROWS
+#define KVE_DEFER_ROWS (2 * kMoveChunk)
+#endif
+constexpr int kDeferRows = KVE_DEFER_ROWS;
 
 // One chunk of a compaction handed from a step to the move kernel that
 // follows it: of the cache whose rows e+1 .. n-1 move down one slot, chunk j

@@ -36,8 +36,11 @@
  *     window longer than 128 rows, on at least 256 caches), a per-device
  *     scratch buffer: allocated on the first such call on a device, grown
  *     (after a device synchronisation) when a later call needs more, shared
- *     by every stream with an event ordering its users.  Other per-layer
- *     calls allocate nothing.  All calls are reentrant.  The batched calls
+ *     by every stream with an event ordering its users.  A call on a stream
+ *     under capture never uses it (its launch compacts in place), so the
+ *     per-layer single-token calls can be captured into a graph and
+ *     replayed.  Other per-layer calls allocate nothing.  All calls are
+ *     reentrant.  The batched calls
  *     also use a per-device descriptor ring (see below).
  *   - Arguments are checked on the host before anything is enqueued.  A
  *     failing check returns KVE_EINVAL and leaves the counters and every

@@ -288,12 +288,22 @@ int finish_moves(MoveScratch &s, const kve::SharedArgs &sa, int64_t blocks, int 
 
 // The scratch of the current device for a launch of `blocks` workgroups at
 // budgets up to `budget`, taken (lock held) when the launch hands moves over.
+// A stream under capture never hands moves over: the queue counter's parity
+// alternates on the host per call, and a replayed graph would keep reusing
+// one parity, so its count would never be cleared.  Such launches compact in
+// place, as launches below the threshold always do.
 MoveScratch *take_moves(const Policy &p, int64_t blocks, int32_t budget, int d,
                         hipStream_t stream, std::unique_lock<std::mutex> &lock,
                         kve::SharedArgs &sa) {
   int dev = 0;
   if (!defers(p, blocks) || hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 128)
     return nullptr;
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &capture) != hipSuccess ||
+      capture != hipStreamCaptureStatusNone) {
+    (void)hipGetLastError();                  // so the launch check does not report it
+    return nullptr;
+  }
   lock = std::unique_lock<std::mutex>(g_moves[dev].mu);
   if (move_scratch(g_moves[dev], blocks, defer_slots(budget), d, stream, sa.defer))
     return &g_moves[dev];

@@ -978,3 +978,48 @@ def test_tova_handoff_equals_own_moves(dev, recent):
         assert torch.equal(getattr(A, name)[:, :budget], joined[:, :budget]), name
     moved = torch.where((ev_a >= 0) & (ev_a < budget), budget - 1 - ev_a, 0)
     assert int(moved.max()) > 128                      # some move was handed over
+
+
+def test_captured_step_replays_match_eager(dev):
+    """keyformer_step captured into a graph on 320 caches.  Eagerly, long
+    moves of such a launch go to the move kernel; under capture the launch
+    compacts in place (the move queue's host-side state cannot be replayed).
+    Each replay, from the same restored state and with eager work and a
+    synchronisation between replays, must give the eager call's bits."""
+    import kv_cache_eviction_step_amd as kve
+    from gpu_harness import bulk_state
+    bh, d, budget, pos0 = 320, 128, 1000, 6000
+    _say(f"[graph capture] keyformer_step bh={bh} budget={budget} d={d}")
+    w = synth.Workload("graph", 1, 1, bh, d, pos0, 1, budget, 4, "keyformer", 1.0, 2.0, 64)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(83)
+    S0 = kve.Layer.empty(bh, budget + 1, d, dev, gumbel=True)
+    bulk_state(S0, budget, w, gen)
+    nk, nv = synth.bulk_kv_torch(w, pos0, 1, bh, gen, dev)
+    names = ("k", "v", "scores", "gumbel", "positions")
+
+    def copy_of(L):
+        return kve.Layer(*[getattr(L, x).clone() for x in names])
+
+    args = (budget, 4, 1.0, 2.0, 64, 1e4, 5)
+    E = copy_of(S0)
+    ev_e = torch.full((bh,), -9, dtype=torch.int32, device=dev)
+    kve.keyformer_step(E, nk[0], nv[0], kve.Counters(budget, pos0, pos0), *args, ev_e)
+    torch.cuda.synchronize()
+    assert int((budget - ev_e)[ev_e >= 0].max()) > 128   # eagerly, some move was handed over
+
+    G = copy_of(S0)
+    ev_g = torch.full((bh,), -9, dtype=torch.int32, device=dev)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        kve.keyformer_step(G, nk[0], nv[0], kve.Counters(budget, pos0, pos0), *args, ev_g)
+    for replay in range(3):
+        for x in names:
+            getattr(G, x).copy_(getattr(S0, x))
+        ev_g.fill_(-9)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ev_g, ev_e), replay
+        for x in names:
+            assert torch.equal(getattr(G, x)[:, :budget], getattr(E, x)[:, :budget]), (replay, x)

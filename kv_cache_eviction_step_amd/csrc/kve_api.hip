@@ -218,6 +218,10 @@ struct MoveScratch {
   hipEvent_t done = nullptr;     // the last move kernel that used the scratch has finished
   hipStream_t last = nullptr;    // ... on this stream
   bool used = false;
+  // A launch that queued moves without its move kernel (a failed launch or
+  // event record) leaves a count that no kernel clears: the device then never
+  // hands moves over again.
+  bool broken = false;
 };
 
 void free_moves(MoveScratch &s) {
@@ -277,9 +281,11 @@ bool move_scratch(MoveScratch &s, int64_t blocks, int slots, int d, hipStream_t 
 // later users of the scratch wait for.
 int finish_moves(MoveScratch &s, const kve::SharedArgs &sa, int64_t blocks, int d,
                  hipStream_t stream) {
-  if (kve::launch_moves(sa.defer, (int)blocks, sa.back1, d, stream) != hipSuccess)
+  if (kve::launch_moves(sa.defer, (int)blocks, sa.back1, d, stream) != hipSuccess ||
+      hipEventRecord(s.done, stream) != hipSuccess) {
+    s.broken = true;
     return KVE_ELAUNCH;
-  if (hipEventRecord(s.done, stream) != hipSuccess) return KVE_ELAUNCH;
+  }
   s.last = stream;
   s.used = true;
   s.parity ^= 1;
@@ -305,7 +311,8 @@ MoveScratch *take_moves(const Policy &p, int64_t blocks, int32_t budget, int d,
     return nullptr;
   }
   lock = std::unique_lock<std::mutex>(g_moves[dev].mu);
-  if (move_scratch(g_moves[dev], blocks, defer_slots(budget), d, stream, sa.defer))
+  if (!g_moves[dev].broken &&
+      move_scratch(g_moves[dev], blocks, defer_slots(budget), d, stream, sa.defer))
     return &g_moves[dev];
   sa.defer = kve::DeferArgs{};
   lock.unlock();

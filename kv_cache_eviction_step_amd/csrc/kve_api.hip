@@ -331,7 +331,9 @@ int step_impl(const kve_layer *L, const void *new_k, const void *new_v, kve_coun
   kve::SharedArgs sa = shared_args(L->d, p);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   std::unique_lock<std::mutex> lock;
-  MoveScratch *ms = take_moves(p, L->bh, budget, L->d, s, lock, sa);
+  // a step under its budget evicts nothing, so it has no move to hand over
+  MoveScratch *ms =
+      ctr->n_kept + 1 > budget ? take_moves(p, L->bh, budget, L->d, s, lock, sa) : nullptr;
   if (kve::launch_step(la, sa, L->bh, L->d, p.gumbel, s) != hipSuccess) return KVE_ELAUNCH;
   if (ms && finish_moves(*ms, sa, L->bh, L->d, s) != KVE_OK) return KVE_ELAUNCH;
   advance(ctr, budget);
@@ -447,8 +449,12 @@ int batch_impl(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
   MoveScratch *ms = nullptr;
   if (n_tokens == 1) {
     int32_t max_budget = 1;
-    for (int32_t l = 0; l < n_layers; ++l) max_budget = std::max(max_budget, budgets[l]);
-    ms = take_moves(p, blocks, max_budget, d, s, move_lock, sa);
+    bool evicts = false;                      // some layer is at its budget
+    for (int32_t l = 0; l < n_layers; ++l) {
+      max_budget = std::max(max_budget, budgets[l]);
+      evicts = evicts || ctrs[l].n_kept + 1 > budgets[l];
+    }
+    if (evicts) ms = take_moves(p, blocks, max_budget, d, s, move_lock, sa);
   }
   // The copy runs on the library's own stream (it touches only this slot, which
   // no queued launch reads any more), so it overlaps the caller's earlier work;

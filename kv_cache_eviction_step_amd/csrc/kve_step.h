@@ -27,6 +27,11 @@ constexpr int kMoveChunk = 64;
 #define KVE_DEFER_ROWS (2 * kMoveChunk)
 #endif
 constexpr int kDeferRows = KVE_DEFER_ROWS;
+// Workgroups of the move kernel that share a queue longer than its grid.
+#ifndef KVE_MOVE_STREAMS
+#define KVE_MOVE_STREAMS 256
+#endif
+constexpr int kMoveStreams = KVE_MOVE_STREAMS;
 
 // One chunk of a compaction handed from a step to the move kernel that
 // follows it: of the cache whose rows e+1 .. n-1 move down one slot, chunk j

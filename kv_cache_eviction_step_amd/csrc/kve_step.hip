@@ -909,7 +909,14 @@ __global__ __launch_bounds__(256) void move_kernel(DeferArgs defer, RopeTable ba
     cs[i] = back1.c[lm * 8 + i];
     sn[i] = back1.s[lm * 8 + i];
   }
-  for (int item = blockIdx.x; item < queued; item += gridDim.x) {
+  // Up to a grid's worth of chunks, each gets a workgroup of its own (the
+  // launch is one round trip long).  A longer queue is shared by fewer
+  // workgroups, each taking many chunks in turn: fewer streams in flight
+  // move more bytes per second.
+  const int active = queued > (int)gridDim.x ? min((int)gridDim.x, kMoveStreams)
+                                             : (int)gridDim.x;
+  if ((int)blockIdx.x >= active) return;
+  for (int item = blockIdx.x; item < queued; item += active) {
     const MoveItem md = defer.items[item];
     const int b = md.b, j = md.j, e = md.e, n = md.n, last = n - 2;
     const int chunks = (n - 1 - e + kMoveChunk - 1) / kMoveChunk;
@@ -968,12 +975,15 @@ __global__ __launch_bounds__(256) void move_kernel(DeferArgs defer, RopeTable ba
 // launch
 // ---------------------------------------------------------------------------
 
-// Launch shape (tuning builds may override these two with -D).
+// Launch shapes (tuning builds may override these with -D).
 #ifndef KVE_THREADS
 #define KVE_THREADS 512
 #endif
 #ifndef KVE_UNROLL
 #define KVE_UNROLL 8
+#endif
+#ifndef KVE_MOVE_WGS
+#define KVE_MOVE_WGS (4 * kComputeUnits)
 #endif
 constexpr int kThreads = KVE_THREADS;
 constexpr int kWideThreads = 2 * KVE_THREADS;
@@ -1123,7 +1133,7 @@ hipError_t launch_moves(const DeferArgs &defer, int blocks, const RopeTable &bac
   // enough workgroups to spread the longest moves of a launch over the GPU;
   // each strides over the queued chunks
   const int64_t most = (int64_t)blocks * defer.slots;
-  const dim3 grid((unsigned)std::min<int64_t>(most, 4 * kComputeUnits));
+  const dim3 grid((unsigned)std::min<int64_t>(most, KVE_MOVE_WGS));
   if (d == 128)
     hipLaunchKernelGGL(move_kernel<128>, grid, dim3(256), 0, stream, defer, back1);
   else

@@ -1,12 +1,13 @@
 // kve_step.hip -- gfx950 kernel of the per-token KV-cache eviction step.
 //
 // One workgroup owns one cache (one (batch, kv-head) of the layer) for the
-// whole step, so no cross-workgroup synchronisation or scratch memory is
-// needed.  Phases inside the workgroup:
+// whole step, so no workgroup ever waits for another.  Phases inside the
+// workgroup:
 //   A  score pass: coalesced 128-bit loads of the stored keys (non-temporal,
 //      or cached in a token loop whose keys fit the last-level cache), fp16
-//      dot2 products against the incoming key, 16-lane DPP reduction per row,
-//      logits to LDS (a matrix-vector product: bandwidth bound, no MFMA);
+//      dot2 products against the incoming key, a DPP reduction over each
+//      row's lanes, logits to LDS (a matrix-vector product: bandwidth bound,
+//      no MFMA);
 //   B  softmax: block max, exponentials and an exact (fixed-point) block sum;
 //      each thread holds the old scores / gumbel of its rows in registers,
 //      loaded before the score pass in latency-bound launches, else here;
@@ -22,7 +23,9 @@
 // Two entry kernels share the body: one layer and one token per launch
 // (everything passed by value), or several layers and/or tokens per launch
 // (descriptors in device memory, the workgroups of each layer contiguous in
-// the grid, each walking its cache through the tokens).
+// the grid, each walking its cache through the tokens).  A third kernel
+// finishes the long compactions that large single-token launches queue for
+// it in a scratch buffer, spreading them over the GPU.
 //
 // Method (VeloxQuant-MLX pages): "veloxquant_mlx.quantizers.keyformer
 // module" -- keyformer_update steps 1-3, KeyformerState, FIXED GAP #1/#2,

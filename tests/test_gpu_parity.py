@@ -980,6 +980,58 @@ def test_tova_handoff_equals_own_moves(dev, recent):
     assert int(moved.max()) > 128                      # some move was handed over
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_handoff_edges_against_oracle(dev, d):
+    """One single-token Keyformer launch of 320 caches (moves over 128 rows go
+    to the move kernel), sampled caches steered to the edges of the handoff
+    and checked against the oracle bit for bit: row 0 with no sinks (999 rows
+    move: every one of the 16 scratch chunk slots is used), 998 rows, exactly
+    129 rows (the shortest move handed over, a last chunk of one row), exactly
+    128 rows (kept in place), 193 and 482 rows (ragged last chunks), and the
+    newest stored row (nothing moves).  The other caches get random states and
+    must evict a valid row."""
+    import kv_cache_eviction_step_amd as kve
+    from gpu_harness import bulk_state
+    bh, budget, n_sink = 320, 1000, 0
+    n, cap = budget, budget + 5
+    next_pos = 5000 + n
+    targets = {0: 0, 37: 1, 101: n - 1 - 129, 150: n - 1 - 128, 203: n - 1 - 193,
+               260: n - 1 - 482, 319: n - 1}
+    _say(f"[handoff edges] d={d} bh={bh} budget={budget} targets={targets}")
+    w = synth.Workload(f"handoff{d}", 40, 1, 8, d, 64, 0, budget, n_sink, "keyformer",
+                       1.0, 2.0, 64)
+    assert w.bh == bh
+    samples = []
+    for hh, target in targets.items():
+        c = _forced(w, hh, n, cap, next_pos, target)
+        init = c.snapshot()
+        tr = guarded_trajectory(w, 0, hh, budget, 1, cap=cap, t0=next_pos, cache=c,
+                                params=params_for(w, budget, hh))
+        assert tr.evicted[0] == target
+        samples.append(Sample(hh, budget, init, tr.ks, tr.vs, tr.evicted, tr.cache.snapshot(),
+                              int(tr.attempts.sum())))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(97 + d)
+    L = kve.Layer.empty(bh, cap, d, dev, gumbel=True)
+    bulk_state(L, n, w, gen)
+    for s in samples:
+        load_state_into(L, s.hh, s.init)
+    nk, nv = synth.bulk_kv_torch(w, next_pos, 1, bh, gen, dev)
+    nk, nv = nk[0].contiguous(), nv[0].contiguous()
+    for s in samples:
+        nk[s.hh] = torch.from_numpy(s.ks[0].view(np.float16)).to(dev)
+        nv[s.hh] = torch.from_numpy(s.vs[0].view(np.float16)).to(dev)
+    ev = torch.full((bh,), -7, dtype=torch.int32, device=dev)
+    ctr = kve.Counters(n, next_pos, next_pos)
+    prm = params_for(w, budget, 0)
+    kve.keyformer_step(L, nk, nv, ctr, budget, n_sink, prm.tau_init, prm.tau_end,
+                       prm.anneal_steps, w.rope_base, w.gumbel_seed, ev)
+    torch.cuda.synchronize()
+    evn = ev.cpu().numpy()
+    _assert_parity(L, evn[None, :], samples, next_pos)
+    assert ((evn >= 0) & (evn <= n)).all()
+    assert ctr.n_kept == budget
+
 def test_captured_step_replays_match_eager(dev):
     """keyformer_step captured into a graph on 320 caches.  Eagerly, long
     moves of such a launch go to the move kernel; under capture the launch

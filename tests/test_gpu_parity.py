@@ -1032,6 +1032,47 @@ def test_handoff_edges_against_oracle(dev, d):
     assert ((evn >= 0) & (evn <= n)).all()
     assert ctr.n_kept == budget
 
+def test_batched_handoff_mixed_budgets_equals_own_moves(dev):
+    """kve_step with TOVA scoring and a 200-row window over two layers of 160
+    caches with budgets 1500 and 700, one token per call: as one launch (320
+    caches: long moves go to the move kernel, whose per-workgroup scratch is
+    sized by the larger budget and indexed across both layers) and as one
+    launch per layer (160 caches: every cache compacted by its own
+    workgroup).  Same bits."""
+    import kv_cache_eviction_step_amd as kve
+    from gpu_harness import bulk_state
+    half, d, T, pos0, recent = 160, 128, 16, 6000, 200
+    budgets = [1500, 700]
+    _say(f"[batched handoff] budgets={budgets} 2x{half} caches T={T}")
+    pol = kve.policy("tova", n_sink=4, recent=recent, rope_base=1e4)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(113)
+    A, B = [], []
+    for i, b in enumerate(budgets):
+        w = synth.Workload(f"bh{i}", 20, 1, 8, d, pos0, T, b, 4, "tova", recent=recent)
+        L = kve.Layer.empty(half, b + 1, d, dev, gumbel=False)
+        bulk_state(L, b, w, gen)
+        A.append(L)
+        B.append(kve.Layer(L.k.clone(), L.v.clone(), L.scores.clone(), None, L.positions.clone()))
+    nk = torch.randn(2, T, half, d, generator=gen, device=dev).half()
+    nv = torch.randn(2, T, half, d, generator=gen, device=dev).half()
+    ev_a = torch.full((2, T, half), -9, dtype=torch.int32, device=dev)
+    ev_b = torch.full((2, T, half), -9, dtype=torch.int32, device=dev)
+    ba = kve.LayerBatch(A, budgets, [kve.Counters(b, pos0, pos0) for b in budgets])
+    bb = [kve.LayerBatch([B[i]], [budgets[i]], [kve.Counters(budgets[i], pos0, pos0)])
+          for i in range(2)]
+    for t in range(T):
+        kve.step(ba, [nk[0, t], nk[1, t]], [nv[0, t], nv[1, t]], pol, [ev_a[0, t], ev_a[1, t]])
+        for i in range(2):
+            kve.step(bb[i], [nk[i, t]], [nv[i, t]], pol, [ev_b[i, t]])
+    torch.cuda.synchronize()
+    assert torch.equal(ev_a, ev_b)
+    for i, b in enumerate(budgets):
+        for name in ("k", "v", "scores", "positions"):
+            assert torch.equal(getattr(A[i], name)[:, :b], getattr(B[i], name)[:, :b]), (i, name)
+        moved = torch.where((ev_a[i] >= 0) & (ev_a[i] < b), b - 1 - ev_a[i], 0)
+        assert int(moved.max()) > 128                  # some move was handed over
+
 def test_captured_step_replays_match_eager(dev):
     """keyformer_step captured into a graph on 320 caches.  Eagerly, long
     moves of such a launch go to the move kernel; under capture the launch

@@ -30,18 +30,18 @@
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and the call returns without synchronising.  Results are visible to
  *     later work on the same stream; synchronise before reading elsewhere.
- *   - The per-layer calls keep no state besides small per-thread caches of
- *     rotation frequencies and, in single-token calls that hand long
- *     compactions to a second kernel (Keyformer noise, TOVA scoring or a
- *     window longer than 128 rows, on at least 256 caches), a per-device
- *     scratch buffer: allocated on the first such call on a device, grown
- *     (after a device synchronisation) when a later call needs more, shared
- *     by every stream with an event ordering its users.  A call on a stream
- *     under capture never uses it (its launch compacts in place), so the
- *     per-layer single-token calls can be captured into a graph and
- *     replayed.  Other per-layer calls allocate nothing.  All calls are
- *     reentrant.  The batched calls
- *     also use a per-device descriptor ring (see below).
+ *   - The calls keep no state besides small per-thread caches of rotation
+ *     frequencies and, in single-token launches that hand long compactions
+ *     to a second kernel (Keyformer noise, TOVA scoring or a window longer
+ *     than 128 rows, on at least 256 caches, with some cache at its
+ *     budget), a per-device scratch buffer: allocated on the first such call
+ *     on a device, grown (after a device synchronisation) when a later call
+ *     needs more, shared by every stream with an event ordering its users.
+ *     A call on a stream under capture never uses it (its launch compacts in
+ *     place), so every call can be captured into a graph and replayed (the
+ *     host counters advance at capture, not at replay).  Other calls
+ *     allocate nothing: the batched forms pass their layer descriptors by
+ *     value with the launch.  All calls are reentrant.
  *   - Arguments are checked on the host before anything is enqueued.  A
  *     failing check returns KVE_EINVAL and leaves the counters and every
  *     tensor untouched.  A device fault is asynchronous and surfaces at the
@@ -159,14 +159,11 @@ int pyramid_step(const kve_layer *L, const void *new_k, const void *new_v,
  *              be NULL), or NULL
  *   n_sink, tau_*, anneal_steps, rope_base, seed, stream: as per layer, shared
  * Every layer is checked before anything is enqueued; on KVE_EINVAL no
- * counter changes.  The descriptors reach the device through a ring of 64
- * pinned host / device slots per device, allocated (with one non-blocking
- * copy stream) on the first batched call on that device (a failed
- * allocation returns KVE_ELAUNCH); each call copies its slot on that stream
- * and makes `stream` wait for the copy, then launches on `stream`.  A call
- * blocks the host only if the device is 64 batched calls behind.  Calls from
- * several threads are serialised on that ring.  Not for use under stream
- * capture (the descriptor copies read the ring at replay time).
+ * counter changes.  The descriptors of up to 32 layers travel by value with
+ * a launch; a call over more layers is one launch per group of 32, in order
+ * on `stream` (the same bits, since layers are independent).  On
+ * KVE_ELAUNCH the groups launched before the failure have been stepped and
+ * their counters advanced; the rest are untouched.
  */
 int keyformer_step_layers(int32_t n_layers, const kve_layer *layers, const void *const *new_k,
                           const void *const *new_v, kve_counters *ctrs, const int32_t *budgets,
@@ -194,8 +191,8 @@ int pyramid_step_layers(int32_t n_layers, const kve_layer *layers, const void *c
  *   ctr        advanced by S tokens on success
  *   other arguments as keyformer_step / pyramid_step.
  * Checked as one per-layer call (the first token's counters), plus
- * 1 <= n_tokens <= 128.  Uses the batched calls' descriptor ring; not for use
- * under stream capture.
+ * 1 <= n_tokens <= 128; launched as keyformer_step_layers_tokens with one
+ * layer.
  */
 int keyformer_step_tokens(const kve_layer *L, int32_t n_tokens, const void *new_k,
                           const void *new_v, kve_counters *ctr, int32_t budget, int32_t n_sink,
@@ -222,8 +219,7 @@ int pyramid_step_tokens(const kve_layer *L, int32_t n_tokens, const void *new_k,
  *              new_k[l] + t*bh_l*d
  *   evicted    HOST array [n_layers] of device i32 [S][bh_l] (entries may be
  *              NULL), or NULL
- * Checked and queued as keyformer_step_layers (same descriptor ring; not for
- * use under stream capture).
+ * Checked and launched as keyformer_step_layers.
  */
 int keyformer_step_layers_tokens(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
                                  const void *const *new_k, const void *const *new_v,
@@ -281,8 +277,8 @@ typedef struct kve_policy {
  *   policy     HOST pointer, read during the call only
  * Returns as keyformer_step; KVE_EINVAL also for a NULL policy, an unknown
  * score rule, gumbel not 0 or 1, recent < 0 or budget <= n_sink + recent.
- * One layer and one token launch directly; otherwise the call uses the
- * descriptor ring of the batched calls (not for use under stream capture).
+ * One layer and one token launch as keyformer_step does; otherwise as the
+ * batched calls.
  */
 int kve_step(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
              const void *const *new_k, const void *const *new_v, kve_counters *ctrs,

@@ -1,8 +1,8 @@
 // kve_api.hip -- host side of the C ABI declared in include/kve.h:
 // argument checks, the eviction policy, fp64 rotation constants and
-// frequencies, the launch on the caller's stream, the counter update, the
-// descriptor ring of the multi-layer / multi-token calls, and the host-only
-// helpers (pyramid budget schedule, kept indices, byte accounting).
+// frequencies, the launches on the caller's stream, the counter update, the
+// move scratch of large single-token launches, and the host-only helpers
+// (pyramid budget schedule, kept indices, byte accounting).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -341,46 +341,12 @@ int step_impl(const kve_layer *L, const void *new_k, const void *new_v, kve_coun
 }
 
 // ---------------------------------------------------------------------------
-// batched calls: per-layer descriptors travel to the device through a ring of
-// pinned host slots and device slots (one slot per call, reused once the
-// launch that read it has finished)
+// batched calls: up to kLaunchLayers layer descriptors travel by value with
+// each launch; a call over more layers is several launches (layers never
+// exchange data, so any grouping gives the same bits)
 // ---------------------------------------------------------------------------
 
-struct Ring {
-  static constexpr int kSlots = 64;
-  static constexpr size_t kSlotBytes = sizeof(kve::LayerArgs) * kve::kMaxBatchLayers;
-  std::mutex mu;
-  bool ready = false;
-  char *host = nullptr;
-  char *dev = nullptr;
-  hipStream_t copy_stream = nullptr;   // descriptor copies overlap the caller's previous work
-  hipEvent_t copied[kSlots];           // slot's copy landed (the launch waits on it)
-  hipEvent_t done[kSlots];             // launch that read the slot finished
-  bool pending[kSlots] = {};
-  int next = 0;
-};
-
-Ring g_rings[128];
-
-int ring_init(Ring &r) {
-  if (r.ready) return KVE_OK;
-  if (hipHostMalloc(reinterpret_cast<void **>(&r.host), Ring::kSlotBytes * Ring::kSlots,
-                    hipHostMallocDefault) != hipSuccess)
-    return KVE_ELAUNCH;
-  if (hipMalloc(reinterpret_cast<void **>(&r.dev), Ring::kSlotBytes * Ring::kSlots) !=
-      hipSuccess)
-    return KVE_ELAUNCH;
-  if (hipStreamCreateWithFlags(&r.copy_stream, hipStreamNonBlocking) != hipSuccess)
-    return KVE_ELAUNCH;
-  for (int i = 0; i < Ring::kSlots; ++i)
-    if (hipEventCreateWithFlags(&r.done[i], hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&r.copied[i], hipEventDisableTiming) != hipSuccess)
-      return KVE_ELAUNCH;
-  r.ready = true;
-  return KVE_OK;
-}
-
-// One descriptor-driven launch: n_layers layers, each stepped n_tokens tokens.
+// Descriptor-driven launches: n_layers layers, each stepped n_tokens tokens.
 // Checks every layer first.
 int batch_impl(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
                const void *const *new_k, const void *const *new_v, kve_counters *ctrs,
@@ -391,7 +357,6 @@ int batch_impl(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
   if (check_policy(p) != KVE_OK) return KVE_EINVAL;
   const int d = layers[0].d;
   int64_t blocks = 0;
-  int max_n = 0;
   for (int32_t l = 0; l < n_layers; ++l) {
     if (check_layer(&layers[l], new_k[l], new_v[l], &ctrs[l], budgets[l], p) != KVE_OK)
       return KVE_EINVAL;
@@ -400,8 +365,6 @@ int batch_impl(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
         (int64_t)ctrs[l].pos + n_tokens >= INT32_MAX)
       return KVE_EINVAL;
     blocks += layers[l].bh;
-    const int32_t n_last = std::min(ctrs[l].n_kept + n_tokens - 1, budgets[l]);
-    if (n_last > max_n) max_n = n_last;
   }
   if (blocks > INT32_MAX) return KVE_EINVAL;
   // Two layers sharing cache memory (the same layer passed twice, say) would be
@@ -420,59 +383,37 @@ int batch_impl(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
   }
   const int dev_state = check_device();
   if (dev_state != KVE_OK) return dev_state;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 128) return KVE_ENODEV;
 
-  Ring &r = g_rings[dev];
-  std::lock_guard<std::mutex> lock(r.mu);
-  if (ring_init(r) != KVE_OK) return KVE_ELAUNCH;
-  const int slot = r.next;
-  r.next = (r.next + 1) % Ring::kSlots;
-  if (r.pending[slot] && hipEventSynchronize(r.done[slot]) != hipSuccess) return KVE_ELAUNCH;
-  r.pending[slot] = false;
-
-  char *hslot = r.host + (size_t)slot * Ring::kSlotBytes;
-  char *dslot = r.dev + (size_t)slot * Ring::kSlotBytes;
-  kve::LayerArgs *hl = reinterpret_cast<kve::LayerArgs *>(hslot);
-  int32_t block0 = 0;
-  for (int32_t l = 0; l < n_layers; ++l) {
-    hl[l] = layer_args(&layers[l], new_k[l], new_v[l], &ctrs[l], budgets[l],
-                       evicted ? evicted[l] : nullptr, p.gumbel);
-    hl[l].block0 = block0;
-    hl[l].n_tokens = n_tokens;
-    block0 += layers[l].bh;
-  }
-  kve::SharedArgs sa = shared_args(d, p);
+  const kve::SharedArgs shared = shared_args(d, p);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const size_t layer_bytes = sizeof(kve::LayerArgs) * n_layers;
-  std::unique_lock<std::mutex> move_lock;
-  MoveScratch *ms = nullptr;
-  if (n_tokens == 1) {
-    int32_t max_budget = 1;
+  for (int32_t g0 = 0; g0 < n_layers; g0 += kve::kLaunchLayers) {
+    const int32_t g1 = std::min(n_layers, g0 + kve::kLaunchLayers);
+    kve::LayerPack pack{};
+    int32_t block0 = 0, max_n = 0, max_budget = 1;
     bool evicts = false;                      // some layer is at its budget
-    for (int32_t l = 0; l < n_layers; ++l) {
+    for (int32_t l = g0; l < g1; ++l) {
+      kve::LayerArgs &a = pack.l[l - g0];
+      a = layer_args(&layers[l], new_k[l], new_v[l], &ctrs[l], budgets[l],
+                     evicted ? evicted[l] : nullptr, p.gumbel);
+      a.block0 = block0;
+      a.n_tokens = n_tokens;
+      block0 += layers[l].bh;
+      max_n = std::max(max_n, std::min(ctrs[l].n_kept + n_tokens - 1, budgets[l]));
       max_budget = std::max(max_budget, budgets[l]);
       evicts = evicts || ctrs[l].n_kept + 1 > budgets[l];
     }
-    if (evicts) ms = take_moves(p, blocks, max_budget, d, s, move_lock, sa);
+    kve::SharedArgs sa = shared;
+    std::unique_lock<std::mutex> move_lock;
+    MoveScratch *ms = n_tokens == 1 && evicts
+                          ? take_moves(p, block0, max_budget, d, s, move_lock, sa)
+                          : nullptr;
+    if (kve::launch_step_layers(pack, g1 - g0, block0, max_n, n_tokens, sa, d, p.gumbel, s) !=
+        hipSuccess)
+      return KVE_ELAUNCH;
+    if (ms && finish_moves(*ms, sa, block0, d, s) != KVE_OK) return KVE_ELAUNCH;
+    for (int32_t l = g0; l < g1; ++l)
+      for (int32_t t = 0; t < n_tokens; ++t) advance(&ctrs[l], budgets[l]);
   }
-  // The copy runs on the library's own stream (it touches only this slot, which
-  // no queued launch reads any more), so it overlaps the caller's earlier work;
-  // the launch on the caller's stream waits for it.
-  if (hipMemcpyAsync(dslot, hslot, layer_bytes, hipMemcpyHostToDevice, r.copy_stream) !=
-          hipSuccess ||
-      hipEventRecord(r.copied[slot], r.copy_stream) != hipSuccess ||
-      hipStreamWaitEvent(s, r.copied[slot], 0) != hipSuccess)
-    return KVE_ELAUNCH;
-  const hipError_t err =
-      kve::launch_step_layers(reinterpret_cast<const kve::LayerArgs *>(dslot), n_layers,
-                              (int)blocks, max_n, n_tokens, sa, d, p.gumbel, s);
-  if (err != hipSuccess) return KVE_ELAUNCH;
-  if (hipEventRecord(r.done[slot], s) != hipSuccess) return KVE_ELAUNCH;
-  r.pending[slot] = true;
-  if (ms && finish_moves(*ms, sa, blocks, d, s) != KVE_OK) return KVE_ELAUNCH;
-  for (int32_t l = 0; l < n_layers; ++l)
-    for (int32_t t = 0; t < n_tokens; ++t) advance(&ctrs[l], budgets[l]);
   return KVE_OK;
 }
 
@@ -577,7 +518,7 @@ KVE_EXPORT int kve_step(int32_t n_layers, int32_t n_tokens, const kve_layer *lay
   p.anneal_steps = p.gumbel ? policy->anneal_steps : 0;
   p.rope_base = policy->rope_base;
   p.seed = p.gumbel ? policy->seed : 0;
-  if (n_layers == 1 && n_tokens == 1)        // no descriptor ring needed
+  if (n_layers == 1 && n_tokens == 1)        // the per-layer kernel
     return step_impl(&layers[0], new_k[0], new_v[0], &ctrs[0], budgets[0], p,
                      evicted ? evicted[0] : nullptr, stream);
   return batch_impl(n_layers, n_tokens, layers, new_k, new_v, ctrs, budgets, p, evicted, stream);

@@ -101,11 +101,18 @@ struct SharedArgs {
 hipError_t launch_step(const LayerArgs &la, const SharedArgs &sa, int bh, int d, bool gumbel,
                        hipStream_t stream);
 
+// Up to kLaunchLayers layer descriptors, passed by value with a launch (in
+// the kernel-argument segment: no copy of its own, nothing to allocate).
+constexpr int kLaunchLayers = 32;
+struct LayerPack {
+  LayerArgs l[kLaunchLayers];
+};
+
 // Several layers and/or several tokens per launch: `layers` is device memory;
 // layer l steps layers[l].n_tokens tokens (n_tokens, the same for every
 // layer), token t reading its incoming rows at new_k + t*bh*d and writing
 // evicted + t*bh.
-hipError_t launch_step_layers(const LayerArgs *layers, int n_layers, int total_blocks,
+hipError_t launch_step_layers(const LayerPack &layers, int n_layers, int total_blocks,
                               int max_n_prev, int n_tokens, const SharedArgs &sa, int d,
                               bool gumbel, hipStream_t stream);
 

@@ -813,8 +813,9 @@ __global__ __launch_bounds__(NT) void step_kernel(LayerArgs la, SharedArgs sa) {
 // of the workgroup has landed and every wave has arrived, so the next token
 // reads the state the previous one left.
 template <int D, int NT, int U, bool GUMBEL, int R, bool REUSE>
-__global__ __launch_bounds__(NT) void step_layers_kernel(const LayerArgs *__restrict__ layers,
-                                                         int n_layers, SharedArgs sa) {
+__global__ __launch_bounds__(NT) void step_layers_kernel(LayerPack pack, int n_layers,
+                                                         SharedArgs sa) {
+  const LayerArgs *__restrict__ layers = pack.l;    // in the kernel-argument segment
   // layer of this workgroup: the number of layers starting at or before it,
   // counted with one load per lane and a ballot (at most 128 layers)
   const int b = blockIdx.x;
@@ -1038,7 +1039,7 @@ static hipError_t launch_d(const LayerArgs &la, const SharedArgs &sa, int bh,
 }
 
 template <int NT, int D, bool GUMBEL, int R, bool REUSE>
-static hipError_t launch_layers_d_r(const LayerArgs *layers, int n_layers, int total_blocks,
+static hipError_t launch_layers_d_r(const LayerPack &layers, int n_layers, int total_blocks,
                                     int max_n_prev, const SharedArgs &sa, hipStream_t stream) {
   auto kern = step_layers_kernel<D, NT, kUnroll, GUMBEL, R, REUSE>;
   const size_t lds = lds_bytes_for(max_n_prev) + (size_t)kTokChunk * (D + 2) * sizeof(float);
@@ -1049,7 +1050,7 @@ static hipError_t launch_layers_d_r(const LayerArgs *layers, int n_layers, int t
 }
 
 template <int NT, int D, bool GUMBEL, bool REUSE>
-static hipError_t launch_layers_d(const LayerArgs *layers, int n_layers, int total_blocks,
+static hipError_t launch_layers_d(const LayerPack &layers, int n_layers, int total_blocks,
                                   int max_n_prev, const SharedArgs &sa, hipStream_t stream) {
   using S = Slots<NT>;
   const int r = (max_n_prev + NT - 1) / NT;
@@ -1074,7 +1075,7 @@ static hipError_t launch_step_nt(const LayerArgs &la, const SharedArgs &sa, int 
 }
 
 template <int NT, bool REUSE>
-static hipError_t launch_layers_nt(const LayerArgs *layers, int n_layers, int total_blocks,
+static hipError_t launch_layers_nt(const LayerPack &layers, int n_layers, int total_blocks,
                                    int max_n_prev, const SharedArgs &sa, int d, bool gumbel,
                                    hipStream_t stream) {
   if (d == 128)
@@ -1109,7 +1110,7 @@ hipError_t launch_step(const LayerArgs &la, const SharedArgs &sa_in, int bh, int
   return launch_step_nt<kThreads>(la, sa, bh, d, gumbel, stream);
 }
 
-hipError_t launch_step_layers(const LayerArgs *layers, int n_layers, int total_blocks,
+hipError_t launch_step_layers(const LayerPack &layers, int n_layers, int total_blocks,
                               int max_n_prev, int n_tokens, const SharedArgs &sa_in, int d,
                               bool gumbel, hipStream_t stream) {
   SharedArgs sa = sa_in;

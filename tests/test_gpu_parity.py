@@ -791,9 +791,9 @@ def test_policy_plain_equals_named_entry_points(dev):
 
 
 def _layers_tokens_equal_single_calls(dev, kind, shapes, T, S, seed, d=128):
-    """Two layers (bh, budget, hh_base) from full synthetic states stepped T
-    tokens, S per launch of the token-loop kernel, give the same bits as
-    single-token calls per layer."""
+    """Layers (bh, budget, hh_base) from full synthetic states stepped T
+    tokens, S per call of the batched form, give the same bits as single-token
+    calls per layer."""
     import kv_cache_eviction_step_amd as kve
     from gpu_harness import bulk_state
     kf = kind == "kf"
@@ -817,7 +817,7 @@ def _layers_tokens_equal_single_calls(dev, kind, shapes, T, S, seed, d=128):
     cas = [kve.Counters(b, pos0, pos0) for b in budgets]
     args = (4, 1.0, 2.0, 64, 1e4, 3) if kf else (4, 1e4)
     for t in range(T):
-        for l in range(2):
+        for l in range(len(shapes)):
             if kf:
                 kve.keyformer_step(As[l], nks[l][t], nvs[l][t], cas[l], budgets[l], *args,
                                    evas[l][t])
@@ -834,7 +834,7 @@ def _layers_tokens_equal_single_calls(dev, kind, shapes, T, S, seed, d=128):
         else:
             kve.pyramid_step_layers_tokens(batch, ks, vs, *args, es)
     torch.cuda.synchronize()
-    for l in range(2):
+    for l in range(len(shapes)):
         assert torch.equal(evas[l], evbs[l]), l
         n = budgets[l]
         for name in ("k", "v", "scores", "positions") + (("gumbel",) if kf else ()):
@@ -842,6 +842,17 @@ def _layers_tokens_equal_single_calls(dev, kind, shapes, T, S, seed, d=128):
                 (l, name)
     if kf:
         assert any(bool(((e >= 0) & (e < b)).any()) for e, b in zip(evas, budgets))
+
+
+@pytest.mark.parametrize("kind", ["kf", "pk"])
+@pytest.mark.parametrize("S", [1, 8])
+def test_more_layers_than_one_launch_equal_single_calls(dev, kind, S):
+    """40 layers in one call are two launches (descriptors of up to 32 layers
+    travel with a launch); with one token per call the first launch holds 256
+    caches, so Keyformer hands its long moves over and the second does not.
+    Budgets 40 .. 313, Gumbel streams offset per layer."""
+    shapes = [(8, 40 + 7 * l, 8 * l) for l in range(40)]
+    _layers_tokens_equal_single_calls(dev, kind, shapes, 24, S, 61 + S)
 
 
 @pytest.mark.parametrize("kind", ["kf", "pk"])
@@ -1116,3 +1127,61 @@ def test_captured_step_replays_match_eager(dev):
         assert torch.equal(ev_g, ev_e), replay
         for x in names:
             assert torch.equal(getattr(G, x)[:, :budget], getattr(E, x)[:, :budget]), (replay, x)
+
+
+
+def test_captured_batched_call_replays_match_eager(dev):
+    """keyformer_step_layers_tokens over 3 layers and 8 tokens, captured into a
+    graph (its descriptors travel by value with the launch) and replayed three
+    times from a restored state, with eager work and synchronisations between
+    replays: every replay equals the eager call bit for bit."""
+    import kv_cache_eviction_step_amd as kve
+    from gpu_harness import bulk_state
+    d, S, pos0 = 128, 8, 4000
+    shapes = [(8, 300, 0), (16, 200, 8), (8, 100, 24)]
+    _say(f"[graph capture] keyformer_step_layers_tokens shapes={shapes} S={S}")
+    names = ("k", "v", "scores", "gumbel", "positions")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(89)
+    S0, nks, nvs = [], [], []
+    for bh, budget, hb in shapes:
+        w = synth.Workload("gc", 1, 1, bh, d, pos0, S, budget, 4, "keyformer", 1.0, 2.0, 64)
+        L = kve.Layer.empty(bh, budget + 1, d, dev, gumbel=True, hh_base=hb)
+        bulk_state(L, budget, w, gen)
+        S0.append(L)
+        k, v = synth.bulk_kv_torch(w, pos0, S, bh, gen, dev)
+        nks.append(k)
+        nvs.append(v)
+    budgets = [x[1] for x in shapes]
+
+    def copy_of(L):
+        return kve.Layer(*[getattr(L, x).clone() for x in names], hh_base=L.hh_base)
+
+    def batch_of(Ls):
+        return kve.LayerBatch(Ls, budgets, [kve.Counters(b, pos0, pos0) for b in budgets])
+
+    args = (4, 1.0, 2.0, 64, 1e4, 3)
+    E = [copy_of(L) for L in S0]
+    ev_e = [torch.full((S, bh), -9, dtype=torch.int32, device=dev) for bh, _, _ in shapes]
+    kve.keyformer_step_layers_tokens(batch_of(E), nks, nvs, *args, ev_e)
+    torch.cuda.synchronize()
+    G = [copy_of(L) for L in S0]
+    ev_g = [torch.full((S, bh), -9, dtype=torch.int32, device=dev) for bh, _, _ in shapes]
+    bg = batch_of(G)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        kve.keyformer_step_layers_tokens(bg, nks, nvs, *args, ev_g)
+    for replay in range(3):
+        for Lg, L0 in zip(G, S0):
+            for x in names:
+                getattr(Lg, x).copy_(getattr(L0, x))
+        for e in ev_g:
+            e.fill_(-9)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for l, (Lg, Le) in enumerate(zip(G, E)):
+            assert torch.equal(ev_g[l], ev_e[l]), (replay, l)
+            n = budgets[l]
+            for x in names:
+                assert torch.equal(getattr(Lg, x)[:, :n], getattr(Le, x)[:, :n]), (replay, l, x)

@@ -188,6 +188,10 @@ class Layer:
             raise ValueError("gumbel must be contiguous float32 [bh, cap] on the same device")
         self.k, self.v, self.scores, self.gumbel, self.positions = k, v, scores, gumbel, positions
         self.bh, self.cap, self.d, self.hh_base = bh, cap, d, hh_base
+        # what the per-call checks compare against (plain ints and tuples are
+        # cheaper to compare than torch.device objects)
+        self._dev = k.get_device()                # -1 for host tensors
+        self._row_shape = (bh, d)
 
     @classmethod
     def empty(cls, bh: int, cap: int, d: int, device, gumbel: bool = True, hh_base: int = 0):
@@ -212,8 +216,8 @@ class Layer:
 
 
 def _rows(t, layer: Layer, name: str):
-    if (t.dtype != torch.float16 or tuple(t.shape) != (layer.bh, layer.d) or
-            not t.is_contiguous() or t.device != layer.k.device):
+    if (t.dtype is not torch.float16 or t.shape != layer._row_shape or
+            not t.is_contiguous() or t.get_device() != layer._dev):
         raise ValueError(f"{name} must be contiguous float16 [{layer.bh}, {layer.d}] on "
                          f"{layer.k.device}")
     return t.data_ptr()
@@ -222,20 +226,29 @@ def _rows(t, layer: Layer, name: str):
 def _evicted_ptr(evicted, layer: Layer):
     if evicted is None:
         return None
-    if (evicted.dtype != torch.int32 or tuple(evicted.shape) != (layer.bh,) or
-            not evicted.is_contiguous() or evicted.device != layer.k.device):
+    if (evicted.dtype is not torch.int32 or evicted.shape != (layer.bh,) or
+            not evicted.is_contiguous() or evicted.get_device() != layer._dev):
         raise ValueError(f"evicted must be contiguous int32 [{layer.bh}] on {layer.k.device}")
     return evicted.data_ptr()
 
 
+# torch's query of the current stream's raw handle (no Stream object is
+# built: about a tenth of the public call's host time); the public call where
+# a build lacks it
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream_ptr(stream, layer: Layer):
     """The stream handle, after checking that the layer lives on the current
-    device (the library launches there, and keeps its descriptor ring there)."""
-    if not layer.k.is_cuda or layer.k.get_device() != torch.cuda.current_device():
+    device (the library launches there)."""
+    dev = layer._dev
+    if dev < 0 or dev != torch.cuda.current_device():
         raise ValueError(f"layer tensors are on {layer.k.device}; calls run on the current "
                          "GPU (use torch.cuda.device(...) to select it)")
     if stream is None:
-        return torch.cuda.current_stream(layer.k.device).cuda_stream
+        if _raw_stream is not None:
+            return _raw_stream(dev)
+        return torch.cuda.current_stream(dev).cuda_stream
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
@@ -305,9 +318,22 @@ class LayerBatch:
         if any(x.k.device != dev for x in layers):
             raise ValueError("all layers must be on one device")
         self.device = dev
+        self._dev = layers[0]._dev
+        self._offsets = {}                        # byte stride -> per-layer offsets
         # (bh, d) of every layer, and the common one when all layers agree
         self._rows = [(x.bh, x.d) for x in layers]
         self._common = self._rows[0] if len(set(self._rows)) == 1 else None
+
+    def _layer_offsets(self, stride_bytes: int):
+        """Byte offsets l * stride_bytes of the layers' blocks in a whole-batch
+        tensor (kept per stride: a decode loop passes the same layout every call)."""
+        offs = self._offsets.get(stride_bytes)
+        if offs is None:
+            if len(self._offsets) >= 16:
+                self._offsets.clear()
+            offs = self._idx * np.uint64(stride_bytes)
+            self._offsets[stride_bytes] = offs
+        return offs
 
     def _same_rows(self, shape: tuple, tok: tuple, with_d: bool = True) -> bool:
         """shape == tok + (bh_l, d_l) for every layer l (tok + (bh_l,) without d)."""
@@ -334,13 +360,14 @@ class LayerBatch:
                                        (self._pv, self._pv_np, new_v, "new_v")):
             if isinstance(src, torch.Tensor):
                 L0 = self.layers[0]
-                if (src.dtype != torch.float16 or src.dim() != 3 + len(tok) or
-                        src.shape[0] != n or not _blocks_contiguous(src) or
-                        src.device != self.device or
-                        not self._same_rows(tuple(src.shape[1:]), tok)):
+                if (src.dtype is not torch.float16 or src.dim() != 3 + len(tok) or
+                        src.shape[0] != n or src.get_device() != self._dev or
+                        not self._same_rows(tuple(src.shape[1:]), tok) or
+                        not (src.is_contiguous() or _blocks_contiguous(src))):
                     raise ValueError(f"{name} must be float16 {[n, *tok, L0.bh, L0.d]} "
                                      "with contiguous per-layer blocks")
-                arr_np[:] = np.uint64(src.data_ptr()) + self._idx * np.uint64(src.stride(0) * 2)
+                np.add(self._layer_offsets(src.stride(0) * 2), np.uint64(src.data_ptr()),
+                       out=arr_np)
             else:
                 if len(src) != n:
                     raise ValueError(f"{name}: one tensor per layer")
@@ -354,14 +381,14 @@ class LayerBatch:
         if evicted is None:
             return None
         if isinstance(evicted, torch.Tensor):
-            if (evicted.dtype != torch.int32 or evicted.dim() != 2 + len(tok) or
-                    evicted.shape[0] != n or not _blocks_contiguous(evicted) or
-                    evicted.device != self.device or
-                    not self._same_rows(tuple(evicted.shape[1:]), tok, with_d=False)):
+            if (evicted.dtype is not torch.int32 or evicted.dim() != 2 + len(tok) or
+                    evicted.shape[0] != n or evicted.get_device() != self._dev or
+                    not self._same_rows(tuple(evicted.shape[1:]), tok, with_d=False) or
+                    not (evicted.is_contiguous() or _blocks_contiguous(evicted))):
                 raise ValueError(f"evicted must be int32 {[n, *tok, 'bh']} with contiguous "
                                  "per-layer blocks")
-            self._pe_np[:] = (np.uint64(evicted.data_ptr()) +
-                              self._idx * np.uint64(evicted.stride(0) * 4))
+            np.add(self._layer_offsets(evicted.stride(0) * 4), np.uint64(evicted.data_ptr()),
+                   out=self._pe_np)
         else:
             if len(evicted) != n:
                 raise ValueError("evicted: one tensor (or None) per layer")
@@ -399,8 +426,8 @@ def pyramid_step_layers(batch: LayerBatch, new_k, new_v, n_sink: int, rope_base:
 
 
 def _tokens(t, layer: Layer, name: str):
-    if (t.dtype != torch.float16 or t.dim() != 3 or tuple(t.shape[1:]) != (layer.bh, layer.d)
-            or not t.is_contiguous() or t.device != layer.k.device):
+    if (t.dtype is not torch.float16 or t.dim() != 3 or t.shape[1:] != layer._row_shape
+            or not t.is_contiguous() or t.get_device() != layer._dev):
         raise ValueError(f"{name} must be contiguous float16 [S, {layer.bh}, {layer.d}] on "
                          f"{layer.k.device}")
     return t.data_ptr()
@@ -409,8 +436,8 @@ def _tokens(t, layer: Layer, name: str):
 def _evicted_tokens(evicted, layer: Layer, n: int):
     if evicted is None:
         return None
-    if (evicted.dtype != torch.int32 or tuple(evicted.shape) != (n, layer.bh) or
-            not evicted.is_contiguous() or evicted.device != layer.k.device):
+    if (evicted.dtype is not torch.int32 or evicted.shape != (n, layer.bh) or
+            not evicted.is_contiguous() or evicted.get_device() != layer._dev):
         raise ValueError(f"evicted must be contiguous int32 [{n}, {layer.bh}]")
     return evicted.data_ptr()
 

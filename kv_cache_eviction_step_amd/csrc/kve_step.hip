@@ -986,9 +986,6 @@ __global__ __launch_bounds__(256) void move_kernel(DeferArgs defer, RopeTable ba
 #ifndef KVE_UNROLL
 #define KVE_UNROLL 8
 #endif
-#ifndef KVE_WIDE_MIN_BLOCKS
-#define KVE_WIDE_MIN_BLOCKS (2 * kComputeUnits)
-#endif
 #ifndef KVE_MOVE_WGS
 #define KVE_MOVE_WGS (4 * kComputeUnits)
 #endif
@@ -1124,7 +1121,7 @@ hipError_t launch_step_layers(const LayerPack &layers, int n_layers, int total_b
   // workgroups: one per compute unit, twice the key bytes in flight per
   // cache.  Fewer, latency-bound workgroups, and single tokens, keep 512
   // threads, whose reductions are shorter.
-  if (n_tokens > 1 && total_blocks >= KVE_WIDE_MIN_BLOCKS)
+  if (n_tokens > 1 && total_blocks >= 2 * kComputeUnits)
     return reuse ? launch_layers_nt<kWideThreads, true>(layers, n_layers, total_blocks,
                                                         max_n_prev, sa, d, gumbel, stream)
                  : launch_layers_nt<kWideThreads, false>(layers, n_layers, total_blocks,

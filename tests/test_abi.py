@@ -376,3 +376,34 @@ def test_binding_refuses_tensors_off_the_current_gpu():
         kve.keyformer_step(L, k, k, Counters(0, 0, 0), 8, 2, 1.0, 2.0, 8, 1e4, 0)
     with pytest.raises(ValueError, match="current"):
         kve.pyramid_step_tokens(L, k[None], k[None], Counters(0, 0, 0), 8, 2, 1e4)
+
+
+def test_layer_batch_pointer_arrays():
+    """The batched calls' per-layer pointers from one whole-batch tensor:
+    block l of a [n_layers, ...] tensor starts at data_ptr + l * stride(0)
+    elements, contiguous or a slice of a longer axis; a pointer list of
+    per-layer tensors works too; bad tensors are refused before any call."""
+    layers = [kve.Layer.empty(4, 17, 64, "cpu", gumbel=True) for _ in range(3)]
+    batch = kve.LayerBatch(layers, [16] * 3)
+    for tok in (None, 5):
+        t_axis = () if tok is None else (tok,)
+        big = torch.zeros((3, *((9,) if tok else ()), 4, 64), dtype=torch.float16)
+        src = big if tok is None else big[:, 2:2 + tok]      # strided along the layer axis
+        ev_big = torch.zeros((3, *((9,) if tok else ()), 4), dtype=torch.int32)
+        ev = ev_big if tok is None else ev_big[:, 1:1 + tok]
+        pe = batch._fill(src, src, ev, tok)
+        for l in range(3):
+            assert batch._pk[l] == src.data_ptr() + l * src.stride(0) * 2
+            assert batch._pv[l] == src.data_ptr() + l * src.stride(0) * 2
+            assert pe[l] == ev.data_ptr() + l * ev.stride(0) * 4
+        per = [src[l].contiguous() for l in range(3)]
+        batch._fill(per, per, None, tok)
+        assert [batch._pk[l] for l in range(3)] == [p.data_ptr() for p in per]
+        with pytest.raises(ValueError):                     # wrong dtype
+            batch._fill(src.float(), src, None, tok)
+        with pytest.raises(ValueError):                     # wrong row shape
+            batch._fill(torch.zeros((3, *t_axis, 4, 32), dtype=torch.float16), src, None, tok)
+    for s in range(20):                                     # the offsets cache stays small
+        batch._layer_offsets(128 * (s + 1))
+    assert len(batch._offsets) <= 16
+    assert (batch._layer_offsets(256) == np.arange(3, dtype=np.uint64) * np.uint64(256)).all()

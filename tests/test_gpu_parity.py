@@ -1043,6 +1043,50 @@ def test_handoff_edges_against_oracle(dev, d):
     assert ((evn >= 0) & (evn <= n)).all()
     assert ctr.n_kept == budget
 
+def test_handoff_largest_budget_against_oracle(dev):
+    """The largest budget (12288 rows) in a single-token Keyformer launch of 256
+    caches, which hands long moves over: sampled caches steered to row 0 with
+    no sinks (12287 rows move: 192 chunks, every scratch slot of the launch),
+    a middle row, and the newest stored row; bit for bit against the oracle."""
+    import kv_cache_eviction_step_amd as kve
+    from gpu_harness import bulk_state
+    bh, budget, n_sink, d = 256, 12288, 0, 128
+    n, cap = budget, budget + 1
+    next_pos = 20000
+    targets = {0: 0, 129: 6001, 255: n - 1}
+    _say(f"[handoff max budget] bh={bh} budget={budget} targets={targets}")
+    w = synth.Workload("handoffmax", 32, 1, 8, d, 64, 0, budget, n_sink, "keyformer",
+                       1.0, 2.0, 64)
+    samples = []
+    for hh, target in targets.items():
+        c = _forced(w, hh, n, cap, next_pos, target)
+        init = c.snapshot()
+        tr = guarded_trajectory(w, 0, hh, budget, 1, cap=cap, t0=next_pos, cache=c,
+                                params=params_for(w, budget, hh))
+        assert tr.evicted[0] == target
+        samples.append(Sample(hh, budget, init, tr.ks, tr.vs, tr.evicted, tr.cache.snapshot(),
+                              int(tr.attempts.sum())))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(101)
+    L = kve.Layer.empty(bh, cap, d, dev, gumbel=True)
+    bulk_state(L, n, w, gen)
+    for s in samples:
+        load_state_into(L, s.hh, s.init)
+    nk, nv = synth.bulk_kv_torch(w, next_pos, 1, bh, gen, dev)
+    nk, nv = nk[0].contiguous(), nv[0].contiguous()
+    for s in samples:
+        nk[s.hh] = torch.from_numpy(s.ks[0].view(np.float16)).to(dev)
+        nv[s.hh] = torch.from_numpy(s.vs[0].view(np.float16)).to(dev)
+    ev = torch.full((bh,), -7, dtype=torch.int32, device=dev)
+    ctr = kve.Counters(n, next_pos, next_pos)
+    prm = params_for(w, budget, 0)
+    kve.keyformer_step(L, nk, nv, ctr, budget, n_sink, prm.tau_init, prm.tau_end,
+                       prm.anneal_steps, w.rope_base, w.gumbel_seed, ev)
+    torch.cuda.synchronize()
+    evn = ev.cpu().numpy()
+    _assert_parity(L, evn[None, :], samples, next_pos)
+    assert ((evn >= 0) & (evn <= n)).all()
+
 def test_batched_handoff_mixed_budgets_equals_own_moves(dev):
     """kve_step with TOVA scoring and a 200-row window over two layers of 160
     caches with budgets 1500 and 700, one token per call: as one launch (320

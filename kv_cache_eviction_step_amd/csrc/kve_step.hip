@@ -224,29 +224,29 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t x) {
   return lane_u64(x, 0) + lane_u64(x, 16) + lane_u64(x, 32) + lane_u64(x, 48);
 }
 
-// (value, index) pairs: smaller value wins, equal values go to the lower index.
-__device__ __forceinline__ void argmin_merge(float &v, int &i, float v2, int i2) {
-  if (v2 < v || (v2 == v && i2 < i)) {
-    v = v2;
-    i = i2;
-  }
+// (value, index) pairs as one 64-bit key whose unsigned order is the pairs'
+// order: smaller value first, equal values by the lower index.  The value's
+// bits map to an unsigned integer of the same order (non-negative floats get
+// the sign bit set, negative ones have every bit flipped); -0 is made +0
+// first, so that it ties with +0 as the float comparison has it.  Values are
+// never NaN.
+__device__ __forceinline__ uint64_t argkey(float v, int i) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v + 0.0f);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)i;
 }
+__device__ __forceinline__ uint64_t min_u64(uint64_t a, uint64_t b) { return b < a ? b : a; }
 template <int CTRL>
-__device__ __forceinline__ void argmin_dpp(float &v, int &i) {
-  argmin_merge(v, i, dpp<CTRL>(v), dpp_i<CTRL>(i));
+__device__ __forceinline__ uint64_t min_dpp_u64(uint64_t x) {
+  return min_u64(x, dpp_u64<CTRL>(x));
 }
-__device__ __forceinline__ void wave_argmin(float &v, int &i) {
-  argmin_dpp<0xB1>(v, i);
-  argmin_dpp<0x4E>(v, i);
-  argmin_dpp<0x141>(v, i);
-  argmin_dpp<0x140>(v, i);
-  float bv = lane_f(v, 0);
-  int bi = __builtin_amdgcn_readlane(i, 0);
-  argmin_merge(bv, bi, lane_f(v, 16), __builtin_amdgcn_readlane(i, 16));
-  argmin_merge(bv, bi, lane_f(v, 32), __builtin_amdgcn_readlane(i, 32));
-  argmin_merge(bv, bi, lane_f(v, 48), __builtin_amdgcn_readlane(i, 48));
-  v = bv;
-  i = bi;
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t x) {
+  x = min_dpp_u64<0xB1>(x);
+  x = min_dpp_u64<0x4E>(x);
+  x = min_dpp_u64<0x141>(x);
+  x = min_dpp_u64<0x140>(x);
+  return min_u64(min_u64(lane_u64(x, 0), lane_u64(x, 16)),
+                 min_u64(lane_u64(x, 32), lane_u64(x, 48)));
 }
 
 // Reductions of the W per-wave partials held by lanes 0..W-1 (identity
@@ -271,13 +271,13 @@ __device__ __forceinline__ uint64_t partials_sum(uint64_t x) {
   return lane_u64(x, 0);
 }
 template <int W>
-__device__ __forceinline__ int partials_argmin(float v, int i) {
+__device__ __forceinline__ uint64_t partials_min_u64(uint64_t x) {
   static_assert(W >= 1 && W <= 16 && (W & (W - 1)) == 0, "partials");
-  if constexpr (W > 1) argmin_dpp<0xB1>(v, i);
-  if constexpr (W > 2) argmin_dpp<0x4E>(v, i);
-  if constexpr (W > 4) argmin_dpp<0x141>(v, i);
-  if constexpr (W > 8) argmin_dpp<0x140>(v, i);
-  return __builtin_amdgcn_readlane(i, 0);
+  if constexpr (W > 1) x = min_dpp_u64<0xB1>(x);
+  if constexpr (W > 2) x = min_dpp_u64<0x4E>(x);
+  if constexpr (W > 4) x = min_dpp_u64<0x141>(x);
+  if constexpr (W > 8) x = min_dpp_u64<0x140>(x);
+  return lane_u64(x, 0);
 }
 
 // The softmax normaliser is summed exactly: each weight w in [0, 1] as the
@@ -371,8 +371,7 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   // one slot per wave for each reduction of the step (written once per step)
   __shared__ float red_m[NWAVE];
   __shared__ uint64_t red_z[NWAVE];
-  __shared__ float red_a[NWAVE];
-  __shared__ int red_i[NWAVE];
+  __shared__ uint64_t red_k[NWAVE];
   __shared__ float rn_c[kMaxHalfD];          // incoming row's rotation (wave 0 only)
   __shared__ float rn_s[kMaxHalfD];
 
@@ -520,11 +519,28 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   if (lane == 0) red_m[wave] = mx;
   __syncthreads();                              // also: every logit is in LDS
   mx = partials_max<NWAVE>(lane < NWAVE ? red_m[lane] : -INFINITY);
+  // The weights stay in this thread's registers (rows i = tid + k*NT, as the
+  // scores) when the slots are few; large caches, whose registers the score
+  // slots already fill, keep them in LDS in place of the logits.
+  constexpr bool WREG = R <= 8;
+  float wreg[WREG ? R : 1];
   uint64_t sum = 0;
-  for (int i = tid; i < n; i += NT) {
-    const float w = expf(lds_x[i] - mx);
-    lds_x[i] = w;
-    sum += (uint64_t)rintf(w * kZScale);
+  if constexpr (WREG) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int i = tid + k * NT;
+      if (i < n) {
+        const float w = expf(lds_x[i] - mx);
+        wreg[k] = w;
+        sum += (uint64_t)rintf(w * kZScale);
+      }
+    }
+  } else {
+    for (int i = tid; i < n; i += NT) {
+      const float w = expf(lds_x[i] - mx);
+      lds_x[i] = w;
+      sum += (uint64_t)rintf(w * kZScale);
+    }
   }
   sum = wave_sum_u64(sum);
   if (lane == 0) red_z[wave] = sum;
@@ -548,7 +564,7 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   for (int k = 0; k < R; ++k) {
     const int i = tid + k * NT;
     if (i < n) {
-      const float pi = lds_x[i] * rz;
+      const float pi = (WREG ? wreg[k] : lds_x[i]) * rz;
       const float s = current ? pi : sreg[k] + pi;
       sreg[k] = s;
       if (over && i >= n_sink && i <= last) {
@@ -560,18 +576,16 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
       }
     }
   }
+  uint64_t best = argkey(bv, bi);
   if (over && tid == 0 && last == n) {     // the new row: score 0
     const float key = GUMBEL ? fmaf(tau, g_new, 0.0f) : 0.0f;
-    argmin_merge(bv, bi, key, n);
+    best = min_u64(best, argkey(key, n));
   }
-  wave_argmin(bv, bi);
-  if (lane == 0) {
-    red_a[wave] = bv;
-    red_i[wave] = bi;
-  }
+  best = wave_min_u64(best);
+  if (lane == 0) red_k[wave] = best;
   __syncthreads();
-  const int arg = partials_argmin<NWAVE>(lane < NWAVE ? red_a[lane] : INFINITY,
-                                         lane < NWAVE ? red_i[lane] : 0x7fffffff);
+  const int arg =
+      (int)(uint32_t)partials_min_u64<NWAVE>(lane < NWAVE ? red_k[lane] : ~(uint64_t)0);
   const int e = over ? arg : -1;
   // The incoming row moves (from next_pos to slot n-1) only when an older row
   // was evicted; only then is its rotation needed.

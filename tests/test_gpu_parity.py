@@ -763,6 +763,53 @@ def test_policy_layers_tokens_equals_single(dev, kind, recent, S):
                 (l, name)
 
 
+@pytest.mark.parametrize("kind,d,n,recent,bh,sampled", [
+    ("tova", 128, 1500, 16, 6, None),              # 8 score slots per thread; a long in-place move
+    ("pyramid", 64, 5000, 8, 3, None),             # 24 slots: the weights go through LDS
+    ("tova", 128, 700, 200, 300, [0, 37, 150, 299]),   # 300 caches: the moves are handed over
+])
+def test_exact_tie_goes_to_lowest_candidate(dev, kind, d, n, recent, bh, sampled):
+    """Every stored key the same vector: every stored row gets the same softmax
+    weight, exactly 1/n on both sides, so every candidate row has the same
+    eviction key (TOVA: the weight; H2O: equal old scores plus the weight).
+    With a window the new row is no candidate, and the lowest candidate row,
+    n_sink, must go in every cache, whichever wave and score slot holds it.
+    Sampled caches are compared with the oracle in full."""
+    import kv_cache_eviction_step_amd as kve
+    n_sink, budget, next_pos, cap = 4, n, 10_000, n + 1
+    w = _wl(f"tie-{kind}", kind, d, 64, 0, budget, recent, heads=bh)
+    hhs = list(range(bh)) if sampled is None else sampled
+    _say(f"[exact tie] kind={kind} d={d} n={n} recent={recent} bh={bh} sampled={hhs}")
+    L = kve.Layer.empty(bh, cap, d, dev, gumbel=False)
+    nk = torch.empty((bh, d), dtype=torch.float16)
+    nv = torch.empty((bh, d), dtype=torch.float16)
+    samples = []
+    for hh in range(bh):
+        c = random_state(w, 0, hh, n, cap, next_pos, seed=hh + 3)
+        c.k[:n] = c.k[0]
+        c.s[:n] = 1.5
+        init = c.snapshot()
+        load_state_into(L, hh, init)
+        if hh in hhs:
+            tr = guarded_trajectory(w, 0, hh, budget, 1, cap=cap, t0=next_pos, cache=c,
+                                    params=params_for(w, budget, hh), min_margin_rel=-1.0)
+            assert tr.evicted[0] == n_sink
+            samples.append(Sample(hh, budget, init, tr.ks, tr.vs, tr.evicted,
+                                  tr.cache.snapshot(), int(tr.attempts.sum())))
+            k1, v1 = tr.ks[0], tr.vs[0]
+        else:
+            k1, v1 = (x[0] for x in synth.token_kv(w, 0, hh, [next_pos]))
+        nk[hh] = torch.from_numpy(k1.view(np.float16))
+        nv[hh] = torch.from_numpy(v1.view(np.float16))
+    ev = torch.full((bh,), -7, dtype=torch.int32, device=dev)
+    batch = kve.LayerBatch([L], [budget], [kve.Counters(n, next_pos, next_pos)])
+    kve.step(batch, [nk.to(dev)], [nv.to(dev)], policy_for(w), [ev])
+    torch.cuda.synchronize()
+    evn = ev.cpu().numpy()[None, :]
+    assert bool((evn == n_sink).all()), np.unique(evn)
+    _assert_parity(L, evn, samples, next_pos)
+
+
 def test_policy_plain_equals_named_entry_points(dev):
     """kve_step with recent 0 and the cumulative score is keyformer_step /
     pyramid_step, bit for bit."""

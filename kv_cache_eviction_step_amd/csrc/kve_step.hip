@@ -365,8 +365,9 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   static_assert(NT % 64 == 0 && RPS * LPR == NT && RPM * LPM == NT && U % CPL == 0,
                 "launch shape");
 
-  // LDS: logits -> weights [np].  Scores and Gumbel values of the rows
-  // i = tid + k*NT, k < R (R*NT >= n), live in this thread's registers.
+  // LDS: the logits [np] (then, past 8 slots per thread, the weights).
+  // Scores and Gumbel values of the rows i = tid + k*NT, k < R (R*NT >= n),
+  // live in this thread's registers.
   extern __shared__ float lds[];
   // one slot per wave for each reduction of the step (written once per step)
   __shared__ float red_m[NWAVE];

@@ -664,6 +664,50 @@ def test_layers_tokens_full_trajectory_oracle(dev, wi, layers):
 
 
 
+@pytest.mark.parametrize("wi,beta", [(1, None), (2, None), (2, 1.0)],
+                         ids=["keyformer", "pyramid-beta2", "pyramid-beta1"])
+def test_every_cache_every_layer_llama_shapes(dev, wi, beta):
+    """The Llama-3.2-3B-shaped workloads in full: all 28 layers x 8 caches
+    (224 caches) through the whole 2048 + 1024-token stream, all layers in one
+    launch per 64 tokens, every cache against the oracle.  PyramidKV runs at
+    beta 2 (budgets 1019 ... 5) and at beta 1 (every layer 512)."""
+    import dataclasses
+    import kv_cache_eviction_step_amd as kve
+    w = synth.WORKLOADS[wi]
+    if beta is not None:
+        w = dataclasses.replace(w, name=f"{w.name}-beta{beta:g}", beta=beta)
+    kf = w.kind == "keyformer"
+    S, T = 64, w.tokens
+    budgets = w.budgets(oracle.pyramid_budgets)
+    _say(f"[every cache] {w.name} layers={w.layers} bh={w.bh} budgets={budgets[0]}..{budgets[-1]} "
+         f"T={T}: oracle")
+    picks = {l: list(range(w.bh)) for l in range(w.layers)}
+    samples = oracle_samples_layers(w, picks, budgets, T, init_n=False)
+    _say(f"[every cache] {w.name}: GPU")
+    Ls = [kve.Layer.empty(w.bh, b + 1, w.d, dev, gumbel=kf) for b in budgets]
+    nk = [torch.stack([torch.from_numpy(s.ks.view(np.float16)) for s in samples[l]], 1).to(dev)
+          for l in range(w.layers)]
+    nv = [torch.stack([torch.from_numpy(s.vs.view(np.float16)) for s in samples[l]], 1).to(dev)
+          for l in range(w.layers)]
+    ev = torch.full((w.layers, T, w.bh), -7, dtype=torch.int32, device=dev)
+    batch = kve.LayerBatch(Ls, budgets)
+    prm = params_for(w, budgets[0], 0)
+    for t0 in range(0, T, S):
+        ks = [x[t0:t0 + S] for x in nk]
+        vs = [x[t0:t0 + S] for x in nv]
+        es = [ev[l, t0:t0 + S] for l in range(w.layers)]
+        if kf:
+            kve.keyformer_step_layers_tokens(batch, ks, vs, w.n_sink, prm.tau_init, prm.tau_end,
+                                             prm.anneal_steps, w.rope_base, w.gumbel_seed, es)
+        else:
+            kve.pyramid_step_layers_tokens(batch, ks, vs, w.n_sink, w.rope_base, es)
+    torch.cuda.synchronize()
+    evh = ev.cpu().numpy()
+    for l in range(w.layers):
+        _assert_parity(Ls[l], evh[l], samples[l], 0)
+        assert batch.ctrs[l].n_kept == budgets[l]
+
+
 # ---------------------------------------------------------------------------
 # the general entry point: recent window and TOVA-adapted scoring
 # ---------------------------------------------------------------------------

@@ -82,22 +82,39 @@ def oracle_samples(w: synth.Workload, layer: int, hhs, budget: int, T: int, cap:
         return list(ex.map(_sample_job, jobs))
 
 
+def _sample_job_next(args) -> Sample:
+    """_sample_job for cache hh, or else for the first of the next `tries` - 1
+    caches whose whole stream can be guarded: over a long stream, a near-tie
+    between two stored rows may be one that no redraw of the incoming token
+    moves past the margin, and such a cache has no unique answer to compare."""
+    (w, layer, hh, *rest), tries = args[:-1], args[-1]
+    for k in range(tries):
+        try:
+            return _sample_job((w, layer, (hh + k) % w.bh, *rest))
+        except RuntimeError:
+            if k == tries - 1:
+                raise
+    raise AssertionError("unreachable")
+
+
 def oracle_samples_layers(w: synth.Workload, picks: dict, budgets, T: int, init_n: bool,
-                          next_pos: int = 0) -> dict:
+                          next_pos: int = 0, tries: int = 1) -> dict:
     """oracle_samples for several layers at once (one pool): picks[l] lists the
-    sampled caches of layer l, budgets[l] its budget; init_n: start full."""
+    sampled caches of layer l, budgets[l] its budget; init_n: start full.
+    tries > 1: a pick whose stream cannot be guarded moves on to the next
+    cache (up to tries - 1 times)."""
     jobs, keys = [], []
     for l, hhs in picks.items():
         for hh in hhs:
             jobs.append((w, l, hh, budgets[l], T, budgets[l] + 1,
-                         budgets[l] if init_n else None, next_pos))
+                         budgets[l] if init_n else None, next_pos, tries))
             keys.append(l)
     workers = min(len(jobs), max(1, min(16, (os.cpu_count() or 2) - 1)))
     if workers <= 1:
-        res = [_sample_job(j) for j in jobs]
+        res = [_sample_job_next(j) for j in jobs]
     else:
         with ProcessPoolExecutor(workers) as ex:
-            res = list(ex.map(_sample_job, jobs))
+            res = list(ex.map(_sample_job_next, jobs))
     out: dict = {}
     for l, smp in zip(keys, res):
         out.setdefault(l, []).append(smp)

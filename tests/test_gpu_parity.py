@@ -397,16 +397,16 @@ def test_whole_run_late_riser_every_layer(dev):
 
 def test_full_size_tokens_long_context_every_layer(dev):
     """The long-context workload, all 32 layers (budgets 6144 .. 2048) x 16
-    tokens in one launch (keys streamed, 1024-thread workgroups), one sampled
-    cache per layer."""
+    tokens per launch (keys streamed, 1024-thread workgroups), four launches,
+    one sampled cache per layer."""
     w = synth.WORKLOADS[4]
     budgets = oracle.pyramid_budgets(w.layers, w.budget, w.n_sink, w.beta)
-    T, next_pos = 16, w.prompt
+    T, next_pos = 64, w.prompt
     picks = {l: [(11 + 53 * l) % w.bh] for l in range(w.layers)}
-    _say(f"[full-tokens] {w.name} layers={w.layers} bh={w.bh} one cache per layer T={T} S={T}")
+    _say(f"[full-tokens] {w.name} layers={w.layers} bh={w.bh} one cache per layer T={T} S=16")
     samples = oracle_samples_layers(w, picks, budgets, T, True, next_pos)
     layers, ev, _ = run_batched(w, list(range(w.layers)), budgets, T, samples, 1, next_pos, dev,
-                                tokens_per_call=T)
+                                tokens_per_call=16)
     errs = []
     for l, ss in samples.items():
         for s in ss:

@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--whole-run", action="store_true",
                     help="time the whole trajectory instead (prompt + decode from empty "
                          "caches, token by token; --steps / --warmup / --fill unused)")
+    ap.add_argument("--skip-whole-run", action="store_true",
+                    help="after the K timed steps, do not also time the whole trajectory "
+                         "(reported as the line's 'whole_run' object)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the CPU oracle baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -383,6 +386,23 @@ def main():
     out["config"]["steady_state_fill"] = args.fill
     out["config"]["fill_seconds"] = round(t_fill, 1)
     out["context"] = bandwidth_context(dev)
+    if not args.skip_whole_run:
+        # the same calls again from empty caches (the tensors are reused: a
+        # cache reads only its first n_kept rows), CPU baseline not repeated
+        del nk, nv, ev
+        for l in range(L):
+            set_counters(l, kve.Counters(0, 0, 0))
+        wr_args = argparse.Namespace(**{**vars(args), "cpu_seconds": 0})
+        wr = whole_run(wr_args, w, budgets, bh, L, d, TPC, call, ctr, batch, entry, stream, gen,
+                       dev, print_line=False)
+        out["whole_run"] = {
+            "value": wr["value"], "unit": wr["unit"], "tokens": w.tokens,
+            "seconds": wr["steps"] * wr["ms_per_step"] / 1e3,
+            "achieved_GBs": wr["roofline"]["achieved"], "frac": wr["roofline"]["frac"],
+            "avg_launch_us": wr["roofline"]["avg_launch_us"],
+            "mean_rows_moved_per_cache_step": wr["config"]["mean_rows_moved_per_cache_step"],
+            "timing": wr["config"]["timing"],
+        }
     print(json.dumps(out), flush=True)
 
 
@@ -435,7 +455,8 @@ def result_line(args, w, budgets, bh, L, d, TPC, batch, entry, steps, warmup, ms
     }
 
 
-def whole_run(args, w, budgets, bh, L, d, TPC, call, ctr, batch, entry, stream, gen, dev):
+def whole_run(args, w, budgets, bh, L, d, TPC, call, ctr, batch, entry, stream, gen, dev,
+              print_line: bool = True):
     """The whole trajectory -- every prompt token appended one by one, then the
     decode tokens -- from empty caches.  Inputs are generated on the device 64
     tokens (all layers) at a time, between the timed parts: HIP events bracket
@@ -491,7 +512,9 @@ def whole_run(args, w, budgets, bh, L, d, TPC, call, ctr, batch, entry, stream, 
     out["config"]["timing"] = (f"whole run: {w.prompt} prompt + {w.decode} decode tokens from "
                                f"empty caches, HIP events around the launches of each "
                                f"{chunk}-token chunk, summed")
-    print(json.dumps(out), flush=True)
+    if print_line:
+        print(json.dumps(out), flush=True)
+    return out
 
 
 if __name__ == "__main__":

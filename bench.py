@@ -177,8 +177,20 @@ def cpu_baseline(w, budgets, seconds: float):
         "sample": (f"{procs} caches (one per process, layers {layers[0]}..{layers[-1]}), each "
                    f"from a synthetic steady state at its layer budget, stepped token by token "
                    f"for ~{seconds / 2:.0f} s; single_core = one such cache alone"),
-        "cpu": platform.processor() or platform.machine(),
+        "cpu": cpu_model(),
     }
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), else the machine type."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def _cpu_worker(args):

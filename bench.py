@@ -195,11 +195,10 @@ def cpu_model() -> str:
 
 def _cpu_worker(args):
     w, layer, budget, seconds = args
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
     import numpy as np
     import synth
-    from gpu_harness import random_state
     from oracle.guard import params_for
+    from oracle.states import random_state
     c = random_state(w, layer, 0, budget, budget + 1, w.prompt)
     prm = params_for(w, budget, 0)
     ks, vs = synth.token_kv(w, layer, 0, np.arange(w.prompt, w.prompt + 4096))

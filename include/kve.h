@@ -30,18 +30,15 @@
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and the call returns without synchronising.  Results are visible to
  *     later work on the same stream; synchronise before reading elsewhere.
- *   - The calls keep no state besides small per-thread caches of rotation
- *     frequencies and, in single-token launches that hand long compactions
- *     to a second kernel (Keyformer noise, TOVA scoring or a window longer
- *     than 128 rows, on at least 256 caches, with some cache at its
- *     budget), a per-device scratch buffer: allocated on the first such call
- *     on a device, grown (after a device synchronisation) when a later call
- *     needs more, shared by every stream with an event ordering its users.
- *     A call on a stream under capture never uses it (its launch compacts in
- *     place), so every call can be captured into a graph and replayed (the
- *     host counters advance at capture, not at replay).  Other calls
- *     allocate nothing: the batched forms pass their layer descriptors by
- *     value with the launch.  All calls are reentrant.
+ *   - The calls allocate nothing, never synchronise, keep no state between
+ *     calls (on the host or the device) and are reentrant.  The batched forms
+ *     pass their layer descriptors by value with the launch.  Every call can
+ *     be captured into a graph and replayed (the host counters advance at
+ *     capture, not at replay).
+ *   - Compaction is done in place by each cache's workgroup.  Large
+ *     single-token launches run faster when their long compactions are
+ *     spread over the GPU by a second kernel; that needs scratch memory, which
+ *     only kve_step_ws uses, from a workspace the caller owns.
  *   - Arguments are checked on the host before anything is enqueued.  A
  *     failing check returns KVE_EINVAL and leaves the counters and every
  *     tensor untouched.  A device fault is asynchronous and surfaces at the
@@ -59,7 +56,7 @@ extern "C" {
 #define KVE_OK        0
 #define KVE_EINVAL   -1   /* an argument failed a host-side check            */
 #define KVE_ELAUNCH  -2   /* the HIP runtime rejected the kernel launch       */
-#define KVE_ENODEV   -3   /* no HIP device, or the current device is not gfx950 */
+#define KVE_ENODEV   -3   /* no HIP device, or no gfx950 code for the current one */
 
 /* One layer's B*H caches.  Rows of a cache are contiguous, caches follow
  * each other:  element (hh, row, j) of k lives at k[(hh*cap + row)*d + j].
@@ -284,6 +281,55 @@ int kve_step(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
              const void *const *new_k, const void *const *new_v, kve_counters *ctrs,
              const int32_t *budgets, const kve_policy *policy, int32_t *const *evicted,
              void *stream);
+
+/*
+ * kve_step_ws -- kve_step with a caller-owned device workspace, for the
+ * large single-token launches whose long compactions dominate them (the
+ * batched call keyformer_update_batched of the Keyformer page, one token,
+ * with the moves of keyformer_update step 3 spread over the GPU).
+ *
+ * A single-token launch of at least 256 caches whose policy makes long
+ * interior evictions routine (Keyformer noise, TOVA scoring, or a window
+ * longer than 128 rows) hands every move of more than 128 rows to a second
+ * kernel enqueued right after the step on `stream`: the step reserves one
+ * workspace item per 64-row chunk of the move and parks the few rows the
+ * chunks would otherwise race on, and the move kernel shifts the chunks on
+ * many compute units at once.  The results are the same bits as kve_step's;
+ * other launches (several tokens, fewer caches, other policies) ignore the
+ * workspace.  A cache whose reservation does not fit in the workspace
+ * compacts in place, so any size of at least one item is correct, and
+ * kve_workspace_size gives the size at which every move can be handed over.
+ *
+ *   workspace        device memory owned by the caller, 256-byte aligned,
+ *                    or NULL (then workspace_bytes must be 0 and the call is
+ *                    kve_step)
+ *   workspace_bytes  its size
+ *   other arguments  as kve_step
+ * Contract: the workspace must be all zero bytes before its first use (for
+ * example torch.zeros); every call returns it to that state once its work
+ * on `stream` has finished, so nothing needs clearing between calls.  Calls
+ * that use one workspace must be ordered (the same stream, or events):
+ * overlapping calls race.  After a KVE_ELAUNCH the layers' tensors and the
+ * workspace are undefined: zero the workspace before using it again.
+ * Returns as kve_step; KVE_EINVAL also for a misaligned workspace or one
+ * too small to hold a single item.
+ */
+int kve_step_ws(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
+                const void *const *new_k, const void *const *new_v, kve_counters *ctrs,
+                const int32_t *budgets, const kve_policy *policy, int32_t *const *evicted,
+                void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * kve_workspace_size -- bytes of workspace with which kve_step_ws hands over
+ * every long move of a single-token launch over `caches` caches (the sum of
+ * bh over its layers) whose budgets are at most max_budget, at head
+ * dimension d: one 32-byte item and one parked 4*d-byte row per 64-row chunk
+ * of each cache's longest possible move (max_budget - 1 rows), plus 256
+ * bytes of counters, each part 256-byte aligned.  Returns -1 for caches < 1,
+ * max_budget outside 1 .. 12288, d not 64 or 128, or a size past 2^30 items.
+ * Pure host arithmetic; needs no device.
+ */
+int64_t kve_workspace_size(int64_t caches, int32_t max_budget, int32_t d);
 
 /*
  * pyramid_budgets -- per-layer budgets ("The budget schedule"): a linear taper

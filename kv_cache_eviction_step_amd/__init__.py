@@ -18,6 +18,9 @@ Calls (same names as the C ABI):
                           tau_end, anneal_steps, rope_base, seed, evicted=None, stream=None)
     pyramid_step_tokens(layer, new_k[S], new_v[S], ctr, budget, n_sink, rope_base,
                         evicted=None, stream=None)
+    step(batch, new_k, new_v, policy, evicted=None, stream=None, n_tokens=None,
+         workspace=None)                     (kve_step / kve_step_ws)
+    workspace_size(caches, max_budget, d), workspace(caches, max_budget, d, device)
     pyramid_budgets(n_layers, avg_budget, n_sink, beta) -> list[int]
 """
 from __future__ import annotations
@@ -117,6 +120,13 @@ _lib.kve_step.argtypes = [
     ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(KveLayer), ctypes.c_void_p, ctypes.c_void_p,
     ctypes.POINTER(Counters), ctypes.c_void_p, ctypes.POINTER(Policy), ctypes.c_void_p,
     ctypes.c_void_p]
+_lib.kve_step_ws.restype = ctypes.c_int
+_lib.kve_step_ws.argtypes = [
+    ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(KveLayer), ctypes.c_void_p, ctypes.c_void_p,
+    ctypes.POINTER(Counters), ctypes.c_void_p, ctypes.POINTER(Policy), ctypes.c_void_p,
+    ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+_lib.kve_workspace_size.restype = ctypes.c_int64
+_lib.kve_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
 _lib.kve_kept_indices.restype = ctypes.c_int32
 _lib.kve_kept_indices.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                   ctypes.c_void_p]
@@ -132,7 +142,8 @@ _lib.kve_strerror.argtypes = [ctypes.c_int]
 
 EXPORTED = ("keyformer_step", "pyramid_step", "keyformer_step_layers", "pyramid_step_layers",
             "keyformer_step_tokens", "pyramid_step_tokens", "keyformer_step_layers_tokens",
-            "pyramid_step_layers_tokens", "kve_step", "pyramid_budgets", "kve_kept_indices",
+            "pyramid_step_layers_tokens", "kve_step", "kve_step_ws", "kve_workspace_size",
+            "pyramid_budgets", "kve_kept_indices",
             "kve_fp16_bytes", "kve_full_fp16_bytes", "kve_strerror")
 
 
@@ -518,17 +529,47 @@ def policy(kind: str, n_sink: int, recent: int = 0, tau_init: float = 0.0, tau_e
 
 
 def step(batch: LayerBatch, new_k, new_v, pol: Policy, evicted=None, stream=None,
-         n_tokens: int | None = None) -> None:
-    """kve_step over every layer of `batch`.
+         n_tokens: int | None = None, workspace=None) -> None:
+    """kve_step over every layer of `batch` (kve_step_ws with a workspace).
 
     n_tokens None: one token, inputs as keyformer_step_layers; n_tokens S:
-    S tokens, inputs as keyformer_step_layers_tokens."""
+    S tokens, inputs as keyformer_step_layers_tokens.  workspace: a tensor
+    from workspace() on the layers' device, or None."""
     S = 1 if n_tokens is None else n_tokens
     pe = batch._fill(new_k, new_v, evicted, n_tokens)
-    rc = _lib.kve_step(batch.n, S, batch.c_layers, batch._pk, batch._pv, batch.ctrs,
-                       batch.budgets, ctypes.byref(pol), pe,
-                       _stream_ptr(stream, batch.layers[0]))
-    _check(rc, "kve_step")
+    st = _stream_ptr(stream, batch.layers[0])
+    if workspace is None:
+        rc = _lib.kve_step(batch.n, S, batch.c_layers, batch._pk, batch._pv, batch.ctrs,
+                           batch.budgets, ctypes.byref(pol), pe, st)
+        _check(rc, "kve_step")
+        return
+    if (workspace.dtype is not torch.uint8 or workspace.dim() != 1 or
+            not workspace.is_contiguous() or workspace.get_device() != batch._dev):
+        raise ValueError("workspace must be a contiguous uint8 tensor on the layers' device "
+                         "(see workspace())")
+    rc = _lib.kve_step_ws(batch.n, S, batch.c_layers, batch._pk, batch._pv, batch.ctrs,
+                          batch.budgets, ctypes.byref(pol), pe, workspace.data_ptr(),
+                          workspace.numel(), st)
+    _check(rc, "kve_step_ws")
+
+
+def workspace_size(caches: int, max_budget: int, d: int) -> int:
+    """kve_workspace_size: bytes with which kve_step_ws hands over every long
+    move of a single-token launch over `caches` caches at budgets <= max_budget."""
+    r = _lib.kve_workspace_size(caches, max_budget, d)
+    if r < 0:
+        raise ValueError("workspace_size: invalid arguments")
+    return int(r)
+
+
+def workspace(caches: int, max_budget: int, d: int, device) -> "torch.Tensor":
+    """A zeroed device workspace of workspace_size(caches, max_budget, d) bytes
+    for step(..., workspace=...).  Calls return it to zero when their work is
+    done; reuse it for every call on one stream."""
+    n = workspace_size(caches, max_budget, d)
+    t = torch.zeros(n + 256, dtype=torch.uint8, device=device)
+    off = (-t.data_ptr()) % 256                   # the library wants 256-byte alignment
+    return t[off:off + n]
 
 
 def kept_indices(n_prev: int, evicted) -> list[int]:

@@ -1,16 +1,15 @@
 // kve_api.hip -- host side of the C ABI declared in include/kve.h:
 // argument checks, the eviction policy, fp64 rotation constants and
 // frequencies, the launches on the caller's stream, the counter update, the
-// move scratch of large single-token launches, and the host-only helpers
-// (pyramid budget schedule, kept indices, byte accounting).
+// caller-owned move workspace of large single-token launches, and the
+// host-only helpers (pyramid budget schedule, kept indices, byte accounting).
+// Nothing here allocates, synchronises or keeps state between calls.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <algorithm>
 #include <cstring>
-#include <mutex>
 
 #include "kve.h"
 #include "kve_step.h"
@@ -26,43 +25,25 @@ constexpr int32_t kMaxBudget = kve::kMaxRows;
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Rotation frequencies base^(-2j/d) and the fp32 cosine / sine of a rotation
-// by -1 position, for the last (d, base) seen on this thread.
-struct FreqCache {
-  int d = 0;
-  double base = 0.0;
-  double freq[kve::kMaxHalfD];
-  float cos_m1[kve::kMaxHalfD];
-  float sin_m1[kve::kMaxHalfD];
-};
-thread_local FreqCache tl_freq;
-
-const FreqCache &freqs(int d, double base) {
-  FreqCache &c = tl_freq;
-  if (c.d != d || c.base != base) {
-    for (int j = 0; j < d / 2; ++j) {
-      c.freq[j] = std::pow(base, -(2.0 * (double)j) / (double)d);
-      const double th = -1.0 * c.freq[j];
-      c.cos_m1[j] = (float)std::cos(th);
-      c.sin_m1[j] = (float)std::sin(th);
-    }
-    c.d = d;
-    c.base = base;
+// by -1 position, evaluated per call with the host's fp64 libm (a few
+// microseconds; only calls in which some cache can evict need them).
+void rope_tables(int d, double base, double *freq, float *cos_m1, float *sin_m1) {
+  for (int j = 0; j < d / 2; ++j) {
+    freq[j] = std::pow(base, -(2.0 * (double)j) / (double)d);
+    const double th = -1.0 * freq[j];
+    cos_m1[j] = (float)std::cos(th);
+    sin_m1[j] = (float)std::sin(th);
   }
-  return c;
 }
 
-int check_device() {
-  static std::atomic<int> state[128];        // 0 unknown, 1 gfx950, -1 other
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 128) return KVE_ENODEV;
-  int s = state[dev].load(std::memory_order_relaxed);
-  if (s == 0) {
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return KVE_ENODEV;
-    s = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
-    state[dev].store(s, std::memory_order_relaxed);
-  }
-  return s == 1 ? KVE_OK : KVE_ENODEV;
+// A HIP error of a launch as a KVE_* code: no device, or no gfx950 code for
+// the current one, is KVE_ENODEV; anything else KVE_ELAUNCH.
+int launch_error(hipError_t err) {
+  if (err == hipSuccess) return KVE_OK;
+  if (err == hipErrorNoDevice || err == hipErrorNoBinaryForGpu ||
+      err == hipErrorInvalidDeviceFunction || err == hipErrorInvalidDevice)
+    return KVE_ENODEV;
+  return KVE_ELAUNCH;
 }
 
 // Everything about a call that is not per layer: the eviction rule and the
@@ -153,7 +134,7 @@ kve::LayerArgs layer_args(const kve_layer *L, const void *new_k, const void *new
   return a;
 }
 
-kve::SharedArgs shared_args(int d, const Policy &p) {
+kve::SharedArgs shared_args(int d, const Policy &p, bool evicts) {
   kve::SharedArgs sa;
   std::memset(&sa, 0, sizeof(sa));
   sa.n_sink = p.n_sink;
@@ -164,16 +145,12 @@ kve::SharedArgs shared_args(int d, const Policy &p) {
   sa.tau_end = p.gumbel ? p.tau_end : 0.0;
   sa.seed = p.seed;
   sa.scale = (float)(1.0 / std::sqrt((double)d));
-  // keyformer FIXED GAP #2: moved stored rows go back one position
-  const FreqCache &fc = freqs(d, p.rope_base);
-  for (int j = 0; j < d / 2; ++j) {
-    sa.back1.c[j] = fc.cos_m1[j];
-    sa.back1.s[j] = fc.sin_m1[j];
-    // The incoming row, if it survives an older row's eviction, goes from
-    // next_pos to slot n-1: the device rotates it by (n-1-next_pos) * freq[j]
-    // with an fp64 sincos rounded once to fp32.
-    sa.freq[j] = fc.freq[j];
-  }
+  // keyformer FIXED GAP #2: moved stored rows go back one position.  The
+  // incoming row, if it survives an older row's eviction, goes from next_pos
+  // to slot n-1: the device rotates it by (n-1-next_pos) * freq[j] with an
+  // fp64 sincos rounded once to fp32.  Nothing moves in a call in which no
+  // cache is at its budget, and such a call leaves the tables unset.
+  if (evicts) rope_tables(d, p.rope_base, sa.freq, sa.back1.c, sa.back1.s);
   return sa;
 }
 
@@ -184,8 +161,8 @@ void advance(kve_counters *ctr, int32_t budget) {
 }
 
 // ---------------------------------------------------------------------------
-// deferred compactions: single-token launches that hand their long moves to
-// the move kernel (kve_step.h) park rows in a per-device scratch
+// handed-over compactions: single-token launches given a workspace (the
+// kve_step_ws form) hand their long moves to the move kernel (kve_step.h)
 // ---------------------------------------------------------------------------
 
 // Handed over in single-token launches whose policy makes long interior
@@ -201,141 +178,47 @@ bool defers(const Policy &p, int64_t caches) {
   return (p.gumbel || p.current || p.recent > kve::kDeferRows) && caches >= kDeferMinCaches;
 }
 
-// Parked rows per workgroup for budgets up to `budget`: the chunks of the
-// longest move (at most budget - 1 rows).
-int defer_slots(int32_t budget) {
-  return std::max(1, (budget - 1 + kve::kMoveChunk - 1) / kve::kMoveChunk);
-}
-
-struct MoveScratch {
-  std::mutex mu;
-  void *rows = nullptr;
-  kve::MoveItem *items = nullptr;
-  int32_t *count = nullptr;      // [2], zero when allocated
-  int64_t rows_cap = 0;          // bytes
-  int64_t items_cap = 0;         // items
-  int parity = 0;                // the counter the next launch appends to
-  hipEvent_t done = nullptr;     // the last move kernel that used the scratch has finished
-  hipStream_t last = nullptr;    // ... on this stream
-  bool used = false;
-  // A launch that queued moves without its move kernel (a failed launch or
-  // event record) leaves a count that no kernel clears: the device then never
-  // hands moves over again.
-  bool broken = false;
-};
-
-void free_moves(MoveScratch &s) {
-  (void)hipFree(s.rows);
-  (void)hipFree(s.items);
-  (void)hipFree(s.count);
-  s.rows = nullptr;
-  s.items = nullptr;
-  s.count = nullptr;
-  s.rows_cap = s.items_cap = 0;
-  s.parity = 0;
-  s.used = false;
-}
-
-MoveScratch g_moves[128];
-
-// The scratch for `blocks` workgroups with `slots` parked rows of dimension d,
-// ordered after its previous user; false if none can be had (the launch then
-// compacts every cache itself).  s.mu must be held until finish_moves.
-bool move_scratch(MoveScratch &s, int64_t blocks, int slots, int d, hipStream_t stream,
-                  kve::DeferArgs &out) {
-  const int64_t rows_bytes = blocks * slots * 4 * (int64_t)d;
-  const int64_t items = blocks * slots;
-  if (!s.done && hipEventCreateWithFlags(&s.done, hipEventDisableTiming) != hipSuccess) {
-    s.done = nullptr;
-    return false;
-  }
-  if (rows_bytes > s.rows_cap || items > s.items_cap) {
-    const int64_t nr = std::max(rows_bytes, 2 * s.rows_cap);
-    const int64_t ni = std::max(items, 2 * s.items_cap);
-    if (s.rows) {                               // launches in flight may still read them
-      if (hipDeviceSynchronize() != hipSuccess) return false;
-      free_moves(s);
-    }
-    if (hipMalloc(&s.rows, nr) != hipSuccess ||
-        hipMalloc(reinterpret_cast<void **>(&s.items), ni * sizeof(kve::MoveItem)) !=
-            hipSuccess ||
-        hipMalloc(reinterpret_cast<void **>(&s.count), 2 * sizeof(int32_t)) != hipSuccess ||
-        hipMemset(s.count, 0, 2 * sizeof(int32_t)) != hipSuccess) {
-      free_moves(s);
-      return false;
-    }
-    s.rows_cap = nr;
-    s.items_cap = ni;
-  }
-  if (s.used && s.last != stream && hipStreamWaitEvent(stream, s.done, 0) != hipSuccess)
-    return false;
-  out.rows = s.rows;
-  out.items = s.items;
-  out.count = s.count;
-  out.slots = slots;
-  out.parity = s.parity;
-  return true;
-}
-
-// The move kernel after a launch that handed moves over, and the record that
-// later users of the scratch wait for.
-int finish_moves(MoveScratch &s, const kve::SharedArgs &sa, int64_t blocks, int d,
-                 hipStream_t stream) {
-  if (kve::launch_moves(sa.defer, (int)blocks, sa.back1, d, stream) != hipSuccess ||
-      hipEventRecord(s.done, stream) != hipSuccess) {
-    s.broken = true;
-    return KVE_ELAUNCH;
-  }
-  s.last = stream;
-  s.used = true;
-  s.parity ^= 1;
+// A caller's workspace, checked: null items when there is none (every cache
+// then compacts in place).  Returns KVE_EINVAL for a misaligned workspace or a
+// size that is negative or too small to hold one item.
+int make_pool(void *ws, int64_t bytes, int d, kve::MovePool &pool) {
+  pool = kve::MovePool{};
+  if (!ws) return bytes == 0 ? KVE_OK : KVE_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return KVE_EINVAL;
+  const int64_t cap = kve::pool_capacity(bytes, d);
+  if (cap < 1) return KVE_EINVAL;
+  char *base = static_cast<char *>(ws);
+  const int64_t c = std::min<int64_t>(cap, INT32_MAX / 2);
+  pool.count = reinterpret_cast<int32_t *>(base);
+  pool.items = reinterpret_cast<kve::MoveItem *>(base + kve::kPoolHeaderBytes);
+  pool.rows = base + kve::kPoolHeaderBytes + kve::pool_items_bytes(c);
+  pool.cap = (int32_t)c;
   return KVE_OK;
 }
 
-// The scratch of the current device for a launch of `blocks` workgroups at
-// budgets up to `budget`, taken (lock held) when the launch hands moves over.
-// A stream under capture never hands moves over: the queue counter's parity
-// alternates on the host per call, and a replayed graph would keep reusing
-// one parity, so its count would never be cleared.  Such launches compact in
-// place, as launches below the threshold always do.
-MoveScratch *take_moves(const Policy &p, int64_t blocks, int32_t budget, int d,
-                        hipStream_t stream, std::unique_lock<std::mutex> &lock,
-                        kve::SharedArgs &sa) {
-  int dev = 0;
-  if (!defers(p, blocks) || hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 128)
-    return nullptr;
-  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(stream, &capture) != hipSuccess ||
-      capture != hipStreamCaptureStatusNone) {
-    (void)hipGetLastError();                  // so the launch check does not report it
-    return nullptr;
-  }
-  lock = std::unique_lock<std::mutex>(g_moves[dev].mu);
-  if (!g_moves[dev].broken &&
-      move_scratch(g_moves[dev], blocks, defer_slots(budget), d, stream, sa.defer))
-    return &g_moves[dev];
-  sa.defer = kve::DeferArgs{};
-  lock.unlock();
-  return nullptr;
-}
-
 // One layer, one token: the descriptor travels by value with the launch.
+// With a pool (and a policy and size that hand moves over), long moves go to
+// the move kernel that follows the step.
 int step_impl(const kve_layer *L, const void *new_k, const void *new_v, kve_counters *ctr,
-              int32_t budget, const Policy &p, int32_t *evicted, void *stream) {
+              int32_t budget, const Policy &p, int32_t *evicted, const kve::MovePool &pool,
+              void *stream) {
   if (check_policy(p) != KVE_OK) return KVE_EINVAL;
   if (check_layer(L, new_k, new_v, ctr, budget, p) != KVE_OK) return KVE_EINVAL;
-  const int dev_state = check_device();
-  if (dev_state != KVE_OK) return dev_state;
 
+  const bool evicts = ctr->n_kept + 1 > budget;
   const kve::LayerArgs la = layer_args(L, new_k, new_v, ctr, budget, evicted, p.gumbel);
-  kve::SharedArgs sa = shared_args(L->d, p);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  std::unique_lock<std::mutex> lock;
+  kve::SharedArgs sa = shared_args(L->d, p, evicts);
   // a step under its budget evicts nothing, so it has no move to hand over
-  MoveScratch *ms =
-      ctr->n_kept + 1 > budget ? take_moves(p, L->bh, budget, L->d, s, lock, sa) : nullptr;
-  if (kve::launch_step(la, sa, L->bh, L->d, p.gumbel, s) != hipSuccess) return KVE_ELAUNCH;
-  if (ms && finish_moves(*ms, sa, L->bh, L->d, s) != KVE_OK) return KVE_ELAUNCH;
+  const bool hand_over = pool.items && evicts && defers(p, L->bh);
+  if (hand_over) sa.pool = pool;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();                     // report this call's launch, not an older error
+  int rc = launch_error(kve::launch_step(la, sa, L->bh, L->d, p.gumbel, s));
+  if (rc != KVE_OK) return rc;
+  if (hand_over) {
+    rc = launch_error(kve::launch_moves(pool, sa.back1, L->d, s));
+    if (rc != KVE_OK) return rc;
+  }
   advance(ctr, budget);
   return KVE_OK;
 }
@@ -350,7 +233,8 @@ int step_impl(const kve_layer *L, const void *new_k, const void *new_v, kve_coun
 // Checks every layer first.
 int batch_impl(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
                const void *const *new_k, const void *const *new_v, kve_counters *ctrs,
-               const int32_t *budgets, const Policy &p, int32_t *const *evicted, void *stream) {
+               const int32_t *budgets, const Policy &p, int32_t *const *evicted,
+               const kve::MovePool &pool, void *stream) {
   if (n_layers < 1 || n_layers > kve::kMaxBatchLayers) return KVE_EINVAL;
   if (n_tokens < 1 || n_tokens > kve::kMaxTokens) return KVE_EINVAL;
   if (!layers || !new_k || !new_v || !ctrs || !budgets) return KVE_EINVAL;
@@ -381,15 +265,14 @@ int batch_impl(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
       if (start(order[i]) < prev_end) return KVE_EINVAL;
     }
   }
-  const int dev_state = check_device();
-  if (dev_state != KVE_OK) return dev_state;
-
-  const kve::SharedArgs shared = shared_args(d, p);
+  bool any_evicts = false;                    // some layer is at its budget
+  for (int32_t l = 0; l < n_layers; ++l) any_evicts = any_evicts || ctrs[l].n_kept + n_tokens > budgets[l];
+  const kve::SharedArgs shared = shared_args(d, p, any_evicts);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   for (int32_t g0 = 0; g0 < n_layers; g0 += kve::kLaunchLayers) {
     const int32_t g1 = std::min(n_layers, g0 + kve::kLaunchLayers);
     kve::LayerPack pack{};
-    int32_t block0 = 0, max_n = 0, max_budget = 1;
+    int32_t block0 = 0, max_n = 0;
     bool evicts = false;                      // some layer is at its budget
     for (int32_t l = g0; l < g1; ++l) {
       kve::LayerArgs &a = pack.l[l - g0];
@@ -399,18 +282,19 @@ int batch_impl(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
       a.n_tokens = n_tokens;
       block0 += layers[l].bh;
       max_n = std::max(max_n, std::min(ctrs[l].n_kept + n_tokens - 1, budgets[l]));
-      max_budget = std::max(max_budget, budgets[l]);
       evicts = evicts || ctrs[l].n_kept + 1 > budgets[l];
     }
     kve::SharedArgs sa = shared;
-    std::unique_lock<std::mutex> move_lock;
-    MoveScratch *ms = n_tokens == 1 && evicts
-                          ? take_moves(p, block0, max_budget, d, s, move_lock, sa)
-                          : nullptr;
-    if (kve::launch_step_layers(pack, g1 - g0, block0, max_n, n_tokens, sa, d, p.gumbel, s) !=
-        hipSuccess)
-      return KVE_ELAUNCH;
-    if (ms && finish_moves(*ms, sa, block0, d, s) != KVE_OK) return KVE_ELAUNCH;
+    const bool hand_over = pool.items && n_tokens == 1 && evicts && defers(p, block0);
+    if (hand_over) sa.pool = pool;
+    (void)hipGetLastError();                   // report this launch, not an older error
+    int rc = launch_error(
+        kve::launch_step_layers(pack, g1 - g0, block0, max_n, n_tokens, sa, d, p.gumbel, s));
+    if (rc != KVE_OK) return rc;
+    if (hand_over) {
+      rc = launch_error(kve::launch_moves(pool, sa.back1, d, s));
+      if (rc != KVE_OK) return rc;
+    }
     for (int32_t l = g0; l < g1; ++l)
       for (int32_t t = 0; t < n_tokens; ++t) advance(&ctrs[l], budgets[l]);
   }
@@ -426,14 +310,14 @@ KVE_EXPORT int keyformer_step(const kve_layer *L, const void *new_k, const void 
                               void *stream) {
   return step_impl(L, new_k, new_v, ctr, budget,
                    keyformer_policy(n_sink, tau_init, tau_end, anneal_steps, rope_base, seed),
-                   evicted, stream);
+                   evicted, kve::MovePool{}, stream);
 }
 
 KVE_EXPORT int pyramid_step(const kve_layer *L, const void *new_k, const void *new_v,
                             kve_counters *ctr, int32_t budget, int32_t n_sink,
                             double rope_base, int32_t *evicted, void *stream) {
   return step_impl(L, new_k, new_v, ctr, budget, pyramid_policy(n_sink, rope_base), evicted,
-                   stream);
+                   kve::MovePool{}, stream);
 }
 
 KVE_EXPORT int keyformer_step_layers(int32_t n_layers, const kve_layer *layers,
@@ -444,7 +328,7 @@ KVE_EXPORT int keyformer_step_layers(int32_t n_layers, const kve_layer *layers,
                                      void *stream) {
   return batch_impl(n_layers, 1, layers, new_k, new_v, ctrs, budgets,
                     keyformer_policy(n_sink, tau_init, tau_end, anneal_steps, rope_base, seed),
-                    evicted, stream);
+                    evicted, kve::MovePool{}, stream);
 }
 
 KVE_EXPORT int pyramid_step_layers(int32_t n_layers, const kve_layer *layers,
@@ -452,7 +336,7 @@ KVE_EXPORT int pyramid_step_layers(int32_t n_layers, const kve_layer *layers,
                                    kve_counters *ctrs, const int32_t *budgets, int32_t n_sink,
                                    double rope_base, int32_t *const *evicted, void *stream) {
   return batch_impl(n_layers, 1, layers, new_k, new_v, ctrs, budgets,
-                    pyramid_policy(n_sink, rope_base), evicted, stream);
+                    pyramid_policy(n_sink, rope_base), evicted, kve::MovePool{}, stream);
 }
 
 KVE_EXPORT int keyformer_step_tokens(const kve_layer *L, int32_t n_tokens, const void *new_k,
@@ -464,7 +348,7 @@ KVE_EXPORT int keyformer_step_tokens(const kve_layer *L, int32_t n_tokens, const
   int32_t *ev[1] = {evicted};
   return batch_impl(1, n_tokens, L, &new_k, &new_v, ctr, &budget,
                     keyformer_policy(n_sink, tau_init, tau_end, anneal_steps, rope_base, seed),
-                    ev, stream);
+                    ev, kve::MovePool{}, stream);
 }
 
 KVE_EXPORT int pyramid_step_tokens(const kve_layer *L, int32_t n_tokens, const void *new_k,
@@ -474,7 +358,7 @@ KVE_EXPORT int pyramid_step_tokens(const kve_layer *L, int32_t n_tokens, const v
   if (!L) return KVE_EINVAL;
   int32_t *ev[1] = {evicted};
   return batch_impl(1, n_tokens, L, &new_k, &new_v, ctr, &budget,
-                    pyramid_policy(n_sink, rope_base), ev, stream);
+                    pyramid_policy(n_sink, rope_base), ev, kve::MovePool{}, stream);
 }
 
 KVE_EXPORT int keyformer_step_layers_tokens(int32_t n_layers, int32_t n_tokens,
@@ -487,7 +371,7 @@ KVE_EXPORT int keyformer_step_layers_tokens(int32_t n_layers, int32_t n_tokens,
                                             void *stream) {
   return batch_impl(n_layers, n_tokens, layers, new_k, new_v, ctrs, budgets,
                     keyformer_policy(n_sink, tau_init, tau_end, anneal_steps, rope_base, seed),
-                    evicted, stream);
+                    evicted, kve::MovePool{}, stream);
 }
 
 KVE_EXPORT int pyramid_step_layers_tokens(int32_t n_layers, int32_t n_tokens,
@@ -497,18 +381,18 @@ KVE_EXPORT int pyramid_step_layers_tokens(int32_t n_layers, int32_t n_tokens,
                                           double rope_base, int32_t *const *evicted,
                                           void *stream) {
   return batch_impl(n_layers, n_tokens, layers, new_k, new_v, ctrs, budgets,
-                    pyramid_policy(n_sink, rope_base), evicted, stream);
+                    pyramid_policy(n_sink, rope_base), evicted, kve::MovePool{}, stream);
 }
 
-KVE_EXPORT int kve_step(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
-                        const void *const *new_k, const void *const *new_v, kve_counters *ctrs,
-                        const int32_t *budgets, const kve_policy *policy,
-                        int32_t *const *evicted, void *stream) {
-  if (!policy || !layers || !new_k || !new_v || !ctrs || !budgets) return KVE_EINVAL;
+namespace {
+
+// The general entry points' policy, checked field by field.
+int policy_from(const kve_policy *policy, Policy &p) {
+  if (!policy) return KVE_EINVAL;
   if (policy->score != KVE_SCORE_CUMULATIVE && policy->score != KVE_SCORE_CURRENT)
     return KVE_EINVAL;
   if (policy->gumbel != 0 && policy->gumbel != 1) return KVE_EINVAL;
-  Policy p;
+  p = Policy{};
   p.n_sink = policy->n_sink;
   p.recent = policy->recent;
   p.current = policy->score == KVE_SCORE_CURRENT;
@@ -518,10 +402,55 @@ KVE_EXPORT int kve_step(int32_t n_layers, int32_t n_tokens, const kve_layer *lay
   p.anneal_steps = p.gumbel ? policy->anneal_steps : 0;
   p.rope_base = policy->rope_base;
   p.seed = p.gumbel ? policy->seed : 0;
+  return KVE_OK;
+}
+
+int general_step(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
+                 const void *const *new_k, const void *const *new_v, kve_counters *ctrs,
+                 const int32_t *budgets, const kve_policy *policy, int32_t *const *evicted,
+                 const kve::MovePool &pool, void *stream) {
+  if (!layers || !new_k || !new_v || !ctrs || !budgets) return KVE_EINVAL;
+  Policy p;
+  if (policy_from(policy, p) != KVE_OK) return KVE_EINVAL;
   if (n_layers == 1 && n_tokens == 1)        // the per-layer kernel
     return step_impl(&layers[0], new_k[0], new_v[0], &ctrs[0], budgets[0], p,
-                     evicted ? evicted[0] : nullptr, stream);
-  return batch_impl(n_layers, n_tokens, layers, new_k, new_v, ctrs, budgets, p, evicted, stream);
+                     evicted ? evicted[0] : nullptr, pool, stream);
+  return batch_impl(n_layers, n_tokens, layers, new_k, new_v, ctrs, budgets, p, evicted, pool,
+                    stream);
+}
+
+}  // namespace
+
+KVE_EXPORT int kve_step(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
+                        const void *const *new_k, const void *const *new_v, kve_counters *ctrs,
+                        const int32_t *budgets, const kve_policy *policy,
+                        int32_t *const *evicted, void *stream) {
+  return general_step(n_layers, n_tokens, layers, new_k, new_v, ctrs, budgets, policy, evicted,
+                      kve::MovePool{}, stream);
+}
+
+KVE_EXPORT int kve_step_ws(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
+                           const void *const *new_k, const void *const *new_v,
+                           kve_counters *ctrs, const int32_t *budgets, const kve_policy *policy,
+                           int32_t *const *evicted, void *workspace, int64_t workspace_bytes,
+                           void *stream) {
+  if (!layers || n_layers < 1) return KVE_EINVAL;
+  kve::MovePool pool;
+  if (make_pool(workspace, workspace_bytes, layers[0].d, pool) != KVE_OK) return KVE_EINVAL;
+  return general_step(n_layers, n_tokens, layers, new_k, new_v, ctrs, budgets, policy, evicted,
+                      pool, stream);
+}
+
+// The workspace that lets every move of a single-token launch over `caches`
+// caches at budgets up to max_budget be handed over: one item and one parked
+// row per chunk of the longest move of each cache.
+KVE_EXPORT int64_t kve_workspace_size(int64_t caches, int32_t max_budget, int32_t d) {
+  if (caches < 1 || caches > INT32_MAX || max_budget < 1 || max_budget > kMaxBudget ||
+      (d != 64 && d != 128))
+    return -1;
+  const int64_t items = caches * (int64_t)kve::max_move_chunks(max_budget);
+  if (items > INT32_MAX / 2) return -1;
+  return kve::pool_bytes(items, d);
 }
 
 // "The budget schedule": linear taper, mean avg_budget, floor n_sink + 1.

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kve_move_plan.h"
+
 namespace kve {
 
 constexpr int kMaxHalfD = 64;        // d <= 128
@@ -19,14 +21,6 @@ struct RopeTable {
   float s[kMaxHalfD];
 };
 
-// Rows per chunk of a deferred compaction (one workgroup of the move kernel
-// each), and the longest move a step still does itself.
-// (Tuning builds may override the second with -D.)
-constexpr int kMoveChunk = 64;
-#ifndef KVE_DEFER_ROWS
-#define KVE_DEFER_ROWS (2 * kMoveChunk)
-#endif
-constexpr int kDeferRows = KVE_DEFER_ROWS;
 // Workgroups of the move kernel that share a queue longer than its grid.
 #ifndef KVE_MOVE_STREAMS
 #define KVE_MOVE_STREAMS 256
@@ -35,30 +29,47 @@ constexpr int kMoveStreams = KVE_MOVE_STREAMS;
 
 // One chunk of a compaction handed from a step to the move kernel that
 // follows it: of the cache whose rows e+1 .. n-1 move down one slot, chunk j
-// (destination rows e + j*kMoveChunk .. up to n-2).
+// (destination rows e + j*kMoveChunk .. up to n-2).  k == nullptr marks an
+// item reserved by a step that then found the pool full (skipped).
 struct MoveItem {
   void *k;                 // the cache's row 0 (keys)
   void *v;                 // the cache's row 0 (values)
   int32_t e;               // evicted row
   int32_t n;               // rows stored before the step
-  int32_t b;               // workgroup of the step (its scratch rows)
+  int32_t base;            // the cache's first item: its parked rows are base .. base+chunks-1
   int32_t j;               // chunk
 };
 
-// Deferred compactions of one launch: per workgroup `slots` rows of key +
-// value (2d fp16 each) -- slot 0 the incoming row (its key already rotated to
-// its final position), slot j >= 1 row e + j*kMoveChunk as it was before the
-// move (the first destination of move chunk j, read by chunk j-1) -- and the
-// queue of chunks, appended at count[parity].  The move kernel works through
-// them and zeroes count[1 - parity], which the launch before it used, so the
-// next launch (the other parity) starts from zero.
-struct DeferArgs {
-  MoveItem *items;         // [workgroups * slots]; null: every step compacts its own cache
-  void *rows;              // fp16 [workgroups][slots][2][d]
-  int32_t *count;          // [2]: items queued, by parity
-  int32_t slots;           // >= the chunks of the longest possible move
-  int32_t parity;          // 0 or 1, alternating between launches
+// The caller-owned workspace of a single-token launch that hands its long
+// compactions to the move kernel.  A step that moves more than kDeferRows
+// rows reserves one item per chunk with a vector atomic on count[0]: item
+// base + j holds chunk j, and parked row base + j holds what the move would
+// otherwise race on -- row 0 the incoming row (its key already rotated to
+// its final slot), row j >= 1 row e + j*kMoveChunk as it was before the move
+// (the first destination of chunk j, read by chunk j-1).  A reservation that
+// does not fit in `cap` items compacts in place instead.  The move kernel
+// works through the items and its last workgroup zeroes both counters, so
+// the workspace is back to zero when the call's work is done: no state is
+// kept between calls, on the host or the device.
+struct MovePool {
+  int32_t *count;          // [2]: items reserved; move-kernel workgroups finished
+  MoveItem *items;         // [cap]; null pointer: every step compacts its own cache
+  void *rows;              // fp16 [cap][2][d]: parked key then value of each item
+  int32_t cap;             // items (and parked rows) the workspace holds
 };
+
+// Workspace layout for `cap` items of head dimension d: counters, items,
+// parked rows, each part 256-byte aligned.
+constexpr int64_t kPoolHeaderBytes = 256;
+inline int64_t pool_items_bytes(int64_t cap) { return (cap * (int64_t)sizeof(MoveItem) + 255) & ~(int64_t)255; }
+inline int64_t pool_bytes(int64_t cap, int d) { return kPoolHeaderBytes + pool_items_bytes(cap) + cap * 4 * (int64_t)d; }
+// The largest item count a workspace of `bytes` bytes holds (0 if none).
+inline int64_t pool_capacity(int64_t bytes, int d) {
+  if (bytes < kPoolHeaderBytes) return 0;
+  int64_t cap = (bytes - kPoolHeaderBytes) / ((int64_t)sizeof(MoveItem) + 4 * (int64_t)d);
+  while (cap > 0 && pool_bytes(cap, d) > bytes) --cap;
+  return cap;
+}
 
 // One layer of a step: its B*H caches and where the incoming rows are.
 struct LayerArgs {
@@ -87,7 +98,7 @@ struct SharedArgs {
   int32_t current;         // 1: score = this step's weight (TOVA), 0: += (H2O / Keyformer)
   int32_t anneal_steps;
   int32_t early;           // 1: load the old scores before the key pass (set per launch)
-  DeferArgs defer;         // long compactions handed to the move kernel (single tokens)
+  MovePool pool;           // long compactions handed to the move kernel (single tokens)
   double tau_init;
   double tau_end;
   uint64_t seed;
@@ -121,9 +132,8 @@ hipError_t launch_step_layers(const LayerPack &layers, int n_layers, int total_b
 bool reuse_keys(int total_blocks, int max_n_prev, int n_tokens, int d);
 
 // The move kernel: finishes the compactions that a single-token launch with
-// sa.defer.items set handed over (`blocks` = that launch's workgroups).  Must
-// run after it on the same stream.
-hipError_t launch_moves(const DeferArgs &defer, int blocks, const RopeTable &back1, int d,
-                        hipStream_t stream);
+// sa.pool.items set handed over, and zeroes the pool's counters.  Must run
+// after it on the same stream.
+hipError_t launch_moves(const MovePool &pool, const RopeTable &back1, int d, hipStream_t stream);
 
 }  // namespace kve

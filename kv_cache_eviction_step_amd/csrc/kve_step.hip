@@ -121,6 +121,16 @@ __device__ __forceinline__ void rotate_pair(float x1, float x2, float c, float s
   y2 = e + f;
 }
 
+// A row's new score: its normalised weight w * (1/Z), rounded to fp32 on its
+// own, added to the old score (TOVA-adapted: the weight alone).  No fused
+// multiply-add: the increment is one rounded value, as the method's
+// definition of the accumulated mass reads.
+__device__ __forceinline__ float score_update(bool current, float old, float w, float rz) {
+#pragma clang fp contract(off)
+  const float p = w * rz;
+  return current ? p : old + p;
+}
+
 __device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 __device__ __forceinline__ uint32_t as_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
 
@@ -565,8 +575,7 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   for (int k = 0; k < R; ++k) {
     const int i = tid + k * NT;
     if (i < n) {
-      const float pi = (WREG ? wreg[k] : lds_x[i]) * rz;
-      const float s = current ? pi : sreg[k] + pi;
+      const float s = score_update(current, sreg[k], WREG ? wreg[k] : lds_x[i], rz);
       sreg[k] = s;
       if (over && i >= n_sink && i <= last) {
         const float key = GUMBEL ? fmaf(tau, greg[k], s) : s;
@@ -623,35 +632,55 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   const int rm = tid / LPM;
 
   // A single-token launch followed by the move kernel hands it every move
-  // longer than kDeferRows: the step parks the rows that move chunks would
-  // otherwise race on (each chunk's first destination) and the incoming row
-  // in the launch's scratch, queues the chunks, and the move kernel shifts
-  // them in parallel over the GPU instead of one compute unit doing them in
-  // turn.
-  const bool defer = !PRE && sa.defer.items != nullptr && e >= 0 && e < n - 1 &&
-                     n - 1 - e > kDeferRows;
-  gptr<u32x4> slot = nullptr;                   // this workgroup's scratch rows
+  // longer than kDeferRows (the move plan): the step reserves one pool item
+  // per chunk, parks the rows that chunks would otherwise race on (each
+  // chunk's first destination) and the incoming row, queues the chunks, and
+  // the move kernel shifts them in parallel over the GPU instead of one
+  // compute unit doing them in turn.  A reservation that does not fit in the
+  // pool marks its items empty and compacts in place.
+  bool defer = !PRE && sa.pool.items != nullptr && move_handed_over(e, n);
+  gptr<u32x4> slot = nullptr;                   // this move's parked rows
   if (defer) {
     __shared__ int item_base;
-    slot = global(reinterpret_cast<u32x4 *>(sa.defer.rows)) +
-           (size_t)blockIdx.x * sa.defer.slots * (2 * V16);
-    const int chunks = (n - 1 - e + kMoveChunk - 1) / kMoveChunk;
-    if (tid == 0) item_base = atomicAdd(sa.defer.count + sa.defer.parity, chunks);
-    for (int i = tid; i < (chunks - 1) * 2 * V16; i += NT) {
+    constexpr int PIECES_EARLY = 2;             // parked 16-byte pieces loaded per thread
+    const int chunks = move_chunks(e, n);       //   while the reservation is in flight
+    const int pieces = (chunks - 1) * 2 * V16;
+    u32x4 pk[PIECES_EARLY];
+    auto parked_piece = [&](int i) {            // piece i of parked rows 1 .. chunks-1
       const int j = 1 + i / (2 * V16), w = i % (2 * V16);
-      const size_t row = (size_t)(e + j * kMoveChunk) * V16;
-      slot[(size_t)j * 2 * V16 + w] = w < V16 ? Kw[row + w] : Vw[row + w - V16];
-    }
+      const size_t row = (size_t)parked_row(e, j) * V16;
+      return w < V16 ? Kw[row + w] : Vw[row + w - V16];
+    };
+#pragma unroll
+    for (int u = 0; u < PIECES_EARLY; ++u)
+      if (tid + u * NT < pieces) pk[u] = parked_piece(tid + u * NT);
+    if (tid == 0) item_base = atomicAdd(sa.pool.count, chunks);
     __syncthreads();                            // item_base
-    if (tid < chunks) {
-      MoveItem it;
-      it.k = static_cast<char *>(la.k) + row0 * (size_t)(2 * D);
-      it.v = static_cast<char *>(la.v) + row0 * (size_t)(2 * D);
-      it.e = e;
-      it.n = n;
-      it.b = (int32_t)blockIdx.x;
-      it.j = tid;
-      sa.defer.items[item_base + tid] = it;
+    const int base = __builtin_amdgcn_readfirstlane(item_base);
+    MoveItem *const items = sa.pool.items;
+    if (!reservation_fits(base, chunks, sa.pool.cap)) {
+      for (int i = tid; i < chunks; i += NT) {  // the part of the reservation inside the pool
+        const int64_t it = (int64_t)base + i;
+        if (it >= 0 && it < sa.pool.cap) items[it].k = nullptr;
+      }
+      defer = false;
+    } else {
+      slot = global(reinterpret_cast<u32x4 *>(sa.pool.rows)) + (size_t)base * (2 * V16);
+      // slot row 0 is the incoming row, rows 1 .. chunks-1 the parked ones
+#pragma unroll
+      for (int u = 0; u < PIECES_EARLY; ++u)
+        if (tid + u * NT < pieces) slot[2 * V16 + tid + u * NT] = pk[u];
+      for (int i = tid + PIECES_EARLY * NT; i < pieces; i += NT) slot[2 * V16 + i] = parked_piece(i);
+      if (tid < chunks) {
+        MoveItem it;
+        it.k = static_cast<char *>(la.k) + row0 * (size_t)(2 * D);
+        it.v = static_cast<char *>(la.v) + row0 * (size_t)(2 * D);
+        it.e = e;
+        it.n = n;
+        it.base = base;
+        it.j = tid;
+        items[base + tid] = it;
+      }
     }
   }
 
@@ -901,26 +930,25 @@ __global__ __launch_bounds__(NT) void step_layers_kernel(LayerPack pack, int n_l
 }
 
 // Finishes the compactions a single-token launch handed over, one queued
-// chunk at a time.  Chunk j of a cache fills destination rows e + j*C ..
-// e + (j+1)*C - 1 (C = kMoveChunk, the last chunk ending at row n-2) from the
-// rows one below, keys rotated by -1 position.  A chunk reads
-// from the cache only rows inside its own destination range, plus row n-1
-// for the last chunk; the one row it needs beyond that, the next chunk's
-// first destination, comes from the scratch slot the step filled before
-// anything moved.  So no two chunks touch the same row, and each chunk reads
-// everything before it writes.  The last chunk then writes the incoming row
-// at n-1.  The grid strides over the queued items; workgroup 0 first zeroes
-// the other parity's counter (its launch has finished).
+// chunk at a time, following the move plan (kve_move_plan.h): chunk j fills
+// its destination rows from the rows one below, keys rotated by -1 position,
+// reading every source from the cache except its next chunk's first
+// destination, which comes from the parked copy.  So no two chunks touch the
+// same row, and each chunk reads everything before it writes.  The last
+// chunk then writes the incoming row at n-1.  The grid strides over the
+// queued items; when every workgroup has passed its last item the last one
+// to finish zeroes the pool's two counters, so the next launch finds them at
+// zero without any clearing on the host.
 template <int D>
-__global__ __launch_bounds__(256) void move_kernel(DeferArgs defer, RopeTable back1) {
+__global__ __launch_bounds__(256) void move_kernel(MovePool pool, RopeTable back1) {
   constexpr int NT = 256;
   constexpr int V16 = D / 8;
   constexpr int LPM = D / 16;                   // lanes per row: chunks lm and lm + LPM
   constexpr int RPM = NT / LPM;                 // rows per sweep
   constexpr int SW = kMoveChunk / RPM;          // sweeps per chunk
   static_assert(SW * RPM == kMoveChunk, "move chunk");
-  if (blockIdx.x == 0 && threadIdx.x == 0) defer.count[1 - defer.parity] = 0;
-  const int queued = defer.count[defer.parity];
+  const int reserved = __hip_atomic_load(pool.count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int queued = items_queued(reserved, pool.cap);
   const int tid = threadIdx.x, lm = tid % LPM, rm = tid / LPM;
   float cs[8], sn[8];
 #pragma unroll
@@ -934,24 +962,25 @@ __global__ __launch_bounds__(256) void move_kernel(DeferArgs defer, RopeTable ba
   // move more bytes per second.
   const int active = queued > (int)gridDim.x ? min((int)gridDim.x, kMoveStreams)
                                              : (int)gridDim.x;
-  if ((int)blockIdx.x >= active) return;
-  for (int item = blockIdx.x; item < queued; item += active) {
-    const MoveItem md = defer.items[item];
-    const int b = md.b, j = md.j, e = md.e, n = md.n, last = n - 2;
-    const int chunks = (n - 1 - e + kMoveChunk - 1) / kMoveChunk;
-    const int d0 = e + j * kMoveChunk;
+  const int first = (int)blockIdx.x < active ? (int)blockIdx.x : queued;
+  for (int item = first; item < queued; item += active) {
+    const MoveItem md = pool.items[item];
+    if (md.k == nullptr) continue;              // reserved by a step that found no room
+    const int j = md.j, e = md.e, n = md.n, last = move_last_dst(n);
+    const int chunks = move_chunks(e, n);
+    const int d0 = chunk_first_dst(e, j);
     const gptr<u32x4> K = global(reinterpret_cast<u32x4 *>(md.k));
     const gptr<u32x4> V = global(reinterpret_cast<u32x4 *>(md.v));
-    const gptr<const u32x4> S = global(reinterpret_cast<const u32x4 *>(defer.rows)) +
-                                (size_t)b * defer.slots * (2 * V16);
+    const gptr<const u32x4> P = global(reinterpret_cast<const u32x4 *>(pool.rows)) +
+                                (size_t)md.base * (2 * V16);     // the cache's parked rows
     u32x4 k1[SW], k2[SW], v1[SW], v2[SW];
 #pragma unroll
     for (int w = 0; w < SW; ++w) {
       const int dst = d0 + rm + w * RPM;
       if (dst <= last) {
-        const int src = dst + 1;
-        if (j + 1 < chunks && src == d0 + kMoveChunk) {    // next chunk's first row
-          const gptr<const u32x4> r = S + (size_t)(j + 1) * 2 * V16;
+        const int src = chunk_source_row(e, j, chunks, dst);
+        if (src < 0) {                          // the next chunk's first row: parked
+          const gptr<const u32x4> r = P + (size_t)(j + 1) * 2 * V16;
           k1[w] = r[lm];
           k2[w] = r[lm + LPM];
           v1[w] = r[V16 + lm];
@@ -979,13 +1008,23 @@ __global__ __launch_bounds__(256) void move_kernel(DeferArgs defer, RopeTable ba
         __builtin_nontemporal_store(v2[w], V + o + lm + LPM);
       }
     }
-    if (j == chunks - 1 && tid < 2 * V16) {     // the incoming row (slot 0) at n-1
-      const u32x4 x = S[tid];
+    if (j == chunks - 1 && tid < 2 * V16) {     // the incoming row (parked row 0) at n-1
+      const u32x4 x = P[tid];
       const size_t o = (size_t)(n - 1) * V16;
       if (tid < V16)
         K[o + tid] = x;
       else
         V[o + tid - V16] = x;
+    }
+  }
+  // Every thread of this workgroup has read the count (it bounds the loop
+  // above); the workgroup that finishes last knows that every other one has.
+  __syncthreads();
+  if (tid == 0) {
+    const int done = atomicAdd(pool.count + 1, 1);
+    if (done == (int)gridDim.x - 1) {
+      atomicExch(pool.count, 0);
+      atomicExch(pool.count + 1, 0);
     }
   }
 }
@@ -1147,16 +1186,15 @@ hipError_t launch_step_layers(const LayerPack &layers, int n_layers, int total_b
                                                    d, gumbel, stream);
 }
 
-hipError_t launch_moves(const DeferArgs &defer, int blocks, const RopeTable &back1, int d,
+hipError_t launch_moves(const MovePool &pool, const RopeTable &back1, int d,
                         hipStream_t stream) {
   // enough workgroups to spread the longest moves of a launch over the GPU;
   // each strides over the queued chunks
-  const int64_t most = (int64_t)blocks * defer.slots;
-  const dim3 grid((unsigned)std::min<int64_t>(most, KVE_MOVE_WGS));
+  const dim3 grid((unsigned)std::min<int64_t>(pool.cap, KVE_MOVE_WGS));
   if (d == 128)
-    hipLaunchKernelGGL(move_kernel<128>, grid, dim3(256), 0, stream, defer, back1);
+    hipLaunchKernelGGL(move_kernel<128>, grid, dim3(256), 0, stream, pool, back1);
   else
-    hipLaunchKernelGGL(move_kernel<64>, grid, dim3(256), 0, stream, defer, back1);
+    hipLaunchKernelGGL(move_kernel<64>, grid, dim3(256), 0, stream, pool, back1);
   return hipGetLastError();
 }
 

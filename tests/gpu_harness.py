@@ -19,6 +19,7 @@ import oracle
 import synth
 from oracle import OracleCache
 from oracle.guard import guarded_trajectory, params_for
+from oracle.states import random_state  # noqa: F401  (re-exported for the tests)
 
 # acceptance (per cache): kept rows and evicted indices bit-exact, values
 # bit-exact, keys within 1 fp16 ULP, scores within 1e-5 relative, Gumbel
@@ -38,24 +39,6 @@ class Sample:
     evicted: np.ndarray          # [T] oracle eviction log
     final: dict                  # oracle snapshot after T tokens
     attempts: int
-
-
-def random_state(w: synth.Workload, layer: int, hh: int, n: int, cap: int, next_pos: int,
-                 seed: int = 1) -> OracleCache:
-    """A plausible mid-run cache: n rows with keys at positions 0..n-1, positive
-    scores, frozen Gumbel values, positions == index."""
-    c = OracleCache(w.d, cap)
-    if n > 0:
-        ks, vs = synth.token_kv(w, layer, hh, np.arange(n), attempt=10_000 + seed)
-        rng = np.random.default_rng([seed, layer, hh])
-        c.k[:n], c.v[:n] = ks, vs
-        c.s[:n] = rng.gamma(0.7, 1.5, n).astype(np.float32)
-        c.g[:n] = np.array([oracle.gumbel(w.gumbel_seed, hh, 7_000_000 + i) for i in range(n)],
-                           dtype=np.float32) if w.kind == "keyformer" else 0.0
-        c.p[:n] = np.arange(n)
-        c.tid[:n] = np.arange(n)
-    c.set_counters(n, next_pos, next_pos)
-    return c
 
 
 def _sample_job(args) -> Sample:
@@ -214,9 +197,12 @@ def policy_for(w: synth.Workload):
 
 def run_layer(w: synth.Workload, layer_idx: int, budget: int, T: int, samples: list[Sample],
               init_n: int | None, next_pos: int, device, cap: int | None = None,
-              bh: int | None = None, gen_seed: int = 1234, hh_base: int = 0):
+              bh: int | None = None, gen_seed: int = 1234, hh_base: int = 0,
+              workspace: bool = False):
     """Step one layer launch T tokens on the GPU; sampled caches get the oracle's
-    inputs and initial states.  Returns (layer, evicted log [T, bh] numpy, counters)."""
+    inputs and initial states.  workspace: one token per kve_step_ws call with
+    a workspace sized for every move (long moves handed to the move kernel).
+    Returns (layer, evicted log [T, bh] numpy, counters)."""
     import kv_cache_eviction_step_amd as kve
     bh = bh or w.bh
     cap = cap or budget + 1
@@ -236,13 +222,17 @@ def run_layer(w: synth.Workload, layer_idx: int, budget: int, T: int, samples: l
     ev = torch.full((T, bh), -7, dtype=torch.int32, device=device)
     ctr = kve.Counters(n0, next_pos, next_pos)
     prm = params_for(w, budget, 0)
-    if w.kind == "tova" or w.recent > 0:
-        # the extensions go through the general entry point, one token per call
+    if w.kind == "tova" or w.recent > 0 or workspace:
+        # the extensions and the workspace form go through the general entry
+        # points, one token per call
         batch = kve.LayerBatch([L], [budget], [ctr])
         pol = policy_for(w)
+        ws = kve.workspace(bh, budget, w.d, device) if workspace else None
         for t in range(T):
-            kve.step(batch, [nk[t]], [nv[t]], pol, [ev[t]])
+            kve.step(batch, [nk[t]], [nv[t]], pol, [ev[t]], workspace=ws)
         torch.cuda.synchronize(device)
+        if ws is not None:
+            assert not bool(ws[:8].any()), "workspace counters not back to zero"
         return L, ev.cpu().numpy(), batch.ctrs[0]
     cl = L.c_struct()
     for t in range(T):
@@ -257,11 +247,15 @@ def run_layer(w: synth.Workload, layer_idx: int, budget: int, T: int, samples: l
 
 
 def run_batched(w: synth.Workload, layer_ids, budgets, T: int, samples: dict, init_n, next_pos,
-                device, gen_seed: int = 99, tokens_per_call: int = 1):
+                device, gen_seed: int = 99, tokens_per_call: int = 1, workspace: bool = False,
+                decode_from: int | None = None):
     """Step several layers together on the GPU: one batched launch per token,
     or per `tokens_per_call` tokens (*_step_layers_tokens).  samples[l] lists
-    the oracle samples of layer position l.  Returns (layers, evicted log
-    [T, L, bh] numpy, batch)."""
+    the oracle samples of layer position l.  workspace: single-token launches
+    go through kve_step_ws with a workspace sized for every move.
+    decode_from: tokens from this one on go one per launch (the decode form
+    after a prompt ingested `tokens_per_call` at a time).  Returns (layers,
+    evicted log [T, L, bh] numpy, batch)."""
     import kv_cache_eviction_step_amd as kve
     kf = w.kind == "keyformer"
     gen = torch.Generator(device=device)
@@ -288,12 +282,15 @@ def run_batched(w: synth.Workload, layer_ids, budgets, T: int, samples: dict, in
     ev = torch.full((T, len(budgets), w.bh), -7, dtype=torch.int32, device=device)
     prm = params_for(w, budgets[0], 0)
     S = tokens_per_call
+    ws = kve.workspace(w.bh * len(budgets), max(budgets), w.d, device) if workspace else None
+    pol = policy_for(w) if workspace else None
+    T_multi = T if decode_from is None else decode_from
     if S > 1:
         # [L, T, bh, d]: each layer's run of tokens is one contiguous block
         nkl, nvl = nk.transpose(0, 1).contiguous(), nv.transpose(0, 1).contiguous()
         evl = torch.full((len(budgets), T, w.bh), -7, dtype=torch.int32, device=device)
-        for t0 in range(0, T, S):
-            n = min(S, T - t0)
+        for t0 in range(0, T_multi, S):
+            n = min(S, T_multi - t0)
             ks, vs, es = nkl[:, t0:t0 + n], nvl[:, t0:t0 + n], evl[:, t0:t0 + n]
             if kf:
                 kve.keyformer_step_layers_tokens(batch, ks, vs, w.n_sink, prm.tau_init,
@@ -302,15 +299,22 @@ def run_batched(w: synth.Workload, layer_ids, budgets, T: int, samples: dict, in
             else:
                 kve.pyramid_step_layers_tokens(batch, ks, vs, w.n_sink, w.rope_base, es,
                                                n_tokens=n)
+        for t in range(T_multi, T):                 # the decode tokens, one per launch
+            kve.step(batch, nkl[:, t], nvl[:, t], pol or policy_for(w), evl[:, t],
+                     workspace=ws)
         ev = evl.transpose(0, 1)
     else:
         for t in range(T):
-            if kf:
+            if ws is not None:
+                kve.step(batch, nk[t], nv[t], pol, ev[t], workspace=ws)
+            elif kf:
                 kve.keyformer_step_layers(batch, nk[t], nv[t], w.n_sink, prm.tau_init,
                                           prm.tau_end, prm.anneal_steps, w.rope_base,
                                           w.gumbel_seed, ev[t])
             else:
                 kve.pyramid_step_layers(batch, nk[t], nv[t], w.n_sink, w.rope_base, ev[t])
     torch.cuda.synchronize(device)
+    if ws is not None:
+        assert not bool(ws[:8].any()), "workspace counters not back to zero"
     _ = layer_ids
     return layers, ev.cpu().numpy(), batch

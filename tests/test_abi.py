@@ -31,9 +31,33 @@ def test_header_declares_the_abi():
     assert set(_declared()) == {"keyformer_step", "pyramid_step", "keyformer_step_layers",
                                 "pyramid_step_layers", "keyformer_step_tokens",
                                 "pyramid_step_tokens", "keyformer_step_layers_tokens",
-                                "pyramid_step_layers_tokens", "kve_step", "pyramid_budgets",
+                                "pyramid_step_layers_tokens", "kve_step", "kve_step_ws",
+                                "kve_workspace_size", "pyramid_budgets",
                                 "kve_kept_indices", "kve_fp16_bytes", "kve_full_fp16_bytes",
                                 "kve_strerror"}
+
+
+# HIP runtime calls the library may import: kernel registration and launch,
+# the LDS-size attribute of a launch, and the launch-error query.  No
+# allocation (hipMalloc, hipHostMalloc, hipMallocAsync, ...), free, memset,
+# copy, event or synchronisation call is imported, so no path of any entry
+# point can allocate device memory or stall the caller's streams.
+ALLOWED_HIP_IMPORTS = {"__hipPopCallConfiguration", "__hipPushCallConfiguration",
+                       "__hipRegisterFatBinary", "__hipRegisterFunction",
+                       "__hipUnregisterFatBinary", "hipFuncSetAttribute", "hipGetLastError",
+                       "hipLaunchKernel"}
+
+
+def test_library_imports_no_allocation_or_synchronisation():
+    out = subprocess.run(["nm", "-D", "--undefined-only", kve.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    hip = {line.split()[-1].split("@")[0] for line in out.splitlines()
+           if "hip" in line.lower()}
+    assert hip, "no HIP import found: the check would prove nothing"
+    assert hip <= ALLOWED_HIP_IMPORTS, sorted(hip - ALLOWED_HIP_IMPORTS)
+    for banned in ("hipMalloc", "hipFree", "hipDeviceSynchronize", "hipStreamSynchronize",
+                   "hipMemset", "hipEventCreate", "hipHostMalloc", "hipMallocAsync"):
+        assert not any(h.startswith(banned) for h in hip), banned
 
 
 def test_library_exports_every_declared_symbol():
@@ -407,3 +431,90 @@ def test_layer_batch_pointer_arrays():
         batch._layer_offsets(128 * (s + 1))
     assert len(batch._offsets) <= 16
     assert (batch._layer_offsets(256) == np.arange(3, dtype=np.uint64) * np.uint64(256)).all()
+
+
+# ---------------------------------------------------------------------------
+# the workspace form (kve_step_ws, kve_workspace_size)
+# ---------------------------------------------------------------------------
+
+def _ws_bytes(caches, budget, d):
+    """The layout kve_workspace_size documents: 256 bytes of counters, one
+    32-byte item per 64-row chunk of each cache's longest move (budget - 1
+    rows, at least one chunk), rounded up to 256 bytes, and one parked row of
+    4*d bytes per item."""
+    items = caches * max(1, -(-(budget - 1) // 64))
+    return 256 + -(-items * 32 // 256) * 256 + items * 4 * d
+
+
+@pytest.mark.parametrize("args", [(256, 1024, 128), (8192, 1024, 128), (512, 6144, 128),
+                                  (1, 1, 64), (1, 2, 64), (3, 65, 64), (3, 66, 64),
+                                  (300, 12288, 128), (7, 129, 64)])
+def test_workspace_size(args):
+    assert kve.workspace_size(*args) == _ws_bytes(*args)
+
+
+@pytest.mark.parametrize("args", [(0, 1024, 128), (256, 0, 128), (256, 12289, 128),
+                                  (256, 1024, 96), (2**31, 1024, 128), (2**24, 12288, 128)])
+def test_workspace_size_rejects(args):
+    assert kve.lib().kve_workspace_size(*args) == -1
+
+
+def _ws_call(ws, nbytes, layers=None, ctrs=None, budgets=(32,)):
+    layers = layers or [_layer()]
+    n = len(layers)
+    arr = (KveLayer * n)(*layers)
+    cs = (Counters * n)(*(ctrs or [Counters(32, 100, 100)] * n))
+    bs = (ctypes.c_int32 * n)(*budgets)
+    ptrs = (ctypes.c_void_p * n)(*([FAKE] * n))
+    pol = kve.policy("keyformer", 4, tau_init=1.0, tau_end=2.0, anneal_steps=64)
+    rc = kve.lib().kve_step_ws(n, 1, arr, ptrs, ptrs, cs, bs, ctypes.byref(pol), None, ws,
+                               nbytes, None)
+    return rc, [(c.n_kept, c.next_pos, c.pos) for c in cs]
+
+
+@pytest.mark.parametrize("case", ["misaligned", "one_byte_short", "header_only", "null_with_size",
+                                  "negative", "null_layers"])
+def test_kve_step_ws_rejects_bad_workspace(case):
+    """A workspace must be 256-byte aligned and hold at least one item (one
+    32-byte item and one parked 4*d-byte row, after 256 bytes of counters);
+    NULL means none and then its size must be 0."""
+    one_item = _ws_bytes(1, 2, 64)                  # 256 + 256 + 256 at d = 64
+    ws, nbytes = {"misaligned": (FAKE + 16, 1 << 20), "one_byte_short": (FAKE, one_item - 1),
+                  "header_only": (FAKE, 256), "null_with_size": (None, 4096),
+                  "negative": (FAKE, -1), "null_layers": (FAKE, 1 << 20)}[case]
+    if case == "null_layers":
+        pol = kve.policy("keyformer", 4)
+        assert kve.lib().kve_step_ws(1, 1, None, None, None, None, None, ctypes.byref(pol), None,
+                                     ws, nbytes, None) == kve.KVE_EINVAL
+        return
+    rc, after = _ws_call(ws, nbytes)
+    assert rc == kve.KVE_EINVAL
+    assert after == [(32, 100, 100)]
+
+
+@pytest.mark.parametrize("ws,nbytes", [(None, 0), (FAKE, _ws_bytes(1, 2, 64)),
+                                       (FAKE, 1 << 20)])
+def test_kve_step_ws_passes_host_checks(ws, nbytes):
+    """No workspace, the smallest one, and a large one all pass the host checks
+    and reach the launch (no device here)."""
+    rc, after = _ws_call(ws, nbytes)
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; the no-device path is not reachable")
+    assert rc == kve.KVE_ENODEV
+    assert after == [(32, 100, 100)]
+
+
+def test_kve_step_ws_checks_layers_like_kve_step():
+    layers = [_layer(), _layer(k=FAKE + (1 << 20))]
+    rc, after = _ws_call(FAKE, 1 << 20, layers, [Counters(32, 100, 100), Counters(10, 50, 50)],
+                         budgets=(32, 32))
+    assert rc == kve.KVE_EINVAL
+    assert after == [(32, 100, 100), (10, 50, 50)]
+
+
+def test_binding_workspace_is_aligned_zeroed_and_sized():
+    ws = kve.workspace(300, 1000, 128, "cpu")
+    assert ws.dtype == torch.uint8 and ws.numel() == kve.workspace_size(300, 1000, 128)
+    assert ws.data_ptr() % 256 == 0 and not bool(ws.any())
+    with pytest.raises(ValueError):
+        kve.workspace_size(0, 1000, 128)

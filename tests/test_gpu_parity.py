@@ -218,14 +218,18 @@ def test_beta_one_pyramid_is_h2o_bit_for_bit(dev):
 # full launch sizes: every cache of the layer stepped, sampled caches checked
 # ---------------------------------------------------------------------------
 
-def test_full_size_batched_late_riser(dev):
+@pytest.mark.parametrize("ws", [False, True], ids=["in-place", "workspace"])
+def test_full_size_batched_late_riser(dev, ws):
+    """The 8B-shaped workload, one layer launch of 256 caches per token:
+    keyformer_step (every cache compacts in place) and kve_step_ws (moves of
+    more than 128 rows handed to the move kernel)."""
     w = synth.WORKLOADS[3]                             # B*H = 256, budget 1024, D = 128
     T, next_pos = 40, w.prompt
     hhs = [0, 37, 128, 255]
-    _say(f"[full] {w.name} bh={w.bh} cap={w.budget + 1} sampled={hhs} T={T}")
+    _say(f"[full] {w.name} bh={w.bh} cap={w.budget + 1} sampled={hhs} T={T} ws={ws}")
     samples = oracle_samples(w, 9, hhs, w.budget, T, w.budget + 1, init_n=w.budget,
                              next_pos=next_pos)
-    L, ev, _ = run_layer(w, 9, w.budget, T, samples, w.budget, next_pos, dev)
+    L, ev, _ = run_layer(w, 9, w.budget, T, samples, w.budget, next_pos, dev, workspace=ws)
     _assert_parity(L, ev, samples, next_pos)
     assert ((ev >= 0) & (ev < w.budget)).any()
 
@@ -334,16 +338,19 @@ def test_batched_equals_per_layer_calls(dev, kind):
         assert any(bool(((e >= 0) & (e < b)).any()) for e, (_, b, _) in zip(eva, shapes))
 
 
-def test_full_size_batched_all_layers_late_riser(dev):
-    """The 8B-shaped workload with all 32 layers in one launch per token."""
+@pytest.mark.parametrize("ws", [False, True], ids=["in-place", "workspace"])
+def test_full_size_batched_all_layers_late_riser(dev, ws):
+    """The 8B-shaped workload with all 32 layers in one launch per token:
+    keyformer_step_layers (in place) and kve_step_ws (8192 caches, long moves
+    handed over), the decode form the benchmark times."""
     w = synth.WORKLOADS[3]
     T, next_pos = 24, w.prompt
     picks = {0: [0, 255], 17: [100], 31: [31, 200]}
-    _say(f"[full-batched] {w.name} layers={w.layers} bh={w.bh} sampled={picks} T={T}")
+    _say(f"[full-batched] {w.name} layers={w.layers} bh={w.bh} sampled={picks} T={T} ws={ws}")
     samples = {l: oracle_samples(w, l, hhs, w.budget, T, w.budget + 1, init_n=w.budget,
                                  next_pos=next_pos) for l, hhs in picks.items()}
     layers, ev, _ = run_batched(w, list(range(w.layers)), [w.budget] * w.layers, T, samples,
-                                w.budget, next_pos, dev)
+                                w.budget, next_pos, dev, workspace=ws)
     errs = []
     for l, ss in samples.items():
         for s in ss:
@@ -835,7 +842,7 @@ def test_policy_layers_tokens_equals_single(dev, kind, recent, S):
 @pytest.mark.parametrize("kind,d,n,recent,bh,sampled", [
     ("tova", 128, 1500, 16, 6, None),              # 8 score slots per thread; a long in-place move
     ("pyramid", 64, 5000, 8, 3, None),             # 24 slots: the weights go through LDS
-    ("tova", 128, 700, 200, 300, [0, 37, 150, 299]),   # 300 caches: the moves are handed over
+    ("tova", 128, 700, 200, 300, [0, 37, 150, 299]),   # 300 caches: moves handed over (workspace)
 ])
 def test_exact_tie_goes_to_lowest_candidate(dev, kind, d, n, recent, bh, sampled):
     """Every stored key the same vector: every stored row gets the same softmax
@@ -872,7 +879,8 @@ def test_exact_tie_goes_to_lowest_candidate(dev, kind, d, n, recent, bh, sampled
         nv[hh] = torch.from_numpy(v1.view(np.float16))
     ev = torch.full((bh,), -7, dtype=torch.int32, device=dev)
     batch = kve.LayerBatch([L], [budget], [kve.Counters(n, next_pos, next_pos)])
-    kve.step(batch, [nk.to(dev)], [nv.to(dev)], policy_for(w), [ev])
+    kve.step(batch, [nk.to(dev)], [nv.to(dev)], policy_for(w), [ev],
+             workspace=kve.workspace(bh, budget, d, dev))
     torch.cuda.synchronize()
     evn = ev.cpu().numpy()[None, :]
     assert bool((evn == n_sink).all()), np.unique(evn)
@@ -906,10 +914,10 @@ def test_policy_plain_equals_named_entry_points(dev):
             assert torch.equal(getattr(A, name)[:, :budget], getattr(B, name)[:, :budget]), name
 
 
-def _layers_tokens_equal_single_calls(dev, kind, shapes, T, S, seed, d=128):
+def _layers_tokens_equal_single_calls(dev, kind, shapes, T, S, seed, d=128, ws=False):
     """Layers (bh, budget, hh_base) from full synthetic states stepped T
     tokens, S per call of the batched form, give the same bits as single-token
-    calls per layer."""
+    calls per layer.  ws: the batched form is kve_step_ws with a workspace."""
     import kv_cache_eviction_step_amd as kve
     from gpu_harness import bulk_state
     kf = kind == "kf"
@@ -940,16 +948,23 @@ def _layers_tokens_equal_single_calls(dev, kind, shapes, T, S, seed, d=128):
             else:
                 kve.pyramid_step(As[l], nks[l][t], nvs[l][t], cas[l], budgets[l], *args, evas[l][t])
     batch = kve.LayerBatch(Bs, budgets, [kve.Counters(b, pos0, pos0) for b in budgets])
+    wsb = kve.workspace(sum(x[0] for x in shapes), max(budgets), d, dev) if ws else None
+    pol = (kve.policy("keyformer", 4, 0, 1.0, 2.0, 64, 1e4, 3) if kf else
+           kve.policy("pyramid", 4, rope_base=1e4))
     for t0 in range(0, T, S):
         t1 = min(T, t0 + S)
         ks = [x[t0:t1] for x in nks]
         vs = [x[t0:t1] for x in nvs]
         es = [x[t0:t1] for x in evbs]
-        if kf:
+        if ws:
+            kve.step(batch, ks, vs, pol, es, n_tokens=t1 - t0, workspace=wsb)
+        elif kf:
             kve.keyformer_step_layers_tokens(batch, ks, vs, *args, es)
         else:
             kve.pyramid_step_layers_tokens(batch, ks, vs, *args, es)
     torch.cuda.synchronize()
+    if ws:
+        assert not bool(wsb[:8].any())                 # the counters are back to zero
     for l in range(len(shapes)):
         assert torch.equal(evas[l], evbs[l]), l
         n = budgets[l]
@@ -961,14 +976,15 @@ def _layers_tokens_equal_single_calls(dev, kind, shapes, T, S, seed, d=128):
 
 
 @pytest.mark.parametrize("kind", ["kf", "pk"])
-@pytest.mark.parametrize("S", [1, 8])
-def test_more_layers_than_one_launch_equal_single_calls(dev, kind, S):
+@pytest.mark.parametrize("S,ws", [(1, False), (1, True), (8, False)])
+def test_more_layers_than_one_launch_equal_single_calls(dev, kind, S, ws):
     """40 layers in one call are two launches (descriptors of up to 32 layers
-    travel with a launch); with one token per call the first launch holds 256
-    caches, so Keyformer hands its long moves over and the second does not.
+    travel with a launch); with one token per call and a workspace the first
+    launch holds 256 caches, so Keyformer hands its long moves over, and the
+    second (64 caches) does not: the two launches share one workspace.
     Budgets 40 .. 313, Gumbel streams offset per layer."""
     shapes = [(8, 40 + 7 * l, 8 * l) for l in range(40)]
-    _layers_tokens_equal_single_calls(dev, kind, shapes, 24, S, 61 + S)
+    _layers_tokens_equal_single_calls(dev, kind, shapes, 24, S, 61 + S, ws=ws)
 
 
 @pytest.mark.parametrize("kind", ["kf", "pk"])
@@ -1012,11 +1028,11 @@ def test_layers_tokens_streamed_keys_equal_single_calls(dev, kind):
 def test_launch_size_paths_agree(dev, kind, budget, S, d):
     """A launch's grid size picks code paths that must not change any bit:
     320 caches in one launch (more workgroups than compute units: state loads
-    after the key pass; Keyformer single tokens hand moves over 128 rows to
-    the move kernel; at budget 3000 with S = 16, keys streamed) against the
-    same caches in two launches of 160 (state loads before the key pass;
-    every cache compacted by its own workgroup; keys cached between tokens),
-    from a full synthetic state."""
+    after the key pass; single tokens go through kve_step_ws, so Keyformer
+    hands moves over 128 rows to the move kernel; at budget 3000 with S = 16,
+    keys streamed) against the same caches in two launches of 160 (state
+    loads before the key pass; every cache compacted by its own workgroup;
+    keys cached between tokens), from a full synthetic state."""
     import kv_cache_eviction_step_amd as kve
     from gpu_harness import bulk_state
     kf = kind == "kf"
@@ -1038,10 +1054,16 @@ def test_launch_size_paths_agree(dev, kind, budget, S, d):
     ev_a = torch.full((T, bh), -9, dtype=torch.int32, device=dev)
     ev_p = [torch.full((T, half), -9, dtype=torch.int32, device=dev) for _ in range(2)]
     args = (4, 1.0, 2.0, 64, 1e4, 5) if kf else (4, 1e4)
+    pol = (kve.policy("keyformer", 4, 0, 1.0, 2.0, 64, 1e4, 5) if kf else
+           kve.policy("pyramid", 4, rope_base=1e4))
+    wsa = kve.workspace(bh, budget, d, dev)
 
-    def run(L, ks, vs, ev, c):
+    def run(L, ks, vs, ev, c, ws=None):
+        b = kve.LayerBatch([L], [budget], [c]) if ws is not None else None
         for t0 in range(0, T, S):
-            if S == 1 and kf:
+            if S == 1 and ws is not None:
+                kve.step(b, [ks[t0]], [vs[t0]], pol, [ev[t0]], workspace=ws)
+            elif S == 1 and kf:
                 kve.keyformer_step(L, ks[t0], vs[t0], c, budget, *args, ev[t0])
             elif S == 1:
                 kve.pyramid_step(L, ks[t0], vs[t0], c, budget, *args, ev[t0])
@@ -1052,12 +1074,13 @@ def test_launch_size_paths_agree(dev, kind, budget, S, d):
                 kve.pyramid_step_tokens(L, ks[t0:t0 + S], vs[t0:t0 + S], c, budget, *args,
                                         ev[t0:t0 + S])
 
-    run(A, nk, nv, ev_a, kve.Counters(budget, pos0, pos0))
+    run(A, nk, nv, ev_a, kve.Counters(budget, pos0, pos0), wsa if S == 1 else None)
     for i in range(2):
         sl = slice(i * half, (i + 1) * half)
         run(parts[i], nk[:, sl].contiguous(), nv[:, sl].contiguous(), ev_p[i],
             kve.Counters(budget, pos0, pos0))
     torch.cuda.synchronize()
+    assert not bool(wsa[:8].any())
     assert torch.equal(ev_a, torch.cat(ev_p, dim=1))
     for name in ("k", "v", "scores", "positions") + (("gumbel",) if kf else ()):
         joined = torch.cat([getattr(p, name) for p in parts])
@@ -1069,9 +1092,9 @@ def test_launch_size_paths_agree(dev, kind, budget, S, d):
 @pytest.mark.parametrize("recent", [8, 200])
 def test_tova_handoff_equals_own_moves(dev, recent):
     """TOVA scoring with a window (without one the incoming row, at score 0,
-    is always the one evicted) on 320 caches, one token per call: long moves
-    go to the move kernel; two calls of 160 caches compact every cache in its
-    own workgroup.  Same bits."""
+    is always the one evicted) on 320 caches, one token per kve_step_ws call:
+    long moves go to the move kernel; two kve_step calls of 160 caches compact
+    every cache in its own workgroup.  Same bits."""
     import kv_cache_eviction_step_amd as kve
     from gpu_harness import bulk_state
     bh, half, d, budget, T, pos0 = 320, 160, 128, 1500, 24, 5000
@@ -1093,12 +1116,14 @@ def test_tova_handoff_equals_own_moves(dev, recent):
     ba = kve.LayerBatch([A], [budget], [kve.Counters(budget, pos0, pos0)])
     bp = [kve.LayerBatch([parts[i]], [budget], [kve.Counters(budget, pos0, pos0)])
           for i in range(2)]
+    ws = kve.workspace(bh, budget, d, dev)
     for t in range(T):
-        kve.step(ba, [nk[t]], [nv[t]], pol, [ev_a[t]])
+        kve.step(ba, [nk[t]], [nv[t]], pol, [ev_a[t]], workspace=ws)
         for i in range(2):
             sl = slice(i * half, (i + 1) * half)
             kve.step(bp[i], [nk[t, sl].contiguous()], [nv[t, sl].contiguous()], pol, [ev_p[i][t]])
     torch.cuda.synchronize()
+    assert not bool(ws[:8].any())
     assert torch.equal(ev_a, torch.cat(ev_p, dim=1))
     for name in ("k", "v", "scores", "positions"):
         joined = torch.cat([getattr(p, name) for p in parts])
@@ -1109,8 +1134,8 @@ def test_tova_handoff_equals_own_moves(dev, recent):
 
 @pytest.mark.parametrize("d", [128, 64])
 def test_handoff_edges_against_oracle(dev, d):
-    """One single-token Keyformer launch of 320 caches (moves over 128 rows go
-    to the move kernel), sampled caches steered to the edges of the handoff
+    """One single-token Keyformer kve_step_ws launch of 320 caches (moves over
+    128 rows go to the move kernel), sampled caches steered to the edges of the handoff
     and checked against the oracle bit for bit: row 0 with no sinks (999 rows
     move: every one of the 16 scratch chunk slots is used), 998 rows, exactly
     129 rows (the shortest move handed over, a last chunk of one row), exactly
@@ -1149,19 +1174,20 @@ def test_handoff_edges_against_oracle(dev, d):
         nk[s.hh] = torch.from_numpy(s.ks[0].view(np.float16)).to(dev)
         nv[s.hh] = torch.from_numpy(s.vs[0].view(np.float16)).to(dev)
     ev = torch.full((bh,), -7, dtype=torch.int32, device=dev)
-    ctr = kve.Counters(n, next_pos, next_pos)
-    prm = params_for(w, budget, 0)
-    kve.keyformer_step(L, nk, nv, ctr, budget, n_sink, prm.tau_init, prm.tau_end,
-                       prm.anneal_steps, w.rope_base, w.gumbel_seed, ev)
+    batch = kve.LayerBatch([L], [budget], [kve.Counters(n, next_pos, next_pos)])
+    ws = kve.workspace(bh, budget, d, dev)
+    kve.step(batch, [nk], [nv], policy_for(w), [ev], workspace=ws)
     torch.cuda.synchronize()
+    ctr = batch.ctrs[0]
+    assert not bool(ws[:8].any())
     evn = ev.cpu().numpy()
     _assert_parity(L, evn[None, :], samples, next_pos)
     assert ((evn >= 0) & (evn <= n)).all()
     assert ctr.n_kept == budget
 
 def test_handoff_largest_budget_against_oracle(dev):
-    """The largest budget (12288 rows) in a single-token Keyformer launch of 256
-    caches, which hands long moves over: sampled caches steered to row 0 with
+    """The largest budget (12288 rows) in a single-token Keyformer kve_step_ws
+    launch of 256 caches, which hands long moves over: sampled caches steered to row 0 with
     no sinks (12287 rows move: 192 chunks, every scratch slot of the launch),
     a middle row, and the newest stored row; bit for bit against the oracle."""
     import kv_cache_eviction_step_amd as kve
@@ -1194,22 +1220,22 @@ def test_handoff_largest_budget_against_oracle(dev):
         nk[s.hh] = torch.from_numpy(s.ks[0].view(np.float16)).to(dev)
         nv[s.hh] = torch.from_numpy(s.vs[0].view(np.float16)).to(dev)
     ev = torch.full((bh,), -7, dtype=torch.int32, device=dev)
-    ctr = kve.Counters(n, next_pos, next_pos)
-    prm = params_for(w, budget, 0)
-    kve.keyformer_step(L, nk, nv, ctr, budget, n_sink, prm.tau_init, prm.tau_end,
-                       prm.anneal_steps, w.rope_base, w.gumbel_seed, ev)
+    batch = kve.LayerBatch([L], [budget], [kve.Counters(n, next_pos, next_pos)])
+    ws = kve.workspace(bh, budget, d, dev)
+    kve.step(batch, [nk], [nv], policy_for(w), [ev], workspace=ws)
     torch.cuda.synchronize()
+    ctr = batch.ctrs[0]
+    assert not bool(ws[:8].any())
     evn = ev.cpu().numpy()
     _assert_parity(L, evn[None, :], samples, next_pos)
     assert ((evn >= 0) & (evn <= n)).all()
 
 def test_batched_handoff_mixed_budgets_equals_own_moves(dev):
-    """kve_step with TOVA scoring and a 200-row window over two layers of 160
-    caches with budgets 1500 and 700, one token per call: as one launch (320
-    caches: long moves go to the move kernel, whose per-workgroup scratch is
-    sized by the larger budget and indexed across both layers) and as one
-    launch per layer (160 caches: every cache compacted by its own
-    workgroup).  Same bits."""
+    """TOVA scoring and a 200-row window over two layers of 160 caches with
+    budgets 1500 and 700, one token per call: as one kve_step_ws launch (320
+    caches: long moves go to the move kernel, the workspace sized by the larger
+    budget and shared by both layers) and as one kve_step launch per layer
+    (160 caches: every cache compacted by its own workgroup).  Same bits."""
     import kv_cache_eviction_step_amd as kve
     from gpu_harness import bulk_state
     half, d, T, pos0, recent = 160, 128, 16, 6000, 200
@@ -1232,11 +1258,14 @@ def test_batched_handoff_mixed_budgets_equals_own_moves(dev):
     ba = kve.LayerBatch(A, budgets, [kve.Counters(b, pos0, pos0) for b in budgets])
     bb = [kve.LayerBatch([B[i]], [budgets[i]], [kve.Counters(budgets[i], pos0, pos0)])
           for i in range(2)]
+    ws = kve.workspace(2 * half, max(budgets), d, dev)
     for t in range(T):
-        kve.step(ba, [nk[0, t], nk[1, t]], [nv[0, t], nv[1, t]], pol, [ev_a[0, t], ev_a[1, t]])
+        kve.step(ba, [nk[0, t], nk[1, t]], [nv[0, t], nv[1, t]], pol, [ev_a[0, t], ev_a[1, t]],
+                 workspace=ws)
         for i in range(2):
             kve.step(bb[i], [nk[i, t]], [nv[i, t]], pol, [ev_b[i, t]])
     torch.cuda.synchronize()
+    assert not bool(ws[:8].any())
     assert torch.equal(ev_a, ev_b)
     for i, b in enumerate(budgets):
         for name in ("k", "v", "scores", "positions"):
@@ -1245,15 +1274,16 @@ def test_batched_handoff_mixed_budgets_equals_own_moves(dev):
         assert int(moved.max()) > 128                  # some move was handed over
 
 def test_captured_step_replays_match_eager(dev):
-    """keyformer_step captured into a graph on 320 caches.  Eagerly, long
-    moves of such a launch go to the move kernel; under capture the launch
-    compacts in place (the move queue's host-side state cannot be replayed).
-    Each replay, from the same restored state and with eager work and a
-    synchronisation between replays, must give the eager call's bits."""
+    """A Keyformer kve_step_ws call on 320 caches, which hands its long moves
+    to the move kernel through the workspace, captured into a graph: the
+    workspace's counters return to zero inside the captured work, so each
+    replay, from the same restored state and with eager work and a
+    synchronisation between replays, gives the eager call's bits (and the
+    in-place keyformer_step's)."""
     import kv_cache_eviction_step_amd as kve
     from gpu_harness import bulk_state
     bh, d, budget, pos0 = 320, 128, 1000, 6000
-    _say(f"[graph capture] keyformer_step bh={bh} budget={budget} d={d}")
+    _say(f"[graph capture] kve_step_ws bh={bh} budget={budget} d={d}")
     w = synth.Workload("graph", 1, 1, bh, d, pos0, 1, budget, 4, "keyformer", 1.0, 2.0, 64)
     gen = torch.Generator(device=dev)
     gen.manual_seed(83)
@@ -1261,22 +1291,35 @@ def test_captured_step_replays_match_eager(dev):
     bulk_state(S0, budget, w, gen)
     nk, nv = synth.bulk_kv_torch(w, pos0, 1, bh, gen, dev)
     names = ("k", "v", "scores", "gumbel", "positions")
+    pol = kve.policy("keyformer", 4, 0, 1.0, 2.0, 64, 1e4, 5)
 
     def copy_of(L):
         return kve.Layer(*[getattr(L, x).clone() for x in names])
 
-    args = (budget, 4, 1.0, 2.0, 64, 1e4, 5)
+    def call(L, ev, ws):
+        b = kve.LayerBatch([L], [budget], [kve.Counters(budget, pos0, pos0)])
+        kve.step(b, [nk[0]], [nv[0]], pol, [ev], workspace=ws)
+
+    P = copy_of(S0)                                   # in place, for reference
+    ev_p = torch.full((bh,), -9, dtype=torch.int32, device=dev)
+    kve.keyformer_step(P, nk[0], nv[0], kve.Counters(budget, pos0, pos0), budget, 4, 1.0, 2.0,
+                       64, 1e4, 5, ev_p)
     E = copy_of(S0)
     ev_e = torch.full((bh,), -9, dtype=torch.int32, device=dev)
-    kve.keyformer_step(E, nk[0], nv[0], kve.Counters(budget, pos0, pos0), *args, ev_e)
+    ws = kve.workspace(bh, budget, d, dev)
+    call(E, ev_e, ws)
     torch.cuda.synchronize()
-    assert int((budget - ev_e)[ev_e >= 0].max()) > 128   # eagerly, some move was handed over
+    assert int((budget - ev_e)[ev_e >= 0].max()) > 128   # some move was handed over
+    assert not bool(ws[:8].any())                      # the counters are back to zero
+    assert torch.equal(ev_e, ev_p)
+    for x in names:
+        assert torch.equal(getattr(E, x)[:, :budget], getattr(P, x)[:, :budget]), x
 
     G = copy_of(S0)
     ev_g = torch.full((bh,), -9, dtype=torch.int32, device=dev)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        kve.keyformer_step(G, nk[0], nv[0], kve.Counters(budget, pos0, pos0), *args, ev_g)
+        call(G, ev_g, ws)
     for replay in range(3):
         for x in names:
             getattr(G, x).copy_(getattr(S0, x))
@@ -1284,10 +1327,49 @@ def test_captured_step_replays_match_eager(dev):
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
+        assert not bool(ws[:8].any()), replay
         assert torch.equal(ev_g, ev_e), replay
         for x in names:
             assert torch.equal(getattr(G, x)[:, :budget], getattr(E, x)[:, :budget]), (replay, x)
 
+
+@pytest.mark.parametrize("items", [1, 3, 12])
+def test_workspace_too_small_falls_back_in_place(dev, items):
+    """kve_step_ws with a workspace of only 1, 3 or 12 items on 320 Keyformer
+    caches of 1000 rows: caches whose reservation does not fit compact in
+    place, the rest hand their moves over; every call equals the in-place
+    keyformer_step bit for bit, and the counters return to zero."""
+    import kv_cache_eviction_step_amd as kve
+    from gpu_harness import bulk_state
+    bh, d, budget, pos0, T = 320, 128, 1000, 6000, 12
+    _say(f"[small workspace] items={items} bh={bh} budget={budget} T={T}")
+    w = synth.Workload("small-ws", 1, 1, bh, d, pos0, T, budget, 4, "keyformer", 1.0, 2.0, 64)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(131 + items)
+    A = kve.Layer.empty(bh, budget + 1, d, dev, gumbel=True)
+    bulk_state(A, budget, w, gen)
+    names = ("k", "v", "scores", "gumbel", "positions")
+    B = kve.Layer(*[getattr(A, x).clone() for x in names])
+    nk, nv = synth.bulk_kv_torch(w, pos0, T, bh, gen, dev)
+    nbytes = 256 + -(-items * 32 // 256) * 256 + items * 4 * d   # kve_workspace_size's layout
+    raw = torch.zeros(nbytes + 256, dtype=torch.uint8, device=dev)
+    off = (-raw.data_ptr()) % 256
+    ws = raw[off:off + nbytes]
+    pol = kve.policy("keyformer", 4, 0, 1.0, 2.0, 64, 1e4, 5)
+    ba = kve.LayerBatch([A], [budget], [kve.Counters(budget, pos0, pos0)])
+    cb = kve.Counters(budget, pos0, pos0)
+    ev_a = torch.full((T, bh), -9, dtype=torch.int32, device=dev)
+    ev_b = torch.full((T, bh), -9, dtype=torch.int32, device=dev)
+    for t in range(T):
+        kve.step(ba, [nk[t]], [nv[t]], pol, [ev_a[t]], workspace=ws)
+        kve.keyformer_step(B, nk[t], nv[t], cb, budget, 4, 1.0, 2.0, 64, 1e4, 5, ev_b[t])
+    torch.cuda.synchronize()
+    assert not bool(ws[:8].any())
+    assert torch.equal(ev_a, ev_b)
+    for x in names:
+        assert torch.equal(getattr(A, x)[:, :budget], getattr(B, x)[:, :budget]), x
+    long_moves = int(((ev_a >= 0) & (budget - 1 - ev_a > 128)).sum())
+    assert long_moves > items                        # some moves could not be handed over
 
 
 def test_captured_batched_call_replays_match_eager(dev):

@@ -25,18 +25,27 @@
 
 float oracle_f16_to_f32(uint16_t h)
 {
-    int sign = (h >> 15) & 1;
-    int e = (h >> 10) & 0x1f;
-    int f = h & 0x3ff;
-    double mag;
+    /* Every binary16 value is a binary32 value, so the result is exact.      */
+    /* Normal numbers (1.f) * 2^(e-15) keep their fraction bits (shifted to   */
+    /* the top of binary32's 23) under the exponent re-biased from 15 to 127; */
+    /* zero and the subnormals f * 2^-24 are an integer times a power of two, */
+    /* exact in binary32; exponent 31 is infinity (f = 0) or NaN.             */
+    uint32_t sign = (uint32_t)(h >> 15) << 31;
+    uint32_t e = (h >> 10) & 0x1f;
+    uint32_t f = h & 0x3ff;
+    uint32_t bits;
     if (e == 0x1f) {
-        mag = f ? NAN : INFINITY;
+        bits = sign | 0x7f800000u | (f << 13);          /* inf / NaN          */
     } else if (e == 0) {
-        mag = ldexp((double)f, -24);               /* zero or subnormal   */
+        float m = (float)f * 0x1p-24f;                  /* zero or subnormal  */
+        memcpy(&bits, &m, sizeof bits);
+        bits |= sign;
     } else {
-        mag = ldexp((double)(1024 + f), e - 25);   /* (1.f) * 2^(e-15)    */
+        bits = sign | ((e - 15 + 127) << 23) | (f << 13);
     }
-    return (float)(sign ? -mag : mag);            /* exact: fits binary32 */
+    float out;
+    memcpy(&out, &bits, sizeof out);
+    return out;
 }
 
 /* Round a binary32 value to the nearest binary16 value, ties to even.

@@ -1427,3 +1427,181 @@ def test_captured_batched_call_replays_match_eager(dev):
             n = budgets[l]
             for x in names:
                 assert torch.equal(getattr(Lg, x)[:, :n], getattr(Le, x)[:, :n]), (replay, l, x)
+
+# ---------------------------------------------------------------------------
+# the long-context workload's whole run, as the benchmark times it
+# ---------------------------------------------------------------------------
+
+def _token_stream(args):
+    """The unguarded input stream of one cache (worker process)."""
+    w, layer, hh, T = args
+    return synth.token_kv(w, layer, hh, np.arange(T))
+
+
+@pytest.mark.timeout(1200)
+def test_whole_run_long_context_every_layer(dev):
+    """The long-context PyramidKV workload's whole run: 16384 prompt + 1024
+    decode tokens from empty caches through all 32 layers x 512 caches
+    (budgets 6144 .. 2048), one pyramid_step launch per layer per token -- the
+    benchmark's launch form.  On the way each cache grows through the 2-, 8-
+    and 24-slot paths of a launch of more workgroups than compute units, and
+    its oldest rows take 17408 score increments.
+
+    One cache per layer, spread over batch and head and so over every budget
+    of the taper, runs through the oracle in worker processes while the GPU
+    runs; at the end every one of its evicted indices, kept tokens, values,
+    keys, positions and scores is compared.  Every other cache is checked by
+    what holds at any size at tau 0 ("PyramidKV -- Layer-Adaptive Budget
+    Attention-Mass Eviction", How it works; Relationship to H2O): a stored
+    row's score is positive by the time the argmin is taken, so each
+    over-budget step evicts exactly the incoming row, at index n, and no step
+    under the budget evicts; positions stay 0 .. n-1; scores stay finite and
+    non-negative.  The margin guard of the sampled caches never redraws here
+    (the two smallest keys are the incoming row's 0 and a positive score,
+    whose gap passes the relative margin), which the test asserts, since the
+    GPU is fed the undrawn stream."""
+    import os
+    from concurrent.futures import ProcessPoolExecutor
+    import kv_cache_eviction_step_amd as kve
+    from gpu_harness import _sample_job
+    w = synth.WORKLOADS[4]
+    budgets = oracle.pyramid_budgets(w.layers, w.budget, w.n_sink, w.beta)
+    L, bh, d, T = w.layers, w.bh, w.d, w.tokens
+    picks = [(l, (5 + 97 * l) % bh) for l in range(L)]
+    _say(f"[whole-run] {w.name} layers={L} bh={bh} T={T} budgets {budgets[0]}..{budgets[-1]}; "
+         f"sampled {picks}")
+    # worker processes start before any of the run's device memory exists
+    workers = max(1, min(16, (os.cpu_count() or 2) - 1))
+    ex = ProcessPoolExecutor(workers)
+    try:
+        streams = [ex.submit(_token_stream, (w, l, hh, T)) for l, hh in picks]
+        jobs = sorted(((w, l, hh, budgets[l], T, budgets[l] + 1, None, 0) for l, hh in picks),
+                      key=lambda j: -j[3])             # the longest oracle runs first
+        futs = {j[1]: ex.submit(_sample_job, j) for j in jobs}
+
+        layers = [kve.Layer.empty(bh, b + 1, d, dev, gumbel=False) for b in budgets]
+        cls = [x.c_struct() for x in layers]
+        ctrs = [kve.Counters(0, 0, 0) for _ in range(L)]
+        sk = torch.empty((L, T, d), dtype=torch.float16, device=dev)
+        sv = torch.empty_like(sk)
+        for l, f in enumerate(streams):
+            k, v = f.result()
+            sk[l] = torch.from_numpy(k.view(np.float16)).to(dev)
+            sv[l] = torch.from_numpy(v.view(np.float16)).to(dev)
+        _say(f"[whole-run] inputs of the sampled caches ready; GPU run")
+        chunk = 64
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(4242)
+        ins_k = torch.empty((L, chunk, bh, d), dtype=torch.float16, device=dev)
+        ins_v = torch.empty_like(ins_k)
+        ev = torch.empty((L, chunk, bh), dtype=torch.int32, device=dev)
+        vk = [[ins_k[l, s] for s in range(chunk)] for l in range(L)]
+        vv = [[ins_v[l, s] for s in range(chunk)] for l in range(L)]
+        ve = [[ev[l, s] for s in range(chunk)] for l in range(L)]
+        lidx = torch.arange(L, device=dev)
+        hidx = torch.tensor([hh for _, hh in picks], device=dev)
+        bud = torch.tensor(budgets, device=dev, dtype=torch.int64)
+        n_all = torch.minimum(torch.arange(T, device=dev)[None, :], bud[:, None])  # [L, T]
+        expect = torch.where(n_all + 1 > bud[:, None], n_all, -1).to(torch.int32)
+        ev_s = torch.empty((L, T), dtype=torch.int32, device=dev)
+        bad = torch.zeros((), dtype=torch.int64, device=dev)
+        for t0 in range(0, T, chunk):
+            cnt = min(chunk, T - t0)
+            for l, (_, hh) in enumerate(picks):
+                synth.bulk_kv_torch(w, t0, cnt, bh, gen, dev, out_k=ins_k[l, :cnt],
+                                    out_v=ins_v[l, :cnt])
+                ins_k[l, :cnt, hh] = sk[l, t0:t0 + cnt]
+                ins_v[l, :cnt, hh] = sv[l, t0:t0 + cnt]
+            for s in range(cnt):
+                for l in range(L):
+                    kve.pyramid_step(layers[l], vk[l][s], vv[l][s], ctrs[l], budgets[l],
+                                     w.n_sink, w.rope_base, ve[l][s], c_layer=cls[l])
+            bad += (ev[:, :cnt] != expect[:, t0:t0 + cnt, None]).sum()
+            ev_s[:, t0:t0 + cnt] = ev[lidx[:, None], torch.arange(cnt, device=dev)[None, :],
+                                      hidx[:, None]]
+            if t0 % 4096 == 0:
+                _say(f"[whole-run] token {t0} of {T} enqueued")
+        torch.cuda.synchronize()
+        _say("[whole-run] GPU done; waiting for the oracle")
+        assert int(bad) == 0, f"{int(bad)} cache-steps evicted other than the incoming row"
+        for l in range(L):
+            assert (ctrs[l].n_kept, ctrs[l].next_pos, ctrs[l].pos) == (budgets[l], T, T)
+            b = budgets[l]
+            assert torch.equal(layers[l].positions[:, :b],
+                               torch.arange(b, device=dev, dtype=torch.int32)[None, :].expand(bh, b))
+            sc = layers[l].scores[:, :b]
+            assert bool(torch.isfinite(sc).all()) and bool((sc >= 0).all())
+        evn = ev_s.cpu().numpy()
+        errs = []
+        for l, hh in picks:
+            s = futs[l].result()
+            assert s.attempts == 0, f"layer {l} cache {hh}: the guard redrew {s.attempts} tokens"
+            k, v = streams[l].result()
+            assert np.array_equal(s.ks, k) and np.array_equal(s.vs, v)
+            errs += [f"layer {l}: {e}" for e in compare_cache(layers[l], hh, s, evn[l], 0)]
+        assert not errs, "\n".join(errs[:20])
+    finally:
+        ex.shutdown(wait=False, cancel_futures=True)
+
+
+# ---------------------------------------------------------------------------
+# checkpoint / resume
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("form", ["single-token", "48-token"])
+def test_save_restore_resumes_bit_exact(dev, tmp_path, form):
+    """KeyformerState's `pos` ("veloxquant_mlx.quantizers.keyformer module"):
+    the frozen noise and the temperature depend on the running position
+    alone, not on how the stream is cut into calls.  A Keyformer layer
+    stepped T1 tokens, its tensors and counters written with torch.save, the
+    originals freed, the file loaded into fresh device tensors and stepped T2
+    more tokens, equals T1 + T2 tokens stepped straight, bit for bit: evicted
+    indices, keys, values, scores, Gumbel values, positions and counters.
+    The resumed part runs as single-token calls or as calls of 48 tokens
+    (the last one ragged); the budget is crossed before the save and the
+    annealing ends after it."""
+    import kv_cache_eviction_step_amd as kve
+    bh, d, budget, T1, T2 = 48, 128, 300, 420, 260
+    T = T1 + T2
+    _say(f"[save/restore] form={form} bh={bh} budget={budget} T1={T1} T2={T2}")
+    w = synth.Workload("resume", 1, 1, bh, d, T, 0, budget, 4, "keyformer", 1.0, 2.0, 500)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(17)
+    nk, nv = synth.bulk_kv_torch(w, 0, T, bh, gen, dev)
+    args = (budget, 4, 1.0, 2.0, 500, 1e4, 11)
+    names = ("k", "v", "scores", "gumbel", "positions")
+
+    A = kve.Layer.empty(bh, budget + 1, d, dev, gumbel=True)
+    ca = kve.Counters(0, 0, 0)
+    ev_a = torch.full((T, bh), -9, dtype=torch.int32, device=dev)
+    for t in range(T):
+        kve.keyformer_step(A, nk[t], nv[t], ca, *args, ev_a[t])
+
+    B = kve.Layer.empty(bh, budget + 1, d, dev, gumbel=True)
+    cb = kve.Counters(0, 0, 0)
+    ev_b = torch.full((T, bh), -9, dtype=torch.int32, device=dev)
+    for t in range(T1):
+        kve.keyformer_step(B, nk[t], nv[t], cb, *args, ev_b[t])
+    torch.cuda.synchronize()
+    path = tmp_path / "layer_state.pt"
+    torch.save({**{x: getattr(B, x) for x in names},
+                "counters": [cb.n_kept, cb.next_pos, cb.pos]}, path)
+    del B
+    torch.cuda.empty_cache()
+    st = torch.load(path, weights_only=True, map_location=dev)
+    C = kve.Layer(*[st[x] for x in names])
+    cc = kve.Counters(*st["counters"])
+    assert (cc.n_kept, cc.next_pos, cc.pos) == (budget, T1, T1)
+    if form == "single-token":
+        for t in range(T1, T):
+            kve.keyformer_step(C, nk[t], nv[t], cc, *args, ev_b[t])
+    else:
+        for t0 in range(T1, T, 48):
+            t1 = min(T, t0 + 48)
+            kve.keyformer_step_tokens(C, nk[t0:t1], nv[t0:t1], cc, *args, ev_b[t0:t1])
+    torch.cuda.synchronize()
+    assert (cc.n_kept, cc.next_pos, cc.pos) == (ca.n_kept, ca.next_pos, ca.pos)
+    assert torch.equal(ev_a, ev_b)
+    for x in names:
+        assert torch.equal(getattr(A, x)[:, :budget], getattr(C, x)[:, :budget]), x
+    assert bool(((ev_a[T1:] >= 0) & (ev_a[T1:] < budget)).any())   # interior evictions resumed

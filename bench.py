@@ -54,6 +54,14 @@ def parse():
                     help="protect the last R rows from eviction (kve_step)")
     ap.add_argument("--tova", action="store_true",
                     help="TOVA-adapted scoring (current-step weight; kve_step)")
+    ap.add_argument("--workspace", action="store_true",
+                    help="single-token launches through kve_step_ws with a workspace sized for "
+                         "every move (long compactions handed to the move kernel)")
+    ap.add_argument("--skip-late-riser", action="store_true",
+                    help="leave out the 8B-shaped late-riser decode object of the default line")
+    ap.add_argument("--late-riser-only", action="store_true",
+                    help="run only the 8B-shaped late-riser object (prompt, then the three "
+                         "decode forms) and print it")
     ap.add_argument("--whole-run", action="store_true",
                     help="time the whole trajectory instead (prompt + decode from empty "
                          "caches, token by token; --steps / --warmup / --fill unused)")
@@ -145,10 +153,25 @@ def bandwidth_context(dev) -> dict:
     b.record()
     torch.cuda.synchronize()
     copy_gbs = 5 * 2 * n * 4 / (a.elapsed_time(b) / 1e3) / 1e9
-    del src, dst
+    del dst
+    # a read-only stream: the sum of 4 GiB (the eviction step reads far more
+    # than it writes)
+    big = torch.ones((1 << 32) // 4, dtype=torch.float32, device=dev)
+    acc = torch.empty((), dtype=torch.float32, device=dev)
+    torch.sum(big, dim=0, out=acc)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(5):
+        torch.sum(big, dim=0, out=acc)
+    b.record()
+    torch.cuda.synchronize()
+    read_gbs = 5 * big.numel() * 4 / (a.elapsed_time(b) / 1e3) / 1e9
+    del src, big
     torch.cuda.empty_cache()
     return {"copy_kernel_GBs": copy_gbs,
-            "copy_kernel": "torch elementwise copy, 1 GiB read + 1 GiB written"}
+            "copy_kernel": "torch elementwise copy, 1 GiB read + 1 GiB written",
+            "read_kernel_GBs": read_gbs,
+            "read_kernel": "torch sum of 4 GiB of fp32 (reads only)"}
 
 
 def step_bytes(kind: str, n: int, d: int, m, over: bool = True):
@@ -173,10 +196,12 @@ def cpu_baseline(w, budgets, seconds: float):
     wall_all = max(r[1] for r in res)
     return {
         "value": steps_all / wall_all, "unit": "cache-row updates/s", "cores": procs,
-        "kind": "oracle", "single_core": one[0] / one[1],
+        "host_cores": os.cpu_count(), "kind": "oracle", "single_core": one[0] / one[1],
         "sample": (f"{procs} caches (one per process, layers {layers[0]}..{layers[-1]}), each "
                    f"from a synthetic steady state at its layer budget, stepped token by token "
-                   f"for ~{seconds / 2:.0f} s; single_core = one such cache alone"),
+                   f"for ~{seconds / 2:.0f} s; single_core = one such cache alone; "
+                   f"{procs} of the host's {os.cpu_count()} cores used, one oracle "
+                   f"process each"),
         "cpu": cpu_model(),
     }
 
@@ -228,6 +253,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.late_riser_only:
+        print(json.dumps({"late_riser_8b": late_riser_decode(dev)}), flush=True)
+        return
     w = synth.WORKLOADS[args.config]
     if args.tova or args.recent:
         w = dataclasses.replace(w, kind="tova" if args.tova else w.kind, recent=args.recent,
@@ -254,19 +282,23 @@ def main():
         sys.exit(2)
 
     # ---- the calls: named entry points, or kve_step for the extensions --------
-    use_policy = w.kind == "tova" or w.recent > 0
+    use_policy = w.kind == "tova" or w.recent > 0 or args.workspace
     pol = (kve.policy(w.kind, w.n_sink, w.recent, w.tau_init, w.tau_end, w.anneal_steps,
                       w.rope_base, w.gumbel_seed) if use_policy else None)
     name = "keyformer" if kf else "pyramid"
+    general = "kve_step_ws" if args.workspace else "kve_step"
     if args.batched:
         batch = kve.LayerBatch(layers, budgets)
         singles = None
-        entry = ("kve_step" if use_policy else
+        entry = (general if use_policy else
                  f"{name}_step_layers" + ("_tokens" if TPC > 1 else ""))
     else:
         batch = None
         singles = [kve.LayerBatch([layers[l]], [budgets[l]]) for l in range(L)]
-        entry = "kve_step" if use_policy else f"{name}_step" + ("_tokens" if TPC > 1 else "")
+        entry = general if use_policy else f"{name}_step" + ("_tokens" if TPC > 1 else "")
+    # one workspace serves every launch (calls on one stream are ordered)
+    ws = (kve.workspace(bh * (L if args.batched else 1), max(budgets), d, dev)
+          if args.workspace else None)
 
     def ctr(l):
         return batch.ctrs[l] if batch is not None else singles[l].ctrs[0]
@@ -277,7 +309,7 @@ def main():
         if batch is not None:
             ks, vs = nk[:, s0:s0 + S], nv[:, s0:s0 + S]
             if use_policy:
-                kve.step(batch, ks, vs, pol, ev_out, n_tokens=S)
+                kve.step(batch, ks, vs, pol, ev_out, n_tokens=S, workspace=ws)
             elif S > 1 and kf:
                 kve.keyformer_step_layers_tokens(batch, ks, vs, w.n_sink, w.tau_init,
                                                  w.tau_end, w.anneal_steps, w.rope_base,
@@ -299,7 +331,7 @@ def main():
             c = singles[l].ctrs[0]
             if use_policy:
                 kve.step(singles[l], ks[None], vs[None], pol,
-                         e_l[None] if e_l is not None else None, n_tokens=S)
+                         e_l[None] if e_l is not None else None, n_tokens=S, workspace=ws)
             elif S > 1 and kf:
                 kve.keyformer_step_tokens(layers[l], ks, vs, c, budgets[l], w.n_sink,
                                           w.tau_init, w.tau_end, w.anneal_steps, w.rope_base,
@@ -414,6 +446,13 @@ def main():
             "mean_rows_moved_per_cache_step": wr["config"]["mean_rows_moved_per_cache_step"],
             "timing": wr["config"]["timing"],
         }
+    if not args.skip_late_riser and not (args.config == 3 or args.tova or args.recent or
+                                         args.workspace or args.batched or TPC > 1):
+        # the default line also carries the 8B-shaped workload, decoded
+        del layers, cls
+        batch = singles = None
+        torch.cuda.empty_cache()
+        out["late_riser_8b"] = late_riser_decode(dev)
     print(json.dumps(out), flush=True)
 
 
@@ -463,6 +502,170 @@ def result_line(args, w, budgets, bh, L, d, TPC, batch, entry, steps, warmup, ms
             "algorithmic_bytes_per_launch": bytes_per_launch,
         },
         "cpu_baseline": cpu,
+    }
+
+
+def late_riser_decode(dev) -> dict:
+    """The 8B-shaped late-riser Keyformer workload (B=32, 32 layers, 8 kv-heads,
+    D=128, budget 1024, tau 1 -> 2 over 512) as a model serves it: its 4096-token
+    prompt ingested 32 tokens per launch over all layers (every prompt key is
+    known at once), then its 512 decode tokens one launch per token.  The
+    decode is timed in three forms from the same state after the prompt (the
+    state is saved and restored between them): all 32 layers per launch
+    through kve_step_ws (8192 caches; long moves handed to the move kernel;
+    the eviction step run once per token after the forward pass has made every
+    layer's new key), one kve_step_ws launch per layer, and one in-place
+    keyformer_step launch per layer.  All three must evict the same rows.
+    Decode inputs are resident in HBM before each timed region; HIP events on
+    the launch stream bracket it.  Bytes follow the Keyformer byte model with
+    each cache-step's moved rows taken from the kernel's evicted output."""
+    import numpy as np
+    import torch
+    import synth
+    import kv_cache_eviction_step_amd as kve
+    w = synth.WORKLOADS[3]
+    L, bh, d, B, T = w.layers, w.bh, w.d, w.budget, w.decode
+    S = 32
+    names = ("k", "v", "scores", "gumbel", "positions")
+    layers = [kve.Layer.empty(bh, B + 1, d, dev, gumbel=True) for _ in range(L)]
+    batch = kve.LayerBatch(layers, [B] * L)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(3031)
+    stream = torch.cuda.current_stream(dev)
+    kargs = (w.n_sink, w.tau_init, w.tau_end, w.anneal_steps, w.rope_base, w.gumbel_seed)
+
+    # ---- prompt: S tokens per launch over all layers ----------------------------
+    G = 512                                            # tokens generated at a time
+    pk = torch.empty((L, G, bh, d), dtype=torch.float16, device=dev)
+    pv = torch.empty_like(pk)
+    pev = torch.empty((L, S, bh), dtype=torch.int32, device=dev)
+    marks, m_sum, p_bytes = [], torch.zeros((), dtype=torch.int64, device=dev), 0
+    for g0 in range(0, w.prompt, G):
+        for l in range(L):
+            synth.bulk_kv_torch(w, g0, G, bh, gen, dev, out_k=pk[l], out_v=pv[l])
+        for s0 in range(0, G, S):
+            t0 = g0 + s0
+            n_prev = torch.minimum(torch.arange(t0, t0 + S, device=dev), torch.tensor(B, device=dev))
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            kve.keyformer_step_layers_tokens(batch, pk[:, s0:s0 + S], pv[:, s0:s0 + S], *kargs,
+                                             pev, n_tokens=S)
+            b.record(stream)
+            marks.append((a, b))
+            e = pev.to(torch.int64)
+            npr = n_prev[None, :, None]
+            m_sum += torch.where((e >= 0) & (e < npr), npr - e, 0).sum()
+            for t in range(t0, t0 + S):
+                n = min(t, B)
+                p_bytes += L * bh * int(step_bytes("keyformer", n, d, 0, over=n + 1 > B))
+    torch.cuda.synchronize()
+    p_ms = sum(x.elapsed_time(y) for x, y in marks)
+    p_bytes += int(m_sum) * (8 * d + 24)
+    del pk, pv, pev
+    prompt = {
+        "tokens": w.prompt, "tokens_per_launch": S,
+        "launch": "keyformer_step_layers_tokens, all 32 layers x 32 tokens per launch",
+        "seconds": p_ms / 1e3, "value": bh * L * w.prompt / (p_ms / 1e3),
+        "achieved_GBs": p_bytes / (p_ms / 1e3) / 1e9,
+        "frac": p_bytes / (p_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+        "note": "prompt ingestion: each launch re-reads its caches' keys for 32 tokens, "
+                "mostly from the last-level cache, so this rate is not an HBM rate",
+    }
+
+    # ---- decode: three launch forms from one saved state -------------------------
+    dk = torch.empty((L, T, bh, d), dtype=torch.float16, device=dev)
+    dv = torch.empty_like(dk)
+    for l in range(L):
+        synth.bulk_kv_torch(w, w.prompt, T, bh, gen, dev, out_k=dk[l], out_v=dv[l])
+    snap = [[getattr(x, nm).clone() for nm in names] for x in layers]
+    ctr0 = [batch.ctrs[l].copy() for l in range(L)]
+    pol = kve.policy("keyformer", w.n_sink, 0, w.tau_init, w.tau_end, w.anneal_steps,
+                     w.rope_base, w.gumbel_seed)
+    ws_all = kve.workspace(L * bh, B, d, dev)
+    ws_one = kve.workspace(bh, B, d, dev)
+    singles = [kve.LayerBatch([layers[l]], [B]) for l in range(L)]
+    cls = [x.c_struct() for x in layers]
+    views = [[(dk[l, t], dv[l, t]) for t in range(T)] for l in range(L)]
+
+    def restore():
+        for x, sn in zip(layers, snap):
+            for nm, t in zip(names, sn):
+                getattr(x, nm).copy_(t)
+        for l in range(L):
+            batch.ctrs[l] = ctr0[l].copy()
+            singles[l].ctrs[0] = ctr0[l].copy()
+        torch.cuda.synchronize()
+
+    host = {}
+
+    def timed(run_token, key):
+        ev = torch.full((T, L, bh), -9, dtype=torch.int32, device=dev)
+        evl = [[ev[t, l] for l in range(L)] for t in range(T)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        h0 = time.perf_counter()
+        for t in range(T):
+            run_token(t, ev[t], evl[t])
+        host[key] = time.perf_counter() - h0          # enqueueing, as seen by the host
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1), ev
+
+    def all_layers(t, e, _el):
+        kve.step(batch, dk[:, t], dv[:, t], pol, e, workspace=ws_all)
+
+    def per_layer_ws(t, _e, el):
+        for l in range(L):
+            k, v = views[l][t]
+            kve.step(singles[l], [k], [v], pol, [el[l]], workspace=ws_one)
+
+    def per_layer_in_place(t, _e, el):
+        for l in range(L):
+            k, v = views[l][t]
+            kve.keyformer_step(layers[l], k, v, singles[l].ctrs[0], B, *kargs, el[l],
+                               c_layer=cls[l])
+
+    ms_all, ev_all = timed(all_layers, "all")
+    restore()
+    ms_ws, ev_ws = timed(per_layer_ws, "ws")
+    restore()
+    ms_ip, ev_ip = timed(per_layer_in_place, "ip")
+    same = bool(torch.equal(ev_all, ev_ws)) and bool(torch.equal(ev_all, ev_ip))
+    e = ev_all.to(torch.int64)
+    m = torch.where((e >= 0) & (e < B), B - e, 0)
+    d_bytes = T * L * bh * int(step_bytes("keyformer", B, d, 0)) + int(m.sum()) * (8 * d + 24)
+    mean_m = float(m.double().mean())
+
+    def form(ms, launches, launch, key):
+        sec = ms / 1e3
+        ach = d_bytes / sec / 1e9
+        return {"launch": launch, "value": bh * L * T / sec, "unit": "cache-row updates/s",
+                "ms_per_token": ms / T, "avg_launch_us": ms * 1e3 / launches,
+                "host_us_per_launch": host[key] * 1e6 / launches,
+                "achieved_GBs": ach, "frac": ach / PEAK_HBM_GBS}
+
+    dec = form(ms_all, T, "one kve_step_ws launch per token over all 32 layers (8192 caches)",
+               "all")
+    traffic = measured_traffic(w.name, "step_layers_kernel", "all-layers_x1tok")
+    dec["roofline"] = {
+        "bound": "hbm", "achieved": dec["achieved_GBs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+        "frac": dec["frac"], "traffic": traffic,
+        "kernel": "kve::step_layers_kernel + kve::move_kernel",
+        "avg_launch_us": dec["avg_launch_us"], "algorithmic_bytes_per_launch": d_bytes / T,
+    }
+    return {
+        "workload": (f"{w.name}: B={w.batch} layers={L} kv_heads={w.kv_heads} D={d} keyformer "
+                     f"budget={B} n_sink={w.n_sink} tau {w.tau_init}->{w.tau_end} over "
+                     f"{w.anneal_steps}"),
+        "prompt": prompt,
+        "decode": {"tokens": T, "mean_rows_moved_per_cache_step": mean_m, **dec},
+        "decode_per_layer": form(ms_ws, T * L, "one kve_step_ws launch per layer per token "
+                                 "(256 caches; long moves handed to the move kernel)", "ws"),
+        "decode_per_layer_in_place": form(ms_ip, T * L, "one keyformer_step launch per layer "
+                                          "per token (every cache compacts in place)", "ip"),
+        "evictions_identical_across_forms": same,
+        "timing": "HIP events around the 512 decode tokens of each form, inputs resident",
     }
 
 

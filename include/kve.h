@@ -306,11 +306,15 @@ int kve_step(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
  *   workspace_bytes  its size
  *   other arguments  as kve_step
  * Contract: the workspace must be all zero bytes before its first use (for
- * example torch.zeros); every call returns it to that state once its work
- * on `stream` has finished, so nothing needs clearing between calls.  Calls
- * that use one workspace must be ordered (the same stream, or events):
- * overlapping calls race.  After a KVE_ELAUNCH the layers' tensors and the
- * workspace are undefined: zero the workspace before using it again.
+ * example torch.zeros).  Its first 16 bytes then hold two reservation
+ * counters and a phase that the calls keep consistent: each call reserves on
+ * the counter of the current phase, and its second kernel zeroes the other
+ * counter and advances the phase, so every call leaves the workspace ready
+ * for the next one and nothing needs clearing between calls (graph replays
+ * included).  Calls that use one workspace must be ordered (the same stream,
+ * or events): overlapping calls race.  After a KVE_ELAUNCH the layers'
+ * tensors and the workspace are undefined: zero the workspace before using
+ * it again.
  * Returns as kve_step; KVE_EINVAL also for a misaligned workspace or one
  * too small to hold a single item.
  */
@@ -324,8 +328,8 @@ int kve_step_ws(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
  * every long move of a single-token launch over `caches` caches (the sum of
  * bh over its layers) whose budgets are at most max_budget, at head
  * dimension d: one 32-byte item and one parked 4*d-byte row per 64-row chunk
- * of each cache's longest possible move (max_budget - 1 rows), plus 256
- * bytes of counters, each part 256-byte aligned.  Returns -1 for caches < 1,
+ * of each cache's longest possible move (max_budget - 1 rows), plus a
+ * 256-byte header (counters and phase), each part 256-byte aligned.  Returns -1 for caches < 1,
  * max_budget outside 1 .. 12288, d not 64 or 128, or a size past 2^30 items.
  * Pure host arithmetic; needs no device.
  */

@@ -564,8 +564,8 @@ def workspace_size(caches: int, max_budget: int, d: int) -> int:
 
 def workspace(caches: int, max_budget: int, d: int, device) -> "torch.Tensor":
     """A zeroed device workspace of workspace_size(caches, max_budget, d) bytes
-    for step(..., workspace=...).  Calls return it to zero when their work is
-    done; reuse it for every call on one stream."""
+    for step(..., workspace=...).  Each call leaves it ready for the next;
+    reuse it for every call on one stream."""
     n = workspace_size(caches, max_budget, d)
     t = torch.zeros(n + 256, dtype=torch.uint8, device=device)
     off = (-t.data_ptr()) % 256                   # the library wants 256-byte alignment

@@ -78,4 +78,23 @@ KVE_HD inline bool reservation_fits(int base, int chunks, int cap) {
 // pool's end.
 KVE_HD inline int items_queued(int reserved, int cap) { return reserved < cap ? reserved : cap; }
 
+// The pool's header: 32-bit words that the calls keep consistent among
+// themselves (all zero before the first call):
+//   kPoolCount + 0, + 1   reservation counters of even and odd phases
+//   kPoolPhase            phase of the next call
+//   kPoolLaunchPhase      phase the last step launch used (on a cache line of
+//                         its own, written with ordinary stores, apart from
+//                         the words that atomics update)
+// A step launch reads the phase p, reserves on counter pool_counter(p) --
+// zero at that point -- and records p for the move kernel.  The move kernel
+// reads p and counter pool_counter(p); its workgroup 0 zeroes the other
+// counter, which no one reads until the next call, and sets the phase to
+// p + 1.  So no counter is contended by the move kernel's workgroups, and
+// each call starts with its counter at zero without any clearing by the host.
+constexpr int kPoolCount = 0;
+constexpr int kPoolPhase = 2;
+constexpr int kPoolLaunchPhase = 32;          // byte 128 of the 256-byte header
+KVE_HD inline int pool_counter(int phase) { return kPoolCount + (phase & 1); }
+KVE_HD inline int pool_next_phase(int phase) { return (phase + 1) & 0x3fffffff; }
+
 }  // namespace kve

@@ -48,11 +48,11 @@ struct MoveItem {
 // its final slot), row j >= 1 row e + j*kMoveChunk as it was before the move
 // (the first destination of chunk j, read by chunk j-1).  A reservation that
 // does not fit in `cap` items compacts in place instead.  The move kernel
-// works through the items and its last workgroup zeroes both counters, so
-// the workspace is back to zero when the call's work is done: no state is
-// kept between calls, on the host or the device.
+// works through the items; the header's counters and phase (the move plan)
+// leave the next call's counter at zero, so nothing is cleared between
+// calls and no host state is kept.
 struct MovePool {
-  int32_t *count;          // [2]: items reserved; move-kernel workgroups finished
+  int32_t *count;          // header words: counters, phase, launch phase (the move plan)
   MoveItem *items;         // [cap]; null pointer: every step compacts its own cache
   void *rows;              // fp16 [cap][2][d]: parked key then value of each item
   int32_t cap;             // items (and parked rows) the workspace holds

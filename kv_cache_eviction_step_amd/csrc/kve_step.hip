@@ -420,6 +420,11 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   // end of the step): loaded now, so that no load is left for the step's end.
   u32x4 v_new = {};
   if (tid < V16) v_new = global(reinterpret_cast<const u32x4 *>(la.new_v))[(size_t)hh * V16 + tid];
+  // With a workspace: its phase, written by the previous call's move kernel
+  // and by nothing during this launch; loaded now (an ordinary load: the
+  // workgroups of a compute die share one fetch of it), used only in phase D.
+  int pool_phase_in = 0;
+  if (!PRE && sa.pool.items != nullptr) pool_phase_in = global(sa.pool.count)[kPoolPhase];
   const float scale = sa.scale;
   float mx = -INFINITY;
   const int iters = (n + ROWS_IT - 1) / ROWS_IT;
@@ -610,6 +615,8 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   }
   if (tid == 0 && la.evicted) global(la.evicted)[hh] = e;
 
+  const int pool_phase = __builtin_amdgcn_readfirstlane(pool_phase_in);
+
   // ---- D: write-back ----------------------------------------------------------
   const gptr<int32_t> __restrict__ positions = global(la.positions);
 #pragma unroll
@@ -640,6 +647,8 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   // pool marks its items empty and compacts in place.
   bool defer = !PRE && sa.pool.items != nullptr && move_handed_over(e, n);
   gptr<u32x4> slot = nullptr;                   // this move's parked rows
+  if (!PRE && sa.pool.items != nullptr && blockIdx.x == 0 && tid == 0)
+    global(sa.pool.count)[kPoolLaunchPhase] = pool_phase;     // the launch's phase
   if (defer) {
     __shared__ int item_base;
     constexpr int PIECES_EARLY = 2;             // parked 16-byte pieces loaded per thread
@@ -654,7 +663,7 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
 #pragma unroll
     for (int u = 0; u < PIECES_EARLY; ++u)
       if (tid + u * NT < pieces) pk[u] = parked_piece(tid + u * NT);
-    if (tid == 0) item_base = atomicAdd(sa.pool.count, chunks);
+    if (tid == 0) item_base = atomicAdd(sa.pool.count + pool_counter(pool_phase), chunks);
     __syncthreads();                            // item_base
     const int base = __builtin_amdgcn_readfirstlane(item_base);
     MoveItem *const items = sa.pool.items;
@@ -936,9 +945,10 @@ __global__ __launch_bounds__(NT) void step_layers_kernel(LayerPack pack, int n_l
 // destination, which comes from the parked copy.  So no two chunks touch the
 // same row, and each chunk reads everything before it writes.  The last
 // chunk then writes the incoming row at n-1.  The grid strides over the
-// queued items; when every workgroup has passed its last item the last one
-// to finish zeroes the pool's two counters, so the next launch finds them at
-// zero without any clearing on the host.
+// queued items.  Workgroup 0 also prepares the pool for the next call: it
+// zeroes the counter that call will reserve on and advances the phase (the
+// move plan's header protocol), so the next launch finds its counter at zero
+// without any clearing on the host.
 template <int D>
 __global__ __launch_bounds__(256) void move_kernel(MovePool pool, RopeTable back1) {
   constexpr int NT = 256;
@@ -947,8 +957,16 @@ __global__ __launch_bounds__(256) void move_kernel(MovePool pool, RopeTable back
   constexpr int RPM = NT / LPM;                 // rows per sweep
   constexpr int SW = kMoveChunk / RPM;          // sweeps per chunk
   static_assert(SW * RPM == kMoveChunk, "move chunk");
-  const int reserved = __hip_atomic_load(pool.count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // Ordinary loads: both words were last written before this launch began
+  // (the counter by the step's atomics, the phase by its workgroup 0), and
+  // workgroup 0's updates below change neither of them.
+  const int phase = global(pool.count)[kPoolLaunchPhase];
+  const int reserved = global(pool.count)[pool_counter(phase)];
   const int queued = items_queued(reserved, pool.cap);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {    // the next call's counter, then its phase
+    atomicExch(pool.count + pool_counter(pool_next_phase(phase)), 0);
+    atomicExch(pool.count + kPoolPhase, pool_next_phase(phase));
+  }
   const int tid = threadIdx.x, lm = tid % LPM, rm = tid / LPM;
   float cs[8], sn[8];
 #pragma unroll
@@ -1015,16 +1033,6 @@ __global__ __launch_bounds__(256) void move_kernel(MovePool pool, RopeTable back
         K[o + tid] = x;
       else
         V[o + tid - V16] = x;
-    }
-  }
-  // Every thread of this workgroup has read the count (it bounds the loop
-  // above); the workgroup that finishes last knows that every other one has.
-  __syncthreads();
-  if (tid == 0) {
-    const int done = atomicAdd(pool.count + 1, 1);
-    if (done == (int)gridDim.x - 1) {
-      atomicExch(pool.count, 0);
-      atomicExch(pool.count + 1, 0);
     }
   }
 }

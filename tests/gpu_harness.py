@@ -124,6 +124,14 @@ def bulk_state(layer, n: int, w: synth.Workload, gen) -> None:
                            gen)
 
 
+def workspace_ready(ws) -> bool:
+    """A kve_step_ws workspace left ready for the next call: its header's
+    first words are the two reservation counters and the phase of the next
+    call; the counter of the next call's phase is zero."""
+    h = ws[:16].view(torch.int32).cpu().tolist()
+    return h[h[2] & 1] == 0 and h[2] >= 0
+
+
 def ulp16(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     def ordered(x):
         x = x.astype(np.int32)
@@ -232,7 +240,7 @@ def run_layer(w: synth.Workload, layer_idx: int, budget: int, T: int, samples: l
             kve.step(batch, [nk[t]], [nv[t]], pol, [ev[t]], workspace=ws)
         torch.cuda.synchronize(device)
         if ws is not None:
-            assert not bool(ws[:8].any()), "workspace counters not back to zero"
+            assert workspace_ready(ws), "workspace not ready for the next call"
         return L, ev.cpu().numpy(), batch.ctrs[0]
     cl = L.c_struct()
     for t in range(T):
@@ -315,6 +323,6 @@ def run_batched(w: synth.Workload, layer_ids, budgets, T: int, samples: dict, in
                 kve.pyramid_step_layers(batch, nk[t], nv[t], w.n_sink, w.rope_base, ev[t])
     torch.cuda.synchronize(device)
     if ws is not None:
-        assert not bool(ws[:8].any()), "workspace counters not back to zero"
+        assert workspace_ready(ws), "workspace not ready for the next call"
     _ = layer_ids
     return layers, ev.cpu().numpy(), batch

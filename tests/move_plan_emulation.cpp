@@ -18,6 +18,8 @@
 // move kernel reads was written by this launch (an item or an empty mark),
 // and every cache -- handed over or compacted in place -- ends shifted.
 //
+// Part 3: the pool header (counters and phase) over many calls.
+//
 // Exit status 0 and a summary line on success; a message and status 1 on the
 // first violation.
 #include <algorithm>
@@ -256,11 +258,58 @@ static long part2(std::mt19937 &rng) {
   return launches;
 }
 
+// Part 3: the pool header across a long sequence of calls.  Calls that hand
+// nothing over launch no move kernel and leave the header alone.  In a call
+// that does, every step workgroup records the phase it read and some reserve;
+// the move kernel's workgroup 0 prepares the next call at a random moment
+// among the other workgroups' reads.  Checked: every call starts on a zero
+// counter, and every move workgroup reads exactly this call's reservations.
+static long part3(std::mt19937 &rng) {
+  int h[64] = {0};                                // the 256-byte header, zeroed before use
+  // the launch phase, written with ordinary stores, shares no 128-byte line
+  // with the words that atomics update
+  if (kPoolLaunchPhase * 4 < 128 || kPoolLaunchPhase * 4 >= 256 || kPoolPhase * 4 >= 128 ||
+      pool_counter(0) * 4 >= 128 || pool_counter(1) * 4 >= 128)
+    fail("header layout", kPoolLaunchPhase, kPoolPhase);
+  long calls = 0;
+  for (int call = 0; call < 50000; ++call) {
+    if (rng() % 4 == 0) continue;                 // nothing handed over
+    const int p = h[kPoolPhase];
+    if (h[pool_counter(p)] != 0) fail("a call starts on a counter that is not zero", p, call);
+    const int wgs = 1 + (int)(rng() % 64);
+    int reserved = 0;
+    for (int b = 0; b < wgs; ++b) {
+      h[kPoolLaunchPhase] = h[kPoolPhase];
+      if (rng() % 3 == 0) {
+        const int c = 2 + (int)(rng() % 190);
+        h[pool_counter(h[kPoolPhase])] += c;
+        reserved += c;
+      }
+    }
+    const int grid = 1 + (int)(rng() % 1024);
+    const int wg0_at = (int)(rng() % grid);
+    for (int g = 0; g < grid; ++g) {
+      if (g == wg0_at) {                          // workgroup 0's update
+        const int mp = h[kPoolLaunchPhase];
+        h[pool_counter(pool_next_phase(mp))] = 0;
+        h[kPoolPhase] = pool_next_phase(mp);
+      }
+      const int lp = h[kPoolLaunchPhase];
+      if (lp != p || h[pool_counter(lp)] != reserved)
+        fail("a move workgroup reads another call's count", lp, call);
+    }
+    ++calls;
+  }
+  return calls;
+}
+
 int main() {
   std::mt19937 rng(20241202u);
   const long moves = part1(rng);
   const long launches = part2(rng);
-  std::printf("ok: %ld handed-over moves, %ld pooled launches (chunk %d rows, handed over past "
-              "%d rows)\n", moves, launches, kMoveChunk, kDeferRows);
+  const long calls = part3(rng);
+  std::printf("ok: %ld handed-over moves, %ld pooled launches, %ld calls through one header "
+              "(chunk %d rows, handed over past %d rows)\n", moves, launches, calls, kMoveChunk,
+              kDeferRows);
   return 0;
 }

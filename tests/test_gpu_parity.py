@@ -17,7 +17,7 @@ import synth
 from gpu_harness import (Sample, compare_cache, load_state_into, oracle_samples,
                          oracle_samples_layers, policy_for,
                          random_state,
-                         run_batched, run_layer)
+                         run_batched, run_layer, workspace_ready)
 from oracle.guard import guarded_trajectory, params_for
 
 pytestmark = pytest.mark.gpu
@@ -964,7 +964,7 @@ def _layers_tokens_equal_single_calls(dev, kind, shapes, T, S, seed, d=128, ws=F
             kve.pyramid_step_layers_tokens(batch, ks, vs, *args, es)
     torch.cuda.synchronize()
     if ws:
-        assert not bool(wsb[:8].any())                 # the counters are back to zero
+        assert workspace_ready(wsb)                     # ready for the next call
     for l in range(len(shapes)):
         assert torch.equal(evas[l], evbs[l]), l
         n = budgets[l]
@@ -1080,7 +1080,7 @@ def test_launch_size_paths_agree(dev, kind, budget, S, d):
         run(parts[i], nk[:, sl].contiguous(), nv[:, sl].contiguous(), ev_p[i],
             kve.Counters(budget, pos0, pos0))
     torch.cuda.synchronize()
-    assert not bool(wsa[:8].any())
+    assert workspace_ready(wsa)
     assert torch.equal(ev_a, torch.cat(ev_p, dim=1))
     for name in ("k", "v", "scores", "positions") + (("gumbel",) if kf else ()):
         joined = torch.cat([getattr(p, name) for p in parts])
@@ -1123,7 +1123,7 @@ def test_tova_handoff_equals_own_moves(dev, recent):
             sl = slice(i * half, (i + 1) * half)
             kve.step(bp[i], [nk[t, sl].contiguous()], [nv[t, sl].contiguous()], pol, [ev_p[i][t]])
     torch.cuda.synchronize()
-    assert not bool(ws[:8].any())
+    assert workspace_ready(ws)
     assert torch.equal(ev_a, torch.cat(ev_p, dim=1))
     for name in ("k", "v", "scores", "positions"):
         joined = torch.cat([getattr(p, name) for p in parts])
@@ -1179,7 +1179,7 @@ def test_handoff_edges_against_oracle(dev, d):
     kve.step(batch, [nk], [nv], policy_for(w), [ev], workspace=ws)
     torch.cuda.synchronize()
     ctr = batch.ctrs[0]
-    assert not bool(ws[:8].any())
+    assert workspace_ready(ws)
     evn = ev.cpu().numpy()
     _assert_parity(L, evn[None, :], samples, next_pos)
     assert ((evn >= 0) & (evn <= n)).all()
@@ -1225,7 +1225,7 @@ def test_handoff_largest_budget_against_oracle(dev):
     kve.step(batch, [nk], [nv], policy_for(w), [ev], workspace=ws)
     torch.cuda.synchronize()
     ctr = batch.ctrs[0]
-    assert not bool(ws[:8].any())
+    assert workspace_ready(ws)
     evn = ev.cpu().numpy()
     _assert_parity(L, evn[None, :], samples, next_pos)
     assert ((evn >= 0) & (evn <= n)).all()
@@ -1265,7 +1265,7 @@ def test_batched_handoff_mixed_budgets_equals_own_moves(dev):
         for i in range(2):
             kve.step(bb[i], [nk[i, t]], [nv[i, t]], pol, [ev_b[i, t]])
     torch.cuda.synchronize()
-    assert not bool(ws[:8].any())
+    assert workspace_ready(ws)
     assert torch.equal(ev_a, ev_b)
     for i, b in enumerate(budgets):
         for name in ("k", "v", "scores", "positions"):
@@ -1276,10 +1276,10 @@ def test_batched_handoff_mixed_budgets_equals_own_moves(dev):
 def test_captured_step_replays_match_eager(dev):
     """A Keyformer kve_step_ws call on 320 caches, which hands its long moves
     to the move kernel through the workspace, captured into a graph: the
-    workspace's counters return to zero inside the captured work, so each
-    replay, from the same restored state and with eager work and a
-    synchronisation between replays, gives the eager call's bits (and the
-    in-place keyformer_step's)."""
+    captured work itself leaves the workspace ready for the next call (its
+    header advances a phase per call), so each replay, from the same restored
+    state and with eager work and a synchronisation between replays, gives
+    the eager call's bits (and the in-place keyformer_step's)."""
     import kv_cache_eviction_step_amd as kve
     from gpu_harness import bulk_state
     bh, d, budget, pos0 = 320, 128, 1000, 6000
@@ -1310,7 +1310,7 @@ def test_captured_step_replays_match_eager(dev):
     call(E, ev_e, ws)
     torch.cuda.synchronize()
     assert int((budget - ev_e)[ev_e >= 0].max()) > 128   # some move was handed over
-    assert not bool(ws[:8].any())                      # the counters are back to zero
+    assert workspace_ready(ws)                          # ready for the next call
     assert torch.equal(ev_e, ev_p)
     for x in names:
         assert torch.equal(getattr(E, x)[:, :budget], getattr(P, x)[:, :budget]), x
@@ -1327,7 +1327,7 @@ def test_captured_step_replays_match_eager(dev):
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        assert not bool(ws[:8].any()), replay
+        assert workspace_ready(ws), replay
         assert torch.equal(ev_g, ev_e), replay
         for x in names:
             assert torch.equal(getattr(G, x)[:, :budget], getattr(E, x)[:, :budget]), (replay, x)
@@ -1338,7 +1338,7 @@ def test_workspace_too_small_falls_back_in_place(dev, items):
     """kve_step_ws with a workspace of only 1, 3 or 12 items on 320 Keyformer
     caches of 1000 rows: caches whose reservation does not fit compact in
     place, the rest hand their moves over; every call equals the in-place
-    keyformer_step bit for bit, and the counters return to zero."""
+    keyformer_step bit for bit, and the workspace stays ready for the next."""
     import kv_cache_eviction_step_amd as kve
     from gpu_harness import bulk_state
     bh, d, budget, pos0, T = 320, 128, 1000, 6000, 12
@@ -1364,7 +1364,7 @@ def test_workspace_too_small_falls_back_in_place(dev, items):
         kve.step(ba, [nk[t]], [nv[t]], pol, [ev_a[t]], workspace=ws)
         kve.keyformer_step(B, nk[t], nv[t], cb, budget, 4, 1.0, 2.0, 64, 1e4, 5, ev_b[t])
     torch.cuda.synchronize()
-    assert not bool(ws[:8].any())
+    assert workspace_ready(ws)
     assert torch.equal(ev_a, ev_b)
     for x in names:
         assert torch.equal(getattr(A, x)[:, :budget], getattr(B, x)[:, :budget]), x

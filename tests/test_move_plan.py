@@ -6,11 +6,13 @@ its sources, whether a pool reservation fits, how many items the move kernel
 reads -- from kv_cache_eviction_step_amd/csrc/kve_move_plan.h.
 ``move_plan_emulation.cpp`` compiles that same header with g++ and runs the
 protocol on the host: chunks in random orders and interleavings, many
-caches sharing pools from one item to more than enough.  It checks that no
-chunk reads a row another chunk writes, that every index stays in bounds,
-that the move kernel reads only items this launch wrote, and that every cache
-ends as keyformer_update step 3 leaves it (later rows one slot down, the
-incoming row last).
+caches sharing pools from one item to more than enough, and the pool's
+header over tens of thousands of calls.  It checks that no chunk reads a row
+another chunk writes, that every index stays in bounds, that the move kernel
+reads only items this launch wrote, that every call starts on a zero counter
+and every move workgroup reads that call's count, and that every cache ends
+as keyformer_update step 3 leaves it (later rows one slot down, the incoming
+row last).
 """
 from __future__ import annotations
 
@@ -27,7 +29,8 @@ def test_kernels_take_the_move_plan_from_the_shared_header():
     header's functions rather than restating its arithmetic."""
     src = open(os.path.join(CSRC, "kve_step.hip")).read()
     for fn in ("move_handed_over", "move_chunks", "parked_row", "chunk_first_dst",
-               "move_last_dst", "chunk_source_row", "reservation_fits", "items_queued"):
+               "move_last_dst", "chunk_source_row", "reservation_fits", "items_queued",
+               "pool_counter", "pool_next_phase"):
         assert re.search(rf"\b{fn}\(", src), fn
     assert '#include "kve_move_plan.h"' in open(os.path.join(CSRC, "kve_step.h")).read()
     api = open(os.path.join(CSRC, "kve_api.hip")).read()
@@ -41,5 +44,6 @@ def test_move_protocol_emulation(tmp_path):
                     os.path.join(HERE, "move_plan_emulation.cpp"), "-o", exe], check=True)
     r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
-    m = re.search(r"ok: (\d+) handed-over moves, (\d+) pooled launches", r.stdout)
-    assert m and int(m.group(1)) > 10_000 and int(m.group(2)) > 50, r.stdout
+    m = re.search(r"ok: (\d+) handed-over moves, (\d+) pooled launches, (\d+) calls", r.stdout)
+    assert m and int(m.group(1)) > 10_000 and int(m.group(2)) > 50 and int(m.group(3)) > 10_000, \
+        r.stdout

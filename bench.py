@@ -54,6 +54,9 @@ def parse():
                     help="protect the last R rows from eviction (kve_step)")
     ap.add_argument("--tova", action="store_true",
                     help="TOVA-adapted scoring (current-step weight; kve_step)")
+    ap.add_argument("--fill-tokens-per-call", type=int, default=0,
+                    help="with --fill real: tokens per launch of the prompt (default: "
+                         "--tokens-per-call), e.g. 32 to ingest the prompt as a model would")
     ap.add_argument("--workspace", action="store_true",
                     help="single-token launches through kve_step_ws with a workspace sized for "
                          "every move (long compactions handed to the move kernel)")
@@ -77,7 +80,8 @@ def parse():
 
 
 KERNEL_SOURCES = ["kv_cache_eviction_step_amd/csrc/kve_step.hip",
-                  "kv_cache_eviction_step_amd/csrc/kve_step.h"]
+                  "kv_cache_eviction_step_amd/csrc/kve_step.h",
+                  "kv_cache_eviction_step_amd/csrc/kve_move_plan.h"]
 
 
 def kernel_source_hash() -> str:
@@ -95,8 +99,9 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def launch_mode(batched: bool, tokens_per_call: int) -> str:
-    return ("all-layers" if batched else "per-layer") + f"_x{tokens_per_call}tok"
+def launch_mode(batched: bool, tokens_per_call: int, workspace: bool = False) -> str:
+    return (("all-layers" if batched else "per-layer") + f"_x{tokens_per_call}tok" +
+            ("_ws" if workspace and tokens_per_call == 1 else ""))
 
 
 def measured_traffic(workload: str, kernel: str, mode: str):
@@ -366,16 +371,18 @@ def main():
             synth.bulk_state_torch(x.k, x.v, x.scores, x.gumbel, x.positions, budgets[l], w, gen)
             set_counters(l, kve.Counters(budgets[l], pos0, pos0))
     else:
-        # the prompt through the same calls as the timed steps
-        chunk = 64 * TPC if TPC > 1 else 64
+        # the prompt through the same calls as the timed steps (or as many
+        # tokens per launch as --fill-tokens-per-call asks)
+        FT = args.fill_tokens_per_call or TPC
+        chunk = 64 * FT if FT > 1 else 64
         for t0 in range(0, w.prompt, chunk):
             cnt = min(chunk, w.prompt - t0)
             ins_k = torch.empty((L, cnt, bh, d), dtype=torch.float16, device=dev)
             ins_v = torch.empty_like(ins_k)
             for l in range(L):
                 ins_k[l], ins_v[l] = synth.bulk_kv_torch(w, t0, cnt, bh, gen, dev)
-            for s0 in range(0, cnt, TPC):
-                call(ins_k, ins_v, s0, min(TPC, cnt - s0))
+            for s0 in range(0, cnt, FT):
+                call(ins_k, ins_v, s0, min(FT, cnt - s0))
     torch.cuda.synchronize()
     t_fill = time.time() - t_fill
 
@@ -423,7 +430,7 @@ def main():
     mean_m = float(np.where(evn >= 0, np.maximum(0, n_prev[:, :, None] - evn), 0).mean())
 
     kernel = "step_layers_kernel" if batch is not None or TPC > 1 else "step_kernel"
-    traffic = measured_traffic(w.name, kernel, launch_mode(args.batched, TPC))
+    traffic = measured_traffic(w.name, kernel, launch_mode(args.batched, TPC, args.workspace))
     out = result_line(args, w, budgets, bh, L, d, TPC, batch, entry, args.steps, args.warmup,
                       ms, launches, total_bytes, mean_m, traffic, kernel)
     out["config"]["steady_state_fill"] = args.fill
@@ -647,7 +654,7 @@ def late_riser_decode(dev) -> dict:
 
     dec = form(ms_all, T, "one kve_step_ws launch per token over all 32 layers (8192 caches)",
                "all")
-    traffic = measured_traffic(w.name, "step_layers_kernel", "all-layers_x1tok")
+    traffic = measured_traffic(w.name, "step_layers_kernel", "all-layers_x1tok_ws")
     dec["roofline"] = {
         "bound": "hbm", "achieved": dec["achieved_GBs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
         "frac": dec["frac"], "traffic": traffic,

@@ -57,6 +57,7 @@ extern "C" {
 #define KVE_EINVAL   -1   /* an argument failed a host-side check            */
 #define KVE_ELAUNCH  -2   /* the HIP runtime rejected the kernel launch       */
 #define KVE_ENODEV   -3   /* no HIP device, or no gfx950 code for the current one */
+#define KVE_ENOSPACE -4   /* kve_step_noalloc: more scratch needed than its buffer holds */
 
 /* One layer's B*H caches.  Rows of a cache are contiguous, caches follow
  * each other:  element (hh, row, j) of k lives at k[(hh*cap + row)*d + j].
@@ -334,6 +335,33 @@ int kve_step_ws(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
  * Pure host arithmetic; needs no device.
  */
 int64_t kve_workspace_size(int64_t caches, int32_t max_budget, int32_t d);
+
+/*
+ * kve_step_noalloc -- for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid
+ * allocation): kve_step_ws with the workspace in a fixed array of
+ * KVE_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on,
+ * from its load until the process ends.  The call allocates nothing.
+ *
+ * Arguments, results and errors as kve_step_ws without the workspace; the
+ * results are the same bits.  A call that would hand moves over (one token,
+ * at least 256 caches, Keyformer noise, TOVA scoring or a window of more
+ * than 128 rows) needs kve_workspace_size(sum of bh, largest budget, d)
+ * bytes; if that exceeds KVE_NOALLOC_SCRATCH_BYTES it returns KVE_ENOSPACE
+ * before anything is enqueued (use kve_step_ws with a workspace of that size
+ * instead).  Other calls need no scratch and run as kve_step.  Each call that
+ * uses the array first clears its header with a small kernel on `stream`.
+ * All calls on one GPU share its array: calls that overlap on one GPU (on
+ * different streams or host threads, without ordering) race.  The device
+ * address of the array is looked up once per device, on the first call that
+ * needs it.
+ */
+#define KVE_NOALLOC_SCRATCH_BYTES (16 << 20)
+
+int kve_step_noalloc(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
+                     const void *const *new_k, const void *const *new_v, kve_counters *ctrs,
+                     const int32_t *budgets, const kve_policy *policy, int32_t *const *evicted,
+                     void *stream);
 
 /*
  * pyramid_budgets -- per-layer budgets ("The budget schedule"): a linear taper

@@ -20,6 +20,7 @@ Calls (same names as the C ABI):
                         evicted=None, stream=None)
     step(batch, new_k, new_v, policy, evicted=None, stream=None, n_tokens=None,
          workspace=None)                     (kve_step / kve_step_ws)
+    step_noalloc(batch, new_k, new_v, policy, evicted=None, stream=None, n_tokens=None)
     workspace_size(caches, max_budget, d), workspace(caches, max_budget, d, device)
     pyramid_budgets(n_layers, avg_budget, n_sink, beta) -> list[int]
 """
@@ -35,7 +36,8 @@ import torch  # noqa: F401  (loads torch's HIP runtime first; libkve binds to it
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkve.so")
 
-KVE_OK, KVE_EINVAL, KVE_ELAUNCH, KVE_ENODEV = 0, -1, -2, -3
+KVE_OK, KVE_EINVAL, KVE_ELAUNCH, KVE_ENODEV, KVE_ENOSPACE = 0, -1, -2, -3, -4
+NOALLOC_SCRATCH_BYTES = 16 << 20       # KVE_NOALLOC_SCRATCH_BYTES
 
 
 class KveLayer(ctypes.Structure):
@@ -125,6 +127,11 @@ _lib.kve_step_ws.argtypes = [
     ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(KveLayer), ctypes.c_void_p, ctypes.c_void_p,
     ctypes.POINTER(Counters), ctypes.c_void_p, ctypes.POINTER(Policy), ctypes.c_void_p,
     ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+_lib.kve_step_noalloc.restype = ctypes.c_int
+_lib.kve_step_noalloc.argtypes = [
+    ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(KveLayer), ctypes.c_void_p, ctypes.c_void_p,
+    ctypes.POINTER(Counters), ctypes.c_void_p, ctypes.POINTER(Policy), ctypes.c_void_p,
+    ctypes.c_void_p]
 _lib.kve_workspace_size.restype = ctypes.c_int64
 _lib.kve_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
 _lib.kve_kept_indices.restype = ctypes.c_int32
@@ -143,6 +150,7 @@ _lib.kve_strerror.argtypes = [ctypes.c_int]
 EXPORTED = ("keyformer_step", "pyramid_step", "keyformer_step_layers", "pyramid_step_layers",
             "keyformer_step_tokens", "pyramid_step_tokens", "keyformer_step_layers_tokens",
             "pyramid_step_layers_tokens", "kve_step", "kve_step_ws", "kve_workspace_size",
+            "kve_step_noalloc",
             "pyramid_budgets", "kve_kept_indices",
             "kve_fp16_bytes", "kve_full_fp16_bytes", "kve_strerror")
 
@@ -159,7 +167,7 @@ def _check(rc: int, what: str) -> None:
     if rc == KVE_OK:
         return
     msg = f"{what}: {strerror(rc)} (code {rc})"
-    if rc == KVE_EINVAL:
+    if rc in (KVE_EINVAL, KVE_ENOSPACE):
         raise ValueError(msg)
     raise RuntimeError(msg)
 
@@ -551,6 +559,19 @@ def step(batch: LayerBatch, new_k, new_v, pol: Policy, evicted=None, stream=None
                           batch.budgets, ctypes.byref(pol), pe, workspace.data_ptr(),
                           workspace.numel(), st)
     _check(rc, "kve_step_ws")
+
+
+def step_noalloc(batch: LayerBatch, new_k, new_v, pol: Policy, evicted=None, stream=None,
+                 n_tokens: int | None = None) -> None:
+    """kve_step_noalloc: step() with the workspace in the library's fixed device
+    buffer (nothing allocated; raises ValueError when the call would need more
+    than NOALLOC_SCRATCH_BYTES of it)."""
+    S = 1 if n_tokens is None else n_tokens
+    pe = batch._fill(new_k, new_v, evicted, n_tokens)
+    rc = _lib.kve_step_noalloc(batch.n, S, batch.c_layers, batch._pk, batch._pv, batch.ctrs,
+                               batch.budgets, ctypes.byref(pol), pe,
+                               _stream_ptr(stream, batch.layers[0]))
+    _check(rc, "kve_step_noalloc")
 
 
 def workspace_size(caches: int, max_budget: int, d: int) -> int:

@@ -10,6 +10,7 @@
 #include <cstdint>
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 
 #include "kve.h"
 #include "kve_step.h"
@@ -213,7 +214,10 @@ int step_impl(const kve_layer *L, const void *new_k, const void *new_v, kve_coun
   if (hand_over) sa.pool = pool;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();                     // report this call's launch, not an older error
-  int rc = launch_error(kve::launch_step(la, sa, L->bh, L->d, p.gumbel, s));
+  int rc = KVE_OK;
+  if (hand_over && pool.clear_first) rc = launch_error(kve::launch_pool_clear(pool, s));
+  if (rc != KVE_OK) return rc;
+  rc = launch_error(kve::launch_step(la, sa, L->bh, L->d, p.gumbel, s));
   if (rc != KVE_OK) return rc;
   if (hand_over) {
     rc = launch_error(kve::launch_moves(pool, sa.back1, L->d, s));
@@ -229,12 +233,11 @@ int step_impl(const kve_layer *L, const void *new_k, const void *new_v, kve_coun
 // exchange data, so any grouping gives the same bits)
 // ---------------------------------------------------------------------------
 
-// Descriptor-driven launches: n_layers layers, each stepped n_tokens tokens.
-// Checks every layer first.
-int batch_impl(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
-               const void *const *new_k, const void *const *new_v, kve_counters *ctrs,
-               const int32_t *budgets, const Policy &p, int32_t *const *evicted,
-               const kve::MovePool &pool, void *stream) {
+// The host checks of a descriptor-driven call: n_layers layers, each stepped
+// n_tokens tokens.  KVE_OK or KVE_EINVAL.
+int check_batch(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
+                const void *const *new_k, const void *const *new_v, const kve_counters *ctrs,
+                const int32_t *budgets, const Policy &p) {
   if (n_layers < 1 || n_layers > kve::kMaxBatchLayers) return KVE_EINVAL;
   if (n_tokens < 1 || n_tokens > kve::kMaxTokens) return KVE_EINVAL;
   if (!layers || !new_k || !new_v || !ctrs || !budgets) return KVE_EINVAL;
@@ -265,6 +268,18 @@ int batch_impl(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
       if (start(order[i]) < prev_end) return KVE_EINVAL;
     }
   }
+  return KVE_OK;
+}
+
+// Descriptor-driven launches: n_layers layers, each stepped n_tokens tokens.
+// Checks every layer first.
+int batch_impl(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
+               const void *const *new_k, const void *const *new_v, kve_counters *ctrs,
+               const int32_t *budgets, const Policy &p, int32_t *const *evicted,
+               const kve::MovePool &pool, void *stream) {
+  if (check_batch(n_layers, n_tokens, layers, new_k, new_v, ctrs, budgets, p) != KVE_OK)
+    return KVE_EINVAL;
+  const int d = layers[0].d;
   bool any_evicts = false;                    // some layer is at its budget
   for (int32_t l = 0; l < n_layers; ++l) any_evicts = any_evicts || ctrs[l].n_kept + n_tokens > budgets[l];
   const kve::SharedArgs shared = shared_args(d, p, any_evicts);
@@ -288,7 +303,10 @@ int batch_impl(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
     const bool hand_over = pool.items && n_tokens == 1 && evicts && defers(p, block0);
     if (hand_over) sa.pool = pool;
     (void)hipGetLastError();                   // report this launch, not an older error
-    int rc = launch_error(
+    int rc = KVE_OK;
+    if (hand_over && pool.clear_first) rc = launch_error(kve::launch_pool_clear(pool, s));
+    if (rc != KVE_OK) return rc;
+    rc = launch_error(
         kve::launch_step_layers(pack, g1 - g0, block0, max_n, n_tokens, sa, d, p.gumbel, s));
     if (rc != KVE_OK) return rc;
     if (hand_over) {
@@ -419,6 +437,19 @@ int general_step(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
                     stream);
 }
 
+// general_step's host checks alone (nothing is enqueued).
+int check_general(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
+                  const void *const *new_k, const void *const *new_v, const kve_counters *ctrs,
+                  const int32_t *budgets, const Policy &p) {
+  if (!layers || !new_k || !new_v || !ctrs || !budgets) return KVE_EINVAL;
+  if (n_layers == 1 && n_tokens == 1)
+    return check_policy(p) == KVE_OK &&
+                   check_layer(&layers[0], new_k[0], new_v[0], &ctrs[0], budgets[0], p) == KVE_OK
+               ? KVE_OK
+               : KVE_EINVAL;
+  return check_batch(n_layers, n_tokens, layers, new_k, new_v, ctrs, budgets, p);
+}
+
 }  // namespace
 
 KVE_EXPORT int kve_step(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
@@ -451,6 +482,80 @@ KVE_EXPORT int64_t kve_workspace_size(int64_t caches, int32_t max_budget, int32_
   const int64_t items = caches * (int64_t)kve::max_move_chunks(max_budget);
   if (items > INT32_MAX / 2) return -1;
   return kve::pool_bytes(items, d);
+}
+
+// ---------------------------------------------------------------------------
+// the entry point that allocates nothing (kve_step_noalloc): the workspace
+// of kve_step_ws in a fixed-size array of every device the library runs on
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// Device memory of this array exists once per GPU, from the library's load
+// until the process ends.  Host code never uses its name as an address: the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[KVE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 128;
+
+struct ScratchAddress {
+  std::once_flag once;
+  void *ptr = nullptr;        // device address of `scratch` on this device, or null
+};
+ScratchAddress g_scratch[kMaxDevices];
+
+// The device address of the scratch array on the current device, looked up on
+// the first call on that device (with the device current).
+void *scratch_address(int dev) {
+  ScratchAddress &a = g_scratch[dev];
+  std::call_once(a.once, [&a] {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess) a.ptr = p;
+    else (void)hipGetLastError();
+  });
+  return a.ptr;
+}
+
+}  // namespace
+
+KVE_EXPORT int kve_step_noalloc(int32_t n_layers, int32_t n_tokens, const kve_layer *layers,
+                                const void *const *new_k, const void *const *new_v,
+                                kve_counters *ctrs, const int32_t *budgets,
+                                const kve_policy *policy, int32_t *const *evicted,
+                                void *stream) {
+  if (!layers || !budgets || n_layers < 1 || n_layers > kve::kMaxBatchLayers) return KVE_EINVAL;
+  Policy p;
+  if (policy_from(policy, p) != KVE_OK) return KVE_EINVAL;
+  // the scratch the call would use: every long move handed over, as with
+  // kve_workspace_size's workspace
+  int64_t caches = 0;
+  int32_t max_budget = 1;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    caches += layers[l].bh > 0 ? layers[l].bh : 0;
+    max_budget = std::max(max_budget, budgets[l]);
+  }
+  const bool hands_over = n_tokens == 1 && defers(p, caches);
+  if (!hands_over)                             // needs no scratch: kve_step
+    return general_step(n_layers, n_tokens, layers, new_k, new_v, ctrs, budgets, policy,
+                        evicted, kve::MovePool{}, stream);
+  // every argument is checked before the size and before any device call
+  if (check_general(n_layers, n_tokens, layers, new_k, new_v, ctrs, budgets, p) != KVE_OK)
+    return KVE_EINVAL;
+  const int64_t need = kve_workspace_size(caches, max_budget, layers[0].d);
+  if (need < 0) return KVE_EINVAL;
+  if (need > (int64_t)KVE_NOALLOC_SCRATCH_BYTES) return KVE_ENOSPACE;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return KVE_ENODEV;
+  }
+  void *ptr = scratch_address(dev);
+  if (!ptr) return KVE_ENODEV;
+  kve::MovePool pool;
+  if (make_pool(ptr, KVE_NOALLOC_SCRATCH_BYTES, layers[0].d, pool) != KVE_OK) return KVE_EINVAL;
+  pool.clear_first = 1;                        // the last call on this device left it as it was
+  return general_step(n_layers, n_tokens, layers, new_k, new_v, ctrs, budgets, policy, evicted,
+                      pool, stream);
 }
 
 // "The budget schedule": linear taper, mean avg_budget, floor n_sink + 1.
@@ -513,6 +618,8 @@ KVE_EXPORT const char *kve_strerror(int code) {
     case KVE_EINVAL: return "invalid argument";
     case KVE_ELAUNCH: return "kernel launch failed";
     case KVE_ENODEV: return "no gfx950 HIP device";
+    case KVE_ENOSPACE:
+      return "the call needs more scratch than kve_step_noalloc's fixed device buffer holds";
     default: return "unknown error";
   }
 }

@@ -56,6 +56,7 @@ struct MovePool {
   MoveItem *items;         // [cap]; null pointer: every step compacts its own cache
   void *rows;              // fp16 [cap][2][d]: parked key then value of each item
   int32_t cap;             // items (and parked rows) the workspace holds
+  int32_t clear_first;     // host only: zero the header before the step launch
 };
 
 // Workspace layout for `cap` items of head dimension d: counters, items,
@@ -135,5 +136,9 @@ bool reuse_keys(int total_blocks, int max_n_prev, int n_tokens, int d);
 // sa.pool.items set handed over, and zeroes the pool's counters.  Must run
 // after it on the same stream.
 hipError_t launch_moves(const MovePool &pool, const RopeTable &back1, int d, hipStream_t stream);
+
+// Zeroes the pool's header words (a scratch whose contents are unknown), in
+// stream order before a step launch that uses it.
+hipError_t launch_pool_clear(const MovePool &pool, hipStream_t stream);
 
 }  // namespace kve

@@ -1194,6 +1194,18 @@ hipError_t launch_step_layers(const LayerPack &layers, int n_layers, int total_b
                                                    d, gumbel, stream);
 }
 
+// One wave writes zeros over the header's words (a fill kernel rather than a
+// memset: it may be captured into a graph and replayed).
+__global__ __launch_bounds__(64) void pool_clear_kernel(int32_t *header) {
+  const int i = threadIdx.x;
+  if (i < (int)(kPoolHeaderBytes / sizeof(int32_t))) global(header)[i] = 0;
+}
+
+hipError_t launch_pool_clear(const MovePool &pool, hipStream_t stream) {
+  hipLaunchKernelGGL(pool_clear_kernel, dim3(1), dim3(64), 0, stream, pool.count);
+  return hipGetLastError();
+}
+
 hipError_t launch_moves(const MovePool &pool, const RopeTable &back1, int d,
                         hipStream_t stream) {
   // enough workgroups to spread the longest moves of a launch over the GPU;

@@ -32,20 +32,22 @@ def test_header_declares_the_abi():
                                 "pyramid_step_layers", "keyformer_step_tokens",
                                 "pyramid_step_tokens", "keyformer_step_layers_tokens",
                                 "pyramid_step_layers_tokens", "kve_step", "kve_step_ws",
-                                "kve_workspace_size", "pyramid_budgets",
+                                "kve_workspace_size", "kve_step_noalloc", "pyramid_budgets",
                                 "kve_kept_indices", "kve_fp16_bytes", "kve_full_fp16_bytes",
                                 "kve_strerror"}
 
 
-# HIP runtime calls the library may import: kernel registration and launch,
-# the LDS-size attribute of a launch, and the launch-error query.  No
-# allocation (hipMalloc, hipHostMalloc, hipMallocAsync, ...), free, memset,
-# copy, event or synchronisation call is imported, so no path of any entry
-# point can allocate device memory or stall the caller's streams.
+# HIP runtime calls the library may import: kernel and device-variable
+# registration and launch, the LDS-size attribute of a launch, the
+# launch-error query, and -- for kve_step_noalloc's fixed buffer -- the
+# current device and the device address of that buffer.  No allocation
+# (hipMalloc, hipHostMalloc, hipMallocAsync, ...), free, memset, copy, event or
+# synchronisation call is imported, so no path of any entry point can
+# allocate device memory or stall the caller's streams.
 ALLOWED_HIP_IMPORTS = {"__hipPopCallConfiguration", "__hipPushCallConfiguration",
-                       "__hipRegisterFatBinary", "__hipRegisterFunction",
+                       "__hipRegisterFatBinary", "__hipRegisterFunction", "__hipRegisterVar",
                        "__hipUnregisterFatBinary", "hipFuncSetAttribute", "hipGetLastError",
-                       "hipLaunchKernel"}
+                       "hipLaunchKernel", "hipGetDevice", "hipGetSymbolAddress"}
 
 
 def test_library_imports_no_allocation_or_synchronisation():
@@ -518,3 +520,64 @@ def test_binding_workspace_is_aligned_zeroed_and_sized():
     assert ws.data_ptr() % 256 == 0 and not bool(ws.any())
     with pytest.raises(ValueError):
         kve.workspace_size(0, 1000, 128)
+
+
+# ---------------------------------------------------------------------------
+# kve_step_noalloc: the size check happens before anything touches a device
+# ---------------------------------------------------------------------------
+
+def _noalloc_call(layers, budgets, pol, n_tokens=1):
+    n = len(layers)
+    arr = (KveLayer * n)(*layers)
+    cs = (Counters * n)(*[Counters(b, 5000, 5000) for b in budgets])
+    bs = (ctypes.c_int32 * n)(*budgets)
+    ptrs = (ctypes.c_void_p * n)(*([FAKE] * n))
+    rc = kve.lib().kve_step_noalloc(n, n_tokens, arr, ptrs, ptrs, cs, bs, ctypes.byref(pol), None,
+                                    None)
+    return rc, [(c.n_kept, c.next_pos, c.pos) for c in cs]
+
+
+def test_noalloc_rejects_calls_beyond_its_buffer():
+    """32 layers of 256 caches at budget 1024 (the 8B-shaped decode in one
+    launch) would need 68 MiB of scratch to hand every move over: more than
+    the fixed 16 MiB buffer, so the call is refused before any launch."""
+    gib = 1 << 30
+    layers = [_layer(bh=256, cap=1025, d=128, k=FAKE + l * gib, v=FAKE + l * gib)
+              for l in range(32)]
+    pol = kve.policy("keyformer", 4, 0, 1.0, 2.0, 512, 1e4, 0)
+    assert kve.workspace_size(32 * 256, 1024, 128) > kve.NOALLOC_SCRATCH_BYTES
+    rc, after = _noalloc_call(layers, [1024] * 32, pol)
+    assert rc == kve.KVE_ENOSPACE
+    assert after == [(1024, 5000, 5000)] * 32
+    assert "fixed device buffer" in kve.strerror(kve.KVE_ENOSPACE)
+
+
+@pytest.mark.parametrize("case", ["fits", "no_handover_tokens", "no_handover_policy"])
+def test_noalloc_accepts_what_fits_or_needs_no_scratch(case):
+    """Within the buffer (one 256-cache layer at budget 1024: 2.1 MiB), or a
+    call that hands nothing over (several tokens; H2O without a window): the
+    host checks pass and the call reaches the device (none here)."""
+    pol = kve.policy("keyformer", 4, 0, 1.0, 2.0, 512, 1e4, 0)
+    layers, n_tokens = [_layer(bh=256, cap=1025, d=128)], 1
+    if case == "no_handover_tokens":
+        layers = [_layer(bh=256 * 32, cap=1025, d=128)]
+        n_tokens = 4
+    elif case == "no_handover_policy":
+        layers = [_layer(bh=256 * 32, cap=1025, d=128, gumbel=None)]
+        pol = kve.policy("h2o", 4)
+    assert kve.workspace_size(256, 1024, 128) <= kve.NOALLOC_SCRATCH_BYTES
+    rc, after = _noalloc_call(layers, [1024], pol, n_tokens)
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; the no-device path is not reachable")
+    assert rc == kve.KVE_ENODEV
+    assert after == [(1024, 5000, 5000)]
+
+
+def test_noalloc_checks_arguments_like_kve_step():
+    pol = kve.policy("keyformer", 4, 0, 1.0, 2.0, 512, 1e4, 0)
+    rc, _ = _noalloc_call([_layer(bh=256, cap=1025, d=96)], [1024], pol)
+    assert rc == kve.KVE_EINVAL
+    rc, _ = _noalloc_call([_layer(bh=256, cap=1000, d=128)], [1024], pol)
+    assert rc == kve.KVE_EINVAL
+    assert kve.lib().kve_step_noalloc(1, 1, None, None, None, None, None, ctypes.byref(pol), None,
+                                      None) == kve.KVE_EINVAL

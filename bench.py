@@ -159,24 +159,24 @@ def bandwidth_context(dev) -> dict:
     torch.cuda.synchronize()
     copy_gbs = 5 * 2 * n * 4 / (a.elapsed_time(b) / 1e3) / 1e9
     del dst
-    # a read-only stream: the sum of 4 GiB (the eviction step reads far more
-    # than it writes)
-    big = torch.ones((1 << 32) // 4, dtype=torch.float32, device=dev)
-    acc = torch.empty((), dtype=torch.float32, device=dev)
-    torch.sum(big, dim=0, out=acc)
+    # a read stream: row sums of 4 GiB of fp32 in rows of 1024 (4 GiB read, 4
+    # MiB written; the eviction step reads far more than it writes)
+    big = torch.ones(((1 << 32) // 4 // 1024, 1024), dtype=torch.float32, device=dev)
+    acc = torch.empty(big.shape[0], dtype=torch.float32, device=dev)
+    torch.sum(big, dim=1, out=acc)
     torch.cuda.synchronize()
     a.record()
     for _ in range(5):
-        torch.sum(big, dim=0, out=acc)
+        torch.sum(big, dim=1, out=acc)
     b.record()
     torch.cuda.synchronize()
     read_gbs = 5 * big.numel() * 4 / (a.elapsed_time(b) / 1e3) / 1e9
-    del src, big
+    del src, big, acc
     torch.cuda.empty_cache()
     return {"copy_kernel_GBs": copy_gbs,
             "copy_kernel": "torch elementwise copy, 1 GiB read + 1 GiB written",
             "read_kernel_GBs": read_gbs,
-            "read_kernel": "torch sum of 4 GiB of fp32 (reads only)"}
+            "read_kernel": "torch row sums of 4 GiB of fp32, rows of 1024 (4 GiB read)"}
 
 
 def step_bytes(kind: str, n: int, d: int, m, over: bool = True):

@@ -195,6 +195,41 @@ static void policy_and_workspace(void)
     CHECK(kve_workspace_size((int64_t)1 << 31, 1024, 128) == -1);
 }
 
+static void noalloc(void)
+{
+    /* 32 layers x 256 caches at budget 1024 would need 68 MiB of scratch */
+    static kve_layer Ls[32];
+    kve_counters cs[32];
+    int32_t budgets[32];
+    const void *ptrs[32];
+    for (int i = 0; i < 32; ++i) {
+        Ls[i] = layer();
+        Ls[i].bh = 256; Ls[i].cap = 1025; Ls[i].d = 128;
+        Ls[i].k = (char *)FAKE + (size_t)i * ((size_t)1 << 30);
+        cs[i].n_kept = 1024; cs[i].next_pos = 5000; cs[i].pos = 5000;
+        budgets[i] = 1024;
+        ptrs[i] = FAKE;
+    }
+    kve_policy p;
+    memset(&p, 0, sizeof p);
+    p.n_sink = 4; p.score = KVE_SCORE_CUMULATIVE; p.gumbel = 1;
+    p.tau_init = 1.0; p.tau_end = 2.0; p.anneal_steps = 512; p.rope_base = 1e4;
+    CHECK(kve_workspace_size(32 * 256, 1024, 128) > KVE_NOALLOC_SCRATCH_BYTES);
+    CHECK(kve_step_noalloc(32, 1, Ls, ptrs, ptrs, cs, budgets, &p, NULL, NULL) == KVE_ENOSPACE);
+    CHECK(cs[0].n_kept == 1024 && cs[31].pos == 5000);
+    /* one layer fits; arguments are checked before any device call */
+    CHECK(not_ran(kve_step_noalloc(1, 1, Ls, ptrs, ptrs, cs, budgets, &p, NULL, NULL)));
+    Ls[0].cap = 1000;
+    CHECK(kve_step_noalloc(1, 1, Ls, ptrs, ptrs, cs, budgets, &p, NULL, NULL) == KVE_EINVAL);
+    Ls[0].cap = 1025;
+    CHECK(kve_step_noalloc(1, 1, NULL, ptrs, ptrs, cs, budgets, &p, NULL, NULL) == KVE_EINVAL);
+    CHECK(kve_step_noalloc(1, 1, Ls, ptrs, ptrs, cs, budgets, NULL, NULL, NULL) == KVE_EINVAL);
+    /* several tokens hand nothing over: no scratch needed */
+    CHECK(not_ran(kve_step_noalloc(32, 4, Ls, ptrs, ptrs, cs, budgets, &p, NULL, NULL)));
+    CHECK(cs[0].n_kept == 1024 && cs[31].pos == 5000);
+    CHECK(strstr(kve_strerror(KVE_ENOSPACE), "fixed") != NULL);
+}
+
 static void host_helpers(void)
 {
     static const int32_t page[12] = {1019, 927, 835, 742, 650, 558, 466, 374, 282, 189, 97, 5};
@@ -232,6 +267,7 @@ int main(void)
     keyformer_rejects();
     batched_rejects();
     policy_and_workspace();
+    noalloc();
     host_helpers();
     printf("ok: %d checks\n", checks);
     return 0;

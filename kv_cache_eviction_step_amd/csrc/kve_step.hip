@@ -300,6 +300,12 @@ constexpr float kZScale = 0x1p40f;
 // the kernel
 // ---------------------------------------------------------------------------
 
+// 16-byte chunks per lane in the score pass of 512-thread workgroups
+// (tuning builds may override with -D).
+#ifndef KVE_CPL512
+#define KVE_CPL512 2
+#endif
+
 // Rows each thread moves per chunk of the compaction (tuning builds may
 // override with -D).
 #ifndef KVE_MOVE_UNROLL
@@ -363,7 +369,7 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   // c and c + D/16), then the pairs combined by the in-row butterfly.  With
   // one chunk per lane (lane c reads chunk c), a first step adds the partner
   // lane c ^ (D/16), and the butterfly over the pairs follows.
-  constexpr int CPL = NT >= 1024 ? 1 : 2;
+  constexpr int CPL = NT >= 1024 ? 1 : KVE_CPL512;
   constexpr int LPR = V16 / CPL;
   constexpr int RPS = NT / LPR;     // score pass: rows per sweep
   constexpr int UR = U / CPL;       // score pass: rows per lane per batch
@@ -957,11 +963,20 @@ __global__ __launch_bounds__(256) void move_kernel(MovePool pool, RopeTable back
   constexpr int RPM = NT / LPM;                 // rows per sweep
   constexpr int SW = kMoveChunk / RPM;          // sweeps per chunk
   static_assert(SW * RPM == kMoveChunk, "move chunk");
-  // Ordinary loads: both words were last written before this launch began
-  // (the counter by the step's atomics, the phase by its workgroup 0), and
-  // workgroup 0's updates below change neither of them.
+  // Everything the first chunk depends on is loaded at once, so that the
+  // launch waits for one round trip before its row loads, not three: the
+  // phase, both reservation counters (the phase picks one), and the item this
+  // workgroup takes first if the queue reaches it (items[blockIdx.x] is inside
+  // the pool: the grid is never larger than its capacity).  Ordinary loads:
+  // the phase and the counter it picks were last written before this launch
+  // began (the counter by the step's atomics, the phase by its workgroup 0),
+  // and workgroup 0's updates below change neither of them (the other
+  // counter, which it zeroes, is read here but not used).
   const int phase = global(pool.count)[kPoolLaunchPhase];
-  const int reserved = global(pool.count)[pool_counter(phase)];
+  const int count_even = global(pool.count)[kPoolCount];
+  const int count_odd = global(pool.count)[kPoolCount + 1];
+  const MoveItem first_item = pool.items[blockIdx.x];
+  const int reserved = pool_counter(phase) == kPoolCount ? count_even : count_odd;
   const int queued = items_queued(reserved, pool.cap);
   if (blockIdx.x == 0 && threadIdx.x == 0) {    // the next call's counter, then its phase
     atomicExch(pool.count + pool_counter(pool_next_phase(phase)), 0);
@@ -982,7 +997,7 @@ __global__ __launch_bounds__(256) void move_kernel(MovePool pool, RopeTable back
                                              : (int)gridDim.x;
   const int first = (int)blockIdx.x < active ? (int)blockIdx.x : queued;
   for (int item = first; item < queued; item += active) {
-    const MoveItem md = pool.items[item];
+    const MoveItem md = item == (int)blockIdx.x ? first_item : pool.items[item];
     if (md.k == nullptr) continue;              // reserved by a step that found no room
     const int j = md.j, e = md.e, n = md.n, last = move_last_dst(n);
     const int chunks = move_chunks(e, n);

@@ -996,8 +996,13 @@ __global__ __launch_bounds__(256) void move_kernel(MovePool pool, RopeTable back
   const int active = queued > (int)gridDim.x ? min((int)gridDim.x, kMoveStreams)
                                              : (int)gridDim.x;
   const int first = (int)blockIdx.x < active ? (int)blockIdx.x : queued;
+  // The next item's descriptor is loaded while this chunk moves, so that a
+  // workgroup taking chunks in turn waits for one round trip per chunk (its
+  // rows), not two.
+  MoveItem next_item = first_item;
   for (int item = first; item < queued; item += active) {
-    const MoveItem md = item == (int)blockIdx.x ? first_item : pool.items[item];
+    const MoveItem md = next_item;
+    if (item + active < queued) next_item = pool.items[item + active];
     if (md.k == nullptr) continue;              // reserved by a step that found no room
     const int j = md.j, e = md.e, n = md.n, last = move_last_dst(n);
     const int chunks = move_chunks(e, n);

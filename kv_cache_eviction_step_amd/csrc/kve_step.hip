@@ -624,17 +624,29 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
   const int pool_phase = __builtin_amdgcn_readfirstlane(pool_phase_in);
 
   // ---- D: write-back ----------------------------------------------------------
+  // A single step writes its state through the L2 (agent-scope relaxed atomic
+  // stores, which the L2 writes through at once): written as ordinary stores,
+  // the lines stay dirty in the L2 until the key streams of other caches
+  // evict them one by one, and each of those lone writes turns an HBM channel
+  // around in the middle of the reads.  A token loop re-reads its state on
+  // the next token and keeps ordinary stores.
+  auto st_state = [](auto x, auto p) {
+    if constexpr (REUSE)
+      *p = x;
+    else
+      __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
   const gptr<int32_t> __restrict__ positions = global(la.positions);
 #pragma unroll
   for (int k = 0; k < R; ++k) {
     const int i = tid + k * NT;
     if (i < n) {
       if (e < 0 || i < e) {
-        scores[row0 + i] = sreg[k];
+        st_state(sreg[k], scores + (row0 + i));
       } else if (i > e) {
-        scores[row0 + i - 1] = sreg[k];
-        if constexpr (GUMBEL) gumbel[row0 + i - 1] = greg[k];
-        positions[row0 + i - 1] = i - 1;
+        st_state(sreg[k], scores + (row0 + i - 1));
+        if constexpr (GUMBEL) st_state(greg[k], gumbel + (row0 + i - 1));
+        st_state(i - 1, positions + (row0 + i - 1));
       }
     }
   }
@@ -851,9 +863,9 @@ __device__ __forceinline__ void step_body(const LayerArgs &la, const SharedArgs 
     }
     dv[tid] = v_new;
     if (tid == 0) {
-      scores[row0 + f] = 0.0f;
-      if constexpr (GUMBEL) gumbel[row0 + f] = g_new;
-      positions[row0 + f] = e < 0 ? la.next_pos : f;
+      st_state(0.0f, scores + (row0 + f));
+      if constexpr (GUMBEL) st_state(g_new, gumbel + (row0 + f));
+      st_state(e < 0 ? la.next_pos : f, positions + (row0 + f));
     }
   }
 }

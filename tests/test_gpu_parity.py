@@ -1132,6 +1132,46 @@ def test_tova_handoff_equals_own_moves(dev, recent):
     assert int(moved.max()) > 128                      # some move was handed over
 
 
+def test_handoff_queue_longer_than_grid_equals_own_moves(dev):
+    """A queue of handed-over chunks longer than the move kernel's grid (so
+    its workgroups take chunks in turn, each loading its next chunk's item
+    while the current one moves): TOVA scoring with a 200-row window on 512
+    caches of 4096 rows, one token per kve_step_ws call, against the same
+    caches compacted in place by kve_step.  Same bits on every cache."""
+    import kv_cache_eviction_step_amd as kve
+    from gpu_harness import bulk_state
+    bh, d, budget, T, pos0, recent = 512, 128, 4096, 4, 9000, 200
+    grid = 1024                                        # the move kernel's largest grid
+    _say(f"[handoff long queue] bh={bh} budget={budget} T={T} recent={recent}")
+    w = synth.Workload("tvq", 1, 1, bh, d, pos0, T, budget, 4, "tova", recent=recent)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(131)
+    A = kve.Layer.empty(bh, budget + 1, d, dev, gumbel=False)
+    bulk_state(A, budget, w, gen)
+    B = kve.Layer(A.k.clone(), A.v.clone(), A.scores.clone(), None, A.positions.clone())
+    nk, nv = synth.bulk_kv_torch(w, pos0, T, bh, gen, dev)
+    pol = kve.policy("tova", n_sink=4, recent=recent, rope_base=1e4)
+    ev_a = torch.full((T, bh), -9, dtype=torch.int32, device=dev)
+    ev_b = torch.full((T, bh), -9, dtype=torch.int32, device=dev)
+    ba = kve.LayerBatch([A], [budget], [kve.Counters(budget, pos0, pos0)])
+    bb = kve.LayerBatch([B], [budget], [kve.Counters(budget, pos0, pos0)])
+    ws = kve.workspace(bh, budget, d, dev)
+    for t in range(T):
+        kve.step(ba, [nk[t]], [nv[t]], pol, [ev_a[t]], workspace=ws)
+        kve.step(bb, [nk[t]], [nv[t]], pol, [ev_b[t]])
+    torch.cuda.synchronize()
+    assert workspace_ready(ws)
+    assert torch.equal(ev_a, ev_b)
+    for name in ("k", "v", "scores", "positions"):
+        assert torch.equal(getattr(A, name)[:, :budget], getattr(B, name)[:, :budget]), name
+    # every token queued more chunks than the move kernel has workgroups
+    e = ev_a.to(torch.int64).cpu()
+    rows = budget - 1 - e
+    handed = (e >= 0) & (e < budget - 1) & (rows > 128)
+    chunks = torch.where(handed, (rows + 63) // 64, 0).sum(dim=1)
+    assert int(chunks.min()) > grid, chunks.tolist()
+
+
 @pytest.mark.parametrize("d", [128, 64])
 def test_handoff_edges_against_oracle(dev, d):
     """One single-token Keyformer kve_step_ws launch of 320 caches (moves over

@@ -377,21 +377,28 @@ def test_full_size_tokens_late_riser_every_layer(dev):
     assert any(((ev[:, l] >= 0) & (ev[:, l] < w.budget)).any() for l in range(w.layers))
 
 
-def test_whole_run_late_riser_every_layer(dev):
+@pytest.mark.parametrize("decode", ["tokens32", "single_ws"])
+def test_whole_run_late_riser_every_layer(dev, decode):
     """The 8B-shaped workload's whole run (4096 + 512 tokens from empty caches)
-    through all 32 layers x 256 caches, 32 tokens per launch, one sampled cache
-    per layer spread over batch and head, against the oracle.  Over 4608
-    tokens about one cache in twenty meets a near-tie between two stored rows
-    that no redraw of the incoming token clears; the sample then moves on to
-    the next cache of the layer."""
+    through all 32 layers x 256 caches, one sampled cache per layer spread over
+    batch and head, against the oracle.  The prompt goes 32 tokens per launch;
+    the decode tokens go the same way (tokens32), or one per launch through
+    kve_step_ws over all layers with long moves handed to the move kernel
+    (single_ws: the decode form the benchmark times).  Over 4608 tokens about
+    one cache in twenty meets a near-tie between two stored rows that no
+    redraw of the incoming token clears; the sample then moves on to the next
+    cache of the layer."""
     w = synth.WORKLOADS[3]
     T = w.tokens
     picks = {l: [(13 + 41 * l) % w.bh] for l in range(w.layers)}
-    _say(f"[whole-run] {w.name} layers={w.layers} bh={w.bh} one cache per layer T={T} S=32: oracle")
+    _say(f"[whole-run] {w.name} layers={w.layers} bh={w.bh} one cache per layer T={T} "
+         f"decode={decode}: oracle")
     samples = oracle_samples_layers(w, picks, [w.budget] * w.layers, T, False, tries=4)
     _say(f"[whole-run] {w.name}: GPU, sampled {[s.hh for l in sorted(samples) for s in samples[l]]}")
+    single = decode == "single_ws"
     layers, ev, batch = run_batched(w, list(range(w.layers)), [w.budget] * w.layers, T, samples,
-                                    None, 0, dev, tokens_per_call=32)
+                                    None, 0, dev, tokens_per_call=32, workspace=single,
+                                    decode_from=w.prompt if single else None)
     errs = []
     for l, ss in samples.items():
         for s in ss:
@@ -400,6 +407,9 @@ def test_whole_run_late_riser_every_layer(dev):
     assert all(c.n_kept == w.budget for c in batch.ctrs)
     late = ev[w.budget:]
     assert ((late >= 0) & (late < w.budget)).mean() > 0.02       # interior evictions happened
+    if single:                                  # some decode moves went to the move kernel
+        dec = ev[w.prompt:]
+        assert ((dec >= 0) & (w.budget - 1 - dec > 128)).any()
 
 
 def test_full_size_tokens_long_context_every_layer(dev):

@@ -31,6 +31,10 @@ def hipcc() -> str:
 # workgroup) per compute unit (4 waves per SIMD, i.e. at most 128 VGPRs) and
 # must not spill VGPRs to scratch memory.
 MIN_WAVES_PER_SIMD = 4
+# ... except the per-layer kernel for launches of at most one workgroup per
+# compute unit, which needs room for one 512-thread workgroup (2 waves per SIMD)
+SOLO_KERNEL = "step_kernel_solo"
+MIN_WAVES_PER_SIMD_SOLO = 2
 
 
 def kernel_resources(remarks: str) -> dict[str, dict[str, int]]:
@@ -55,7 +59,8 @@ def check_resources(res: dict[str, dict[str, int]]) -> list[str]:
         if "kernel" not in name:
             continue
         # (an SGPR spill goes to a VGPR lane, not to memory: allowed)
-        if (r.get("Occupancy", 0) < MIN_WAVES_PER_SIMD or r.get("ScratchSize", 0) or
+        need = MIN_WAVES_PER_SIMD_SOLO if SOLO_KERNEL in name else MIN_WAVES_PER_SIMD
+        if (r.get("Occupancy", 0) < need or r.get("ScratchSize", 0) or
                 r.get("VGPRs Spill", 0)):
             bad.append(f"{name}: {r}")
     return bad
